@@ -1,0 +1,193 @@
+"""CPU oracle for causal sliding-window attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the bench's
+CPU-baseline leg. The product path never imports it, and it imports nothing of the
+product (no kernels, headers, tables or helpers are shared).
+
+Two independent implementations of the same definition, both in float64:
+  * `prefill`, `decode`, `append`: a plain C windowed loop (swa_oracle.c), one query row
+    at a time, OpenMP across rows;
+  * `dense.prefill_dense`: numpy, a full [N, N] score matrix masked with the boolean band
+    mask built as in the Sliding Window Attention glossary's example.
+
+Parity status: the selection, the weights (sigmoid and softmax), the bias sign, the
+rotation and the ring are pinned by the tests in tests/test_oracle_pins.py against the
+pages' printed values, closed forms and library special cases. Outputs on random inputs
+beyond those are pinned only by the agreement of the two implementations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "swa_oracle.c")
+_LIB = os.path.join(_HERE, "libswa_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+SIGMOID = 0
+SOFTMAX = 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the C oracle with gcc (-O2, OpenMP) into oracle/libswa_oracle.so."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall", "-Werror",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def bind(path: str):
+    """Load a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    i64, dbl, ip, dp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p
+    lib.swa_oracle_prefill.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                       dbl, dp, dbl, dp, dp, dp, ip, i64, dp]
+    lib.swa_oracle_prefill.restype = ctypes.c_int
+    lib.swa_oracle_append.argtypes = [i64, i64, i64, i64, i64, dbl, dp, dp, ip, dp, dp,
+                                      dp, dp, ip, i64]
+    lib.swa_oracle_append.restype = ctypes.c_int
+    lib.swa_oracle_decode.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, dbl, dp,
+                                      dbl, dp, ip, dp, dp, ip, dp, dp, dp]
+    lib.swa_oracle_decode.restype = ctypes.c_int
+    lib.swa_oracle_ring_fill_positions.argtypes = [i64, i64, ip]
+    lib.swa_oracle_ring_fill_positions.restype = None
+    lib.swa_oracle_threads.argtypes = []
+    lib.swa_oracle_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            _lib = bind(_LIB)
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    """Exact upcast of a float tensor/array (fp32 or bf16 values) to a C-contiguous float64
+    numpy array."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i64(a) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().to("cpu", torch.int64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def threads() -> int:
+    return int(_load().swa_oracle_threads())
+
+
+def prefill(q, k, v, *, w: int, s: int = 0, mode: int = SIGMOID, scale: float = 0.0,
+            slopes=None, rope_theta: float = 0.0, rows=None) -> np.ndarray:
+    """float64 attention output. q [B,N,H_q,d], k/v [B,N,H_kv,d]. rows: optional list of
+    query rows; then the result is [B, len(rows), H_q, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, N, Hkv, d) and v.shape == k.shape
+    sl = None if slopes is None else _f64(slopes)
+    if sl is not None:
+        assert sl.shape == (Hq,)
+    if rows is None:
+        r, nr = None, N
+    else:
+        r = _i64(rows)
+        nr = r.shape[0]
+    out = np.zeros((B, nr, Hq, d), dtype=np.float64)
+    rc = _load().swa_oracle_prefill(B, Hq, Hkv, N, d, w, s, mode, float(scale), _ptr(sl),
+                                    float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(r),
+                                    nr if r is not None else 0, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle prefill rejected its arguments")
+    return out
+
+
+class Ring:
+    """The oracle's ring-buffer cache for S sequences: w slots of (position, rotated key,
+    value) per (sequence, kv head), plus s sink entries."""
+
+    def __init__(self, S: int, H_kv: int, w: int, s: int, d: int):
+        self.S, self.H_kv, self.w, self.s, self.d = S, H_kv, w, s, d
+        self.k = np.zeros((S, H_kv, w, d))
+        self.v = np.zeros((S, H_kv, w, d))
+        self.pos = np.full((S, w), -1, dtype=np.int64)
+        self.k_sink = np.zeros((S, H_kv, max(s, 1), d))
+        self.v_sink = np.zeros((S, H_kv, max(s, 1), d))
+
+    @classmethod
+    def from_state(cls, k_ring, v_ring, k_sink, v_sink, last_pos):
+        """A ring whose slots hold the given rotated keys/values, as left by appending
+        positions 0..last_pos[q] in order (positions found by simulating those writes)."""
+        k_ring, v_ring = _f64(k_ring), _f64(v_ring)
+        S, H_kv, w, d = k_ring.shape
+        s = 0 if k_sink is None else k_sink.shape[2]
+        r = cls(S, H_kv, w, s, d)
+        r.k[...] = k_ring
+        r.v[...] = v_ring
+        if s > 0:
+            r.k_sink[...] = _f64(k_sink)
+            r.v_sink[...] = _f64(v_sink)
+        lp = _i64(last_pos)
+        for qi in range(S):
+            r.pos[qi] = ring_fill_positions(int(lp[qi]), w)
+        return r
+
+    def append(self, k_new, v_new, pos0, rope_theta: float = 0.0):
+        """k_new/v_new [S, n_new, H_kv, d] (keys not yet rotated); pos0 [S]."""
+        kn, vn, p0 = _f64(k_new), _f64(v_new), _i64(pos0)
+        n_new = kn.shape[1]
+        assert kn.shape == (self.S, n_new, self.H_kv, self.d) and vn.shape == kn.shape
+        rc = _load().swa_oracle_append(self.S, self.H_kv, self.w, self.s, self.d,
+                                       float(rope_theta), _ptr(self.k), _ptr(self.v),
+                                       _ptr(self.pos), _ptr(self.k_sink), _ptr(self.v_sink),
+                                       _ptr(kn), _ptr(vn), _ptr(p0), n_new)
+        if rc != 0:
+            raise ValueError("oracle append rejected its arguments")
+
+    def decode(self, q, q_pos, *, H_q: int, mode: int, scale: float = 0.0, slopes=None,
+               rope_theta: float = 0.0) -> np.ndarray:
+        """q [S, H_q, d] (not rotated), q_pos [S] -> float64 [S, H_q, d]."""
+        qq, qp = _f64(q), _i64(q_pos)
+        assert qq.shape == (self.S, H_q, self.d)
+        sl = None if slopes is None else _f64(slopes)
+        out = np.zeros((self.S, H_q, self.d))
+        rc = _load().swa_oracle_decode(self.S, H_q, self.H_kv, self.d, self.w, self.s, mode,
+                                       float(scale), _ptr(sl), float(rope_theta), _ptr(qq),
+                                       _ptr(qp), _ptr(self.k), _ptr(self.v), _ptr(self.pos),
+                                       _ptr(self.k_sink), _ptr(self.v_sink), _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle decode rejected its arguments")
+        return out
+
+
+def ring_fill_positions(p_last: int, w: int) -> np.ndarray:
+    out = np.empty(w, dtype=np.int64)
+    _load().swa_oracle_ring_fill_positions(int(p_last), int(w), _ptr(out))
+    return out
