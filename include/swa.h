@@ -1,0 +1,168 @@
+/*
+ * swa.h - libswa: causal sliding-window attention on AMD MI355X (gfx950).
+ *
+ * The operation (SWAT: Sliding Window Attention Training, "Balanced ALiBi" attention
+ * equation; Sliding Window Attention glossary, the band mask and the ring buffer;
+ * Sliding-window beats linear attention, SWA(w, s) with sink tokens):
+ *
+ *   For batch b, query head h (kv head hk = h / (H_q / H_kv)) and query position i:
+ *     K(i)  = { j : 0 <= j <= i  and  (i - j < w  or  j < s) }
+ *     x_ij  = scale * (R(i) q_i) . (R(j) k_j) + slope_h * (i - j)
+ *     p_ij  = 1 / (1 + exp(-x_ij))                       SWA_SIGMOID (no normalisation)
+ *           = exp(x_ij) / sum_{j' in K(i)} exp(x_ij')    SWA_SOFTMAX
+ *     o_i   = sum_{j in K(i)} p_ij v_j
+ *   R(p) rotates the interleaved pairs (2t, 2t+1) of a head vector by the angle
+ *   p * theta^(-2t/d) (RoPE); the angles come from a table built by swa_rope_table.
+ *   Positions are absolute 0-based token indices everywhere, sinks included.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are caller-owned DEVICE memory unless a comment says "host". The library
+ *     allocates nothing, frees nothing and keeps no pointer after returning.
+ *   - Tensors are dense, row-major, innermost dimension last, with the layouts given
+ *     below. Element types are float32 (SWA_F32) or bfloat16 (SWA_BF16).
+ *   - Arguments are validated on the host before anything is launched; on an error
+ *     nothing is written and nothing is launched. A failed launch returns SWA_ERR_HIP
+ *     (the HIP error code is then available from swa_last_hip_error()).
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the default
+ *     stream). The caller synchronises. Calls on different streams may run concurrently.
+ *   - The library holds no state: positions and cache contents are always explicit.
+ *   - Device values that cannot be checked on the host (positions, table coverage of a
+ *     position) are checked by the kernels: an out-of-range position produces NaN
+ *     outputs for the affected query instead of an out-of-bounds access.
+ */
+#ifndef LIBSWA_SWA_H
+#define LIBSWA_SWA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SWA_OK = 0,
+    SWA_ERR_INVALID_ARGUMENT = 1, /* a null pointer, a negative size, H_q % H_kv != 0, ... */
+    SWA_ERR_UNSUPPORTED = 2,      /* a valid combination this build does not implement     */
+    SWA_ERR_HIP = 3               /* a HIP runtime call or a kernel launch failed          */
+} swa_status;
+
+typedef enum { SWA_SIGMOID = 0, SWA_SOFTMAX = 1 } swa_mode;
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+/*
+ * Prefill over one batch of whole sequences: query row n sits at position n.
+ *   q, o : [B, N, H_q, d]    k, v : [B, N, H_kv, d]
+ * Requirements: B, N >= 0; H_q, H_kv >= 1; H_q % H_kv == 0; d even, 2 <= d <= 256;
+ * w >= 1; s >= 0; mode is a swa_mode; in_dtype/out_dtype are swa_dtype values.
+ * scale <= 0 selects 1/sqrt(d). alibi_slopes: device float[H_q] of signed slopes, or NULL
+ * for no bias (a zero slope also means no bias on that head). rope_table: device float
+ * [rope_rows, d/2, 2] from swa_rope_table, or NULL for no rotation; rope_rows >= N.
+ * The bf16 path with d in {64, 128} runs on the matrix cores; other shapes run on a
+ * general vector kernel.
+ */
+typedef struct swa_prefill_params {
+    int64_t B, H_q, H_kv, N, d;
+    int64_t w;                 /* window length, counting the query itself            */
+    int64_t s;                 /* number of sink tokens (positions 0..s-1)             */
+    int32_t mode;              /* swa_mode                                             */
+    int32_t in_dtype;          /* swa_dtype of q, k, v                                 */
+    int32_t out_dtype;         /* swa_dtype of o                                       */
+    float scale;               /* <= 0: 1/sqrt(d)                                      */
+    const float *alibi_slopes; /* device float[H_q] or NULL                            */
+    const float *rope_table;   /* device float[rope_rows][d/2][2] (cos, sin) or NULL   */
+    int64_t rope_rows;
+} swa_prefill_params;
+
+swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k,
+                       const void *v, void *o, void *stream);
+
+/*
+ * RoPE angle table (SWAT page, "RoPE"; the RoFormer rotation it cites):
+ *   table[pos][t] = (cos(pos * theta^(-2t/d)), sin(pos * theta^(-2t/d))), pos in
+ *   [0, n_pos), t in [0, d/2), evaluated in float64 on the device and rounded to float32.
+ * table: device float[n_pos * d/2 * 2]. Requires n_pos >= 0, d even >= 2, theta > 0.
+ */
+swa_status swa_rope_table(float *table, int64_t n_pos, int64_t d, double theta, void *stream);
+
+/*
+ * In-place rotation of x [B, N, H, d] (dtype), row n of batch b at position pos0[b] + n.
+ * pos0: device int32[B]. rope_table: device [rope_rows, d/2, 2]. A row whose position is
+ * outside [0, rope_rows) is set to NaN.
+ */
+swa_status swa_rope_apply(void *x, int64_t B, int64_t N, int64_t H, int64_t d,
+                          const int32_t *pos0, const float *rope_table, int64_t rope_rows,
+                          int32_t dtype, void *stream);
+
+/*
+ * Ring-buffer KV cache for num_seqs sequences (Sliding Window Attention glossary, ring
+ * buffer: w slots, position i in slot i mod w, the oldest entry overwritten), plus a sink
+ * store for positions 0..s-1 (Sliding-window beats linear attention, SWA(64, 4)).
+ *   k_ring, v_ring : [num_seqs, H_kv, w, d]   keys stored rotated at their own position
+ *   k_sink, v_sink : [num_seqs, H_kv, s, d]   NULL when s == 0
+ * After positions 0..p of a sequence have been appended, slot t holds position
+ * p - ((p - t) mod w) when that is >= 0; the cache itself stores no positions.
+ */
+typedef struct swa_cache {
+    int64_t num_seqs, H_kv, w, s, d;
+    int32_t dtype;             /* swa_dtype of every cache tensor                      */
+    int32_t reserved;
+    void *k_ring, *v_ring;
+    void *k_sink, *v_sink;
+} swa_cache;
+
+/*
+ * Append n_new tokens per sequence: token n of sequence q has position pos0[q] + n; its key
+ * is rotated at that position (when rope_table is not NULL) and written with its value to
+ * slot position mod w; positions below s are also written to the sink store. When
+ * n_new > w, only the last w tokens reach the ring (the result equals appending one token
+ * at a time). k_new, v_new : [num_seqs, n_new, H_kv, d] (cache dtype); pos0: device
+ * int32[num_seqs]. A sequence whose pos0 is negative is skipped (nothing is written for
+ * it), which lets one call serve a subset of the sequences. A key whose position lies
+ * outside the rotation table is written as NaN.
+ */
+swa_status swa_kv_append(const swa_cache *c, const void *k_new, const void *v_new,
+                         const int32_t *pos0, int64_t n_new, const float *rope_table,
+                         int64_t rope_rows, void *stream);
+
+/*
+ * One query token per sequence over the ring cache. The query of sequence q sits at
+ * position q_pos[q] and its own token must already be appended. Its keys are the ring
+ * slots holding positions max(0, q_pos - w + 1) .. q_pos and the sink entries j < s that
+ * the window no longer covers; scores, bias and weights are as in swa_prefill.
+ *   q, o : [num_seqs, H_q, d]   (q not yet rotated; rotated here at q_pos)
+ * H_q % cache->H_kv == 0. workspace: device memory of at least
+ * swa_decode_workspace_bytes(p, c) bytes (may be NULL when that is 0).
+ */
+typedef struct swa_decode_params {
+    int64_t H_q;
+    int32_t mode;              /* swa_mode                                             */
+    int32_t out_dtype;         /* swa_dtype of o                                       */
+    float scale;               /* <= 0: 1/sqrt(d)                                      */
+    int32_t reserved;
+    const float *alibi_slopes; /* device float[H_q] or NULL                            */
+    const float *rope_table;   /* device [rope_rows, d/2, 2] or NULL                   */
+    int64_t rope_rows;
+} swa_decode_params;
+
+swa_status swa_decode(const swa_decode_params *p, const swa_cache *c, const void *q,
+                      const int32_t *q_pos, void *o, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* Bytes of workspace swa_decode needs for this problem (0 when it needs none). */
+size_t swa_decode_workspace_bytes(const swa_decode_params *p, const swa_cache *c);
+
+/* Static, human-readable text for a status code. */
+const char *swa_status_string(swa_status s);
+
+/* The hipError_t of the most recent SWA_ERR_HIP returned on this thread (0 if none). */
+int swa_last_hip_error(void);
+
+/* Version of this interface: major * 10000 + minor * 100 + patch. */
+int swa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSWA_SWA_H */

@@ -194,7 +194,8 @@ int swa_oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
  * a later token overwrites an earlier one in the same slot. Token n of sequence q sits at
  * position pos0[q] + n: its key is rotated at that position and written with its value to
  * slot position mod w, and the slot's position is recorded in ring_pos; a token whose
- * position is below s is also written to the sink store at index position.
+ * position is below s is also written to the sink store at index position. A sequence
+ * whose pos0 is negative receives nothing.
  * k_new/v_new [S, n_new, H_kv, d]; rings [S, H_kv, w, d]; ring_pos [S, w];
  * sinks [S, H_kv, s, d] (may be NULL when s == 0).
  */
@@ -207,9 +208,9 @@ int swa_oracle_append(int64_t S, int64_t Hkv, int64_t w, int64_t s, int64_t d, d
     double *kt = (double *)malloc(sizeof(double) * (size_t)d);
     if (!kt) return -1;
     for (int64_t q = 0; q < S; ++q) {
+        if (pos0[q] < 0) continue;  /* a sequence with a negative start is left untouched */
         for (int64_t n = 0; n < n_new; ++n) {
             int64_t p = pos0[q] + n;
-            if (p < 0) { free(kt); return -1; }
             int64_t slot = p % w;
             ring_pos[q * w + slot] = p;
             for (int64_t hk = 0; hk < Hkv; ++hk) {

@@ -1,0 +1,61 @@
+// swa_kernels.hpp - host-side launch interface between the C ABI layer and the kernels.
+// Arguments here are already validated; each launcher only enqueues work on the stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace swa {
+
+struct PrefillArgs {
+    int64_t B, Hq, Hkv, N, d, w, s;
+    int mode;           // 0 sigmoid, 1 softmax
+    int in_dt, out_dt;  // 0 float32, 1 bfloat16
+    float scale;        // resolved (> 0)
+    const float *slopes;
+    const float *rope;  // [rope_rows, d/2, 2] or null
+    int64_t rope_rows;
+};
+
+struct CacheArgs {
+    int64_t S, Hkv, w, s, d;
+    int dt;
+    void *k_ring, *v_ring, *k_sink, *v_sink;
+};
+
+struct DecodeArgs {
+    int64_t Hq;
+    int mode, out_dt;
+    float scale;
+    const float *slopes;
+    const float *rope;
+    int64_t rope_rows;
+};
+
+// General vector kernel: any even d <= 256, float32 or bfloat16 in/out.
+hipError_t launch_prefill_simt(const PrefillArgs &a, const void *q, const void *k,
+                               const void *v, void *o, hipStream_t st);
+
+// Matrix-core kernel: bfloat16 inputs, d in {64, 128}. Returns hipErrorNotSupported for
+// shapes it does not cover (the caller then uses the general kernel).
+bool prefill_mfma_supported(const PrefillArgs &a);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
+                               const void *v, void *o, hipStream_t st);
+
+hipError_t launch_rope_table(float *table, int64_t n_pos, int64_t d, double theta,
+                             hipStream_t st);
+hipError_t launch_rope_apply(void *x, int64_t B, int64_t N, int64_t H, int64_t d,
+                             const int32_t *pos0, const float *rope, int64_t rope_rows, int dt,
+                             hipStream_t st);
+
+hipError_t launch_kv_append(const CacheArgs &c, const void *k_new, const void *v_new,
+                            const int32_t *pos0, int64_t n_new, const float *rope,
+                            int64_t rope_rows, hipStream_t st);
+
+size_t decode_workspace_bytes(const DecodeArgs &a, const CacheArgs &c);
+hipError_t launch_decode(const DecodeArgs &a, const CacheArgs &c, const void *q,
+                         const int32_t *q_pos, void *o, void *ws, size_t ws_bytes,
+                         hipStream_t st);
+
+}  // namespace swa

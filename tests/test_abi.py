@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every symbol include/swa.h declares, and rejects bad
+arguments on the host before touching a device (no GPU needed: validation happens before
+any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_attention_prefill_amd as swa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(swa.LIB_PATH):
+        from sliding_window_attention_prefill_amd import build
+        build.build()
+    return swa.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(swa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    assert lib.swa_status_string(0) == b"ok"
+    assert lib.swa_status_string(1) == b"invalid argument"
+    assert lib.swa_status_string(2) == b"unsupported combination"
+    assert lib.swa_status_string(3) == b"HIP runtime error"
+    assert lib.swa_version() >= 100
+    assert lib.swa_last_hip_error() == 0
+
+
+def _params(**kw):
+    base = dict(B=1, H_q=4, H_kv=2, N=16, d=64, w=4, s=0, mode=0, in_dtype=1, out_dtype=0,
+                scale=0.0, alibi_slopes=None, rope_table=None, rope_rows=0)
+    base.update(kw)
+    return swa.PrefillParams(**base)
+
+
+DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H_q=3, H_kv=2), 1), (dict(H_kv=0), 1), (dict(B=-1), 1), (dict(N=-5), 1),
+    (dict(d=63), 1), (dict(d=0), 1), (dict(w=0), 1), (dict(s=-1), 1), (dict(mode=2), 1),
+    (dict(in_dtype=7), 1), (dict(out_dtype=-1), 1), (dict(scale=float("nan")), 1),
+    (dict(rope_table=0x2000, rope_rows=8), 1), (dict(d=258), 2),
+])
+def test_prefill_rejects_bad_arguments(lib, kw, status):
+    p = _params(**kw)
+    assert lib.swa_prefill(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, None) == status
+
+
+def test_prefill_rejects_null_tensors(lib):
+    p = _params()
+    assert lib.swa_prefill(ctypes.byref(p), None, DUMMY, DUMMY, DUMMY, None) == 1
+    assert lib.swa_prefill(None, DUMMY, DUMMY, DUMMY, DUMMY, None) == 1
+
+
+def test_rope_table_rejects_bad_arguments(lib):
+    assert lib.swa_rope_table(DUMMY, 10, 63, 1e4, None) == 1
+    assert lib.swa_rope_table(DUMMY, 10, 64, 0.0, None) == 1
+    assert lib.swa_rope_table(DUMMY, -1, 64, 1e4, None) == 1
+    assert lib.swa_rope_table(None, 10, 64, 1e4, None) == 1
+
+
+def _cache(**kw):
+    base = dict(num_seqs=2, H_kv=2, w=8, s=2, d=64, dtype=1, reserved=0, k_ring=0x1000,
+                v_ring=0x1000, k_sink=0x1000, v_sink=0x1000)
+    base.update(kw)
+    return swa.CacheDesc(**base)
+
+
+@pytest.mark.parametrize("kw", [dict(w=0), dict(s=-1), dict(d=7), dict(H_kv=0), dict(dtype=5),
+                                dict(k_ring=None), dict(k_sink=None)])
+def test_append_rejects_bad_cache(lib, kw):
+    c = _cache(**kw)
+    assert lib.swa_kv_append(ctypes.byref(c), DUMMY, DUMMY, DUMMY, 1, None, 0, None) == 1
+
+
+def test_decode_rejects_bad_arguments(lib):
+    c = _cache()
+    p = swa.DecodeParams(H_q=3, mode=1, out_dtype=0, scale=0.0, reserved=0, alibi_slopes=None,
+                         rope_table=None, rope_rows=0)
+    assert lib.swa_decode(ctypes.byref(p), ctypes.byref(c), DUMMY, DUMMY, DUMMY, None, 0,
+                          None) == 1
+    p.H_q = 4
+    p.mode = 9
+    assert lib.swa_decode(ctypes.byref(p), ctypes.byref(c), DUMMY, DUMMY, DUMMY, None, 0,
+                          None) == 1
+    p.mode = 1
+    assert lib.swa_decode(ctypes.byref(p), ctypes.byref(c), None, DUMMY, DUMMY, None, 0,
+                          None) == 1
+    assert lib.swa_decode_workspace_bytes(ctypes.byref(p), ctypes.byref(c)) == 0
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(swa, "_lib", None)
+    monkeypatch.setattr(swa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        swa.load()
