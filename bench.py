@@ -1,0 +1,236 @@
+"""Benchmark: sliding-window attention prefill (and ring-buffer decode) on one MI355X.
+
+One step = one swa_prefill over the SWAT-340M-shaped layer (B=8, H=16, N=4096, d=64,
+w=512, sigmoid + balanced ALiBi + RoPE, bf16 in / fp32 accumulate) with inputs already in
+HBM. The value is in-window TFLOP/s: 4 * B * H_q * d * sum_i |K(i)| per step, counting
+only the two contractions inside the band (SWAT: Sliding Window Attention Training, linear
+O(N w) cost), divided by the timed wall clock of K steps.
+
+The JSON line also carries:
+  roofline      the prefill kernel against the bf16 matrix-core peak, with its average
+                launch duration timed by HIP events on the launch stream;
+  decode        the SWA(64, 4) decode workload (64 sequences, 256 steps of ring append +
+                decode) in tokens/s and algorithmic GB/s against HBM peak;
+  cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "SWA prefill in-window TFLOP/s (% MFMA peak); decode tok/s (% HBM BW)"
+KERNEL_SRC = os.path.join(ROOT, "sliding_window_attention_prefill_amd", "csrc", "prefill_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic_swat340m.json")
+
+
+def in_window_keys(N: int, w: int, s: int) -> int:
+    """sum_i |K(i)| with |K(i)| = min(i+1, w+s)."""
+    c = w + s
+    if N <= c:
+        return N * (N + 1) // 2
+    return c * (c + 1) // 2 + (N - c) * c
+
+
+def prefill_flops(cfg) -> float:
+    return 4.0 * cfg.B * cfg.H_q * cfg.d * in_window_keys(cfg.N, cfg.w, cfg.s)
+
+
+def prefill_bytes(cfg, out_bytes: int) -> float:
+    el = 2 if cfg.dtype == "bf16" else 4
+    q = cfg.B * cfg.N * cfg.H_q * cfg.d
+    kv = cfg.B * cfg.N * cfg.H_kv * cfg.d
+    return float(q * el + 2 * kv * el + q * out_bytes)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed counter profile, if it was taken on the
+    current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
+    import torch
+    import sliding_window_attention_prefill_amd as swa
+    import swa_workloads as wl
+
+    q, k, v = wl.prefill_inputs(cfg, device="cuda")
+    slopes = wl.slopes_tensor(cfg.slopes, device="cuda")
+    table = swa.swa_rope_table(cfg.N, cfg.d, cfg.rope_theta) if cfg.rope_theta > 0 else None
+    out = torch.empty((cfg.B, cfg.N, cfg.H_q, cfg.d), dtype=out_dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        swa.swa_prefill(q, k, v, w=cfg.w, s=cfg.s, mode=cfg.mode, alibi_slopes=slopes,
+                        rope_table=table, out=out, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch HIP events on the launch stream give the kernel's average duration
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return wall, kernel_ms
+
+
+def bench_decode(cfg, out_dtype):
+    """256 steps of ring append + decode over 64 sequences, captured once in a HIP graph
+    (the per-step launches replay without host overhead); timed over the whole replay."""
+    import torch
+    import sliding_window_attention_prefill_amd as swa
+    import swa_workloads as wl
+
+    st = wl.decode_inputs(cfg, device="cuda")
+    T, S = cfg.steps, cfg.num_seqs
+    cache = swa.SwaCache(st.k_ring.clone(), st.v_ring.clone(), st.k_sink.clone(),
+                         st.v_sink.clone())
+    table = swa.swa_rope_table(cfg.len_hi + T + 1, cfg.d, cfg.rope_theta)
+    pos = torch.stack([(st.lengths + t).to(torch.int32) for t in range(T)]).contiguous()
+    out = torch.empty((T, S, cfg.H_q, cfg.d), dtype=out_dtype, device="cuda")
+    ws_bytes = swa.swa_decode_workspace_bytes(cache, cfg.H_q, mode=cfg.mode, out_dtype=out_dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def run_all():
+        for t in range(T):
+            swa.swa_kv_append(cache, st.k_steps[t], st.v_steps[t], pos[t], rope_table=table,
+                              stream=stream)
+            swa.swa_decode(st.q_steps[t], pos[t], cache, mode=cfg.mode, rope_table=table,
+                           out=out[t], workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        run_all()                     # warm-up, eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run_all()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    e0.record(cur)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    el = 2
+    ob = 4 if out_dtype == torch.float32 else 2
+    n_keys = cfg.w + cfg.s  # every sequence is past w + s tokens
+    per_step = (S * cfg.H_kv * n_keys * cfg.d * el * 2      # ring + sink K and V read
+                + S * cfg.H_q * cfg.d * el                  # q read
+                + S * cfg.H_q * cfg.d * ob                  # o written
+                + 2 * S * cfg.H_kv * cfg.d * el * 2)        # append: new k, v read + written
+    secs = ms / 1e3
+    gbs = per_step * T / secs / 1e9
+    return {
+        "workload": cfg.name, "steps": T, "sequences": S,
+        "ms_total": round(ms, 4), "us_per_step": round(ms * 1e3 / T, 3),
+        "tok_per_s": round(S * T / secs, 1),
+        "algorithmic_bytes_per_step": per_step,
+        "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "note": "cache stays resident in the 256 MB last-level cache across steps",
+    }
+
+
+def cpu_baseline(cfg, sample_batches: int):
+    """The float64 oracle on the first `sample_batches` sequences of the batch (all heads,
+    all rows), timed on the host; reported in the metric's unit."""
+    import oracle
+    import swa_workloads as wl
+
+    sub = cfg.with_(B=sample_batches)
+    q, k, v = wl.prefill_inputs(sub, device="cpu")
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, w=sub.w, s=sub.s, mode=sub.mode, slopes=sub.slopes,
+                   rope_theta=sub.rope_theta)
+    secs = time.perf_counter() - t0
+    return {
+        "value": round(prefill_flops(sub) / secs / 1e12, 6), "unit": "TFLOP/s",
+        "cores": oracle.threads(), "kind": "oracle",
+        "sample": "%d of %d sequences (all %d heads, all %d rows): %.1f s"
+                  % (sample_batches, cfg.B, cfg.H_q, cfg.N, secs),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c5"])
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-batches", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the workloads "
+              "fit one MI355X); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import swa_workloads as wl
+
+    cfg = {"c2": wl.C2, "c3": wl.C3, "c5": wl.C5}[args.workload]
+    out_dtype = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
+    wall, kernel_ms = bench_prefill(cfg, args.steps, args.warmup, out_dtype)
+    flops = prefill_flops(cfg)
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (kernel_ms / 1e3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "H_q": cfg.H_q, "H_kv": cfg.H_kv,
+                   "N": cfg.N, "d": cfg.d, "w": cfg.w, "s": cfg.s,
+                   "mode": "sigmoid" if cfg.mode == wl.SIGMOID else "softmax",
+                   "out_dtype": args.out_dtype, "in_window_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": stored_traffic(), "kernel_ms": round(kernel_ms, 5),
+                     "algorithmic_bytes": prefill_bytes(cfg, 4 if args.out_dtype == "f32" else 2)},
+    }
+    if not args.no_decode:
+        result["decode"] = bench_decode(wl.C4, torch.float32)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_batches)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -58,8 +58,10 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * scale <= 0 selects 1/sqrt(d). alibi_slopes: device float[H_q] of signed slopes, or NULL
  * for no bias (a zero slope also means no bias on that head). rope_table: device float
  * [rope_rows, d/2, 2] from swa_rope_table, or NULL for no rotation; rope_rows >= N.
- * The bf16 path with d in {64, 128} runs on the matrix cores; other shapes run on a
- * general vector kernel.
+ * bf16 inputs with d in {64, 128} and 16-byte aligned tensors run on the matrix cores,
+ * which form both products from float16 operands (rotated q and k, the weights, v) with
+ * float32 accumulation: those inputs must stay within the float16 range (|x| < 65504).
+ * Other shapes run on a general float32 vector kernel.
  */
 typedef struct swa_prefill_params {
     int64_t B, H_q, H_kv, N, d;

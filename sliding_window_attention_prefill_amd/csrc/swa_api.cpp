@@ -65,7 +65,12 @@ swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k
                        p->out_dtype, resolve_scale(p->scale, p->d), p->alibi_slopes,
                        p->rope_table, p->rope_table ? p->rope_rows : 0};
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (swa::prefill_mfma_supported(a)) return hip_status(swa::launch_prefill_mfma(a, q, k, v, o, st));
+    // the matrix-core kernel moves 16-byte vectors: it needs 16-byte aligned tensors
+    const bool aligned = ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                           reinterpret_cast<uintptr_t>(p->rope_table)) & 15) == 0;
+    if (aligned && swa::prefill_mfma_supported(a))
+        return hip_status(swa::launch_prefill_mfma(a, q, k, v, o, st));
     if ((a.B * a.N * a.Hq + 3) / 4 > 0x7fffffff) return SWA_ERR_UNSUPPORTED;
     return hip_status(swa::launch_prefill_simt(a, q, k, v, o, st));
 }

@@ -8,6 +8,8 @@ namespace swa {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -27,6 +29,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     f32x2_t f = {a, b};
     bf16x2_t h = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Two floats -> one dword holding two float16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    f32x2_t f = {a, b};
+    f16x2_t h = __builtin_convertvector(f, f16x2_t);
     return __builtin_bit_cast(uint32_t, h);
 }
 
