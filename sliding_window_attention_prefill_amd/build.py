@@ -23,6 +23,9 @@ SOURCES = ["swa_api.cpp", "prefill_simt.hip", "prefill_mfma.hip", "rope.hip", "d
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function",
+          # matrix instructions read and write VGPRs directly: the weights are computed on
+          # the VALU straight from the score accumulators
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", os.path.join(ROOT, "include")]
 
 
