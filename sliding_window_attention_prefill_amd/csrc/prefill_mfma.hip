@@ -23,10 +23,8 @@
 //     key permutation that matches the register layout of the score accumulators, so the
 //     weights feed the second product straight from registers.
 //   * Each wavefront computes S^T = K Q^T (32 keys x 32 queries per v_mfma_f32_32x32x16_f16)
-//     so that a lane holds one query's scores. The ALiBi bias enters through the
-//     accumulator's initial value (its per-lane part is fixed; the per-tile part is one
-//     wave-uniform shift), so each score costs a single FMA before the exponential.
-//     Weights are computed in base 2: sigmoid as 1/(1 + 2^t), softmax online with lazily
+//     so that a lane holds one query's scores. The scale and the ALiBi bias fold into two
+//     FMAs per score in base-2 units. Weights are computed in base 2: sigmoid as 1/(1 + 2^t), softmax online with lazily
 //     rescaled accumulators. O^T += V^T P^T accumulates in float32.
 //   * K/V tiles are fetched with buffer loads whose range check returns zeros past the
 //     sequence end; LDS is double-buffered with the next tile's loads issued before the
@@ -209,11 +207,10 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
 
 // One 64-key tile for one wavefront: S^T = K Q^T, weights, O^T += V^T P^T.
 // kind: 0 = every pair in the key set, 1 = cut by the window edges, 2 = also holds sinks.
-template <int D, int MODE>
+template <int D, int MODE, bool ALIBI>
 __device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl,
-                                          const f16x8_t (&qreg)[D / 16],
-                                          const f32x16_t (&binit)[2], f32x16_t (&oacc)[D / 32],
-                                          float &m_run, float &l_run, float cs, float shift,
+                                          const f16x8_t (&qreg)[D / 16], f32x16_t (&oacc)[D / 32],
+                                          float &m_run, float &l_run, float cs, float slope_l2,
                                           int kind, int dq, int jb, int w, int s, int qc, int g) {
     using T = Tile<D>;
     constexpr int KS = D / 16, DB = D / 32;
@@ -221,7 +218,8 @@ __device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         const f16x8_t a0 = *reinterpret_cast<const f16x8_t *>(kl + (kb * 32 + qc) * T::KSTR + g * 8);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qreg[0], binit[kb], 0, 0, 0);
+        const f32x16_t zero = {};
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qreg[0], zero, 0, 0, 0);
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) {
             const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + (kb * 32 + qc) * T::KSTR + ks * 16 + g * 8);
@@ -231,16 +229,26 @@ __device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl
     if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s);
     else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s);
 
+    const float bias0 = slope_l2 * (float)dq;  // slope log2(e) (i - j) for key_of = 0
     if (MODE == 0) {
         // sigma(x) = 1 / (1 + 2^t) with t = -x log2(e); an excluded key has t = +inf -> 0
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float t = fmaf(sacc[kb][e], -cs, -shift);
+                // -x log2(e) = -(cs * score + slope log2(e) (i - j)), i - j = dq - key_of
+                const float nb = ALIBI ? fmaf(slope_l2, (float)key_of(kb, e), -bias0) : 0.0f;
+                const float t = fmaf(sacc[kb][e], -cs, nb);
                 sacc[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
             }
     } else {
+        // base-2 logits x = cs * score + slope log2(e) (i - j); excluded keys stay -inf
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                sacc[kb][e] = ALIBI ? fmaf(sacc[kb][e], cs, fmaf(-slope_l2, (float)key_of(kb, e), bias0))
+                                    : sacc[kb][e] * cs;
         float mx[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -249,7 +257,6 @@ __device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl
         for (int u = 0; u < 4; ++u)
             mx[u] = fmaxf(mx[u], fmaxf(fmaxf(sacc[1][4 * u], sacc[1][4 * u + 1]), fmaxf(sacc[1][4 * u + 2], sacc[1][4 * u + 3])));
         float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
-        mt = fmaf(mt, cs, shift);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m_run, mt);
         // lazy rescale: keep the stale maximum while the new one exceeds it by less than 8
@@ -264,13 +271,12 @@ __device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl
             l_run *= corr;
             m_run = need ? m_new : m_run;
         }
-        const float off = shift - m_run;
         float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], cs, off));
+                const float pe = __builtin_amdgcn_exp2f(sacc[kb][e] - m_run);
                 ls[e & 3] += pe;
                 sacc[kb][e] = pe;
             }
@@ -294,8 +300,11 @@ __device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl
     }
 }
 
+// Register budget: 3 wavefronts per SIMD at d = 64, 2 at d = 128 (the LDS double buffer
+// allows 4 and 2 workgroups per CU respectively).
 template <int D, int GP, int MODE, bool ALIBI>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(MfmaParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
+void prefill_mfma_kernel(MfmaParams p) {
     using T = Tile<D>;
     constexpr int QP = 128 / GP;  // query positions per workgroup
     constexpr int WPH = 4 / GP;   // wavefronts per query head
@@ -352,16 +361,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(MfmaParams p) {
         }
     }
 
-    // ---- ALiBi: the accumulator starts at slope*log2e*(qc - 4g - key_of)/cs, the part of
-    // slope*(i - j) that is fixed per lane; the tile adds slope*log2e*(qa - j0) afterwards.
-    const float slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;
-    const float slope_acc = ALIBI ? slope_l2 / p.cs : 0.0f;
-    f32x16_t binit[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            binit[kb][e] = slope_acc * (float)(qc - 4 * g - key_of(kb, e));
+    const float slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;  // bias in base-2 units
 
     // ---- band of key tiles: sink tiles the window no longer covers, then the window
     const int lo_wg = q0 - p.w + 1 > 0 ? q0 - p.w + 1 : 0;
@@ -398,12 +398,11 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(MfmaParams p) {
         const bool full = (j0 + BK - 1 <= qa) && (qb - j0 < p.w || j0 + BK - 1 < p.s);
 
         if (!empty) {
-            const float shift = ALIBI ? slope_l2 * (float)(qa - j0) : 0.0f;  // wave-uniform
             const int dq = i - j0 - 4 * g;   // element (kb, e) has i - j = dq - key_of(kb, e)
             const int jb = j0 + 4 * g;       // and key j = jb + key_of(kb, e)
             const int kind = full ? 0 : (j0 >= p.s ? 1 : 2);
-            tile_math<D, MODE>(kl, vl, qreg, binit, oacc, m_run, l_run, cs, shift, kind, dq, jb,
-                               p.w, p.s, qc, g);
+            tile_math<D, MODE, ALIBI>(kl, vl, qreg, oacc, m_run, l_run, cs, slope_l2, kind, dq,
+                                      jb, p.w, p.s, qc, g);
         }
         if (it + 1 < n_tiles) stage_store<D>(st, lds + ((it + 1) & 1) * T::BUF, tid, rope);
         __syncthreads();
