@@ -105,8 +105,9 @@ def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
 
 
 def bench_decode(cfg, out_dtype):
-    """256 steps of ring append + decode over 64 sequences, captured once in a HIP graph
-    (the per-step launches replay without host overhead); timed over the whole replay."""
+    """256 steps of ring append + decode over 64 sequences (one fused launch per step),
+    captured once in a HIP graph so the launches replay without host overhead; timed over
+    the whole replay."""
     import torch
     import sliding_window_attention_prefill_amd as swa
     import swa_workloads as wl
@@ -122,12 +123,15 @@ def bench_decode(cfg, out_dtype):
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.Stream()
 
+    k_steps = st.k_steps[:, :, 0].contiguous()   # [T, S, H_kv, d]
+    v_steps = st.v_steps[:, :, 0].contiguous()
+
     def run_all():
+        # one launch per step: append the step's token and answer its query
         for t in range(T):
-            swa.swa_kv_append(cache, st.k_steps[t], st.v_steps[t], pos[t], rope_table=table,
-                              stream=stream)
-            swa.swa_decode(st.q_steps[t], pos[t], cache, mode=cfg.mode, rope_table=table,
-                           out=out[t], workspace=ws, stream=stream)
+            swa.swa_decode_append(st.q_steps[t], k_steps[t], v_steps[t], pos[t], cache,
+                                  mode=cfg.mode, rope_table=table, out=out[t], workspace=ws,
+                                  stream=stream)
 
     with torch.cuda.stream(stream):
         run_all()                     # warm-up, eager

@@ -151,6 +151,20 @@ swa_status swa_decode(const swa_decode_params *p, const swa_cache *c, const void
                       const int32_t *q_pos, void *o, void *workspace, size_t workspace_bytes,
                       void *stream);
 
+/*
+ * One decode step with the new token's append fused in. For each sequence q, the token at
+ * position q_pos[q] - key k_new[q] (not yet rotated) and value v_new[q], both [num_seqs,
+ * H_kv, d] in the cache dtype - is written to the ring (and to the sink store when
+ * q_pos[q] < s) exactly as swa_kv_append with n_new = 1 writes it, and query q[q] is then
+ * answered as swa_decode answers it. One launch instead of two: every (sequence, kv head)
+ * is handled by a single workgroup, which uses the token it wrote without reading it back.
+ * A sequence whose q_pos is invalid (negative, or outside the rotation table) gets NaN
+ * outputs and its cache is left untouched. Other arguments as in swa_decode.
+ */
+swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, const void *q,
+                             const void *k_new, const void *v_new, const int32_t *q_pos,
+                             void *o, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace swa_decode needs for this problem (0 when it needs none). */
 size_t swa_decode_workspace_bytes(const swa_decode_params *p, const swa_cache *c);
 

@@ -56,8 +56,8 @@ class DecodeParams(ctypes.Structure):
 
 
 EXPORTS = ["swa_prefill", "swa_rope_table", "swa_rope_apply", "swa_kv_append", "swa_decode",
-           "swa_decode_workspace_bytes", "swa_status_string", "swa_last_hip_error",
-           "swa_version"]
+           "swa_decode_append", "swa_decode_workspace_bytes", "swa_status_string",
+           "swa_last_hip_error", "swa_version"]
 
 _lib = None
 
@@ -84,6 +84,9 @@ def load():
         lib.swa_decode.argtypes = [P(DecodeParams), P(CacheDesc), c_ptr, c_ptr, c_ptr, c_ptr,
                                    ctypes.c_size_t, c_ptr]
         lib.swa_decode.restype = ctypes.c_int
+        lib.swa_decode_append.argtypes = [P(DecodeParams), P(CacheDesc), c_ptr, c_ptr, c_ptr, c_ptr,
+                                          c_ptr, c_ptr, ctypes.c_size_t, c_ptr]
+        lib.swa_decode_append.restype = ctypes.c_int
         lib.swa_decode_workspace_bytes.argtypes = [P(DecodeParams), P(CacheDesc)]
         lib.swa_decode_workspace_bytes.restype = ctypes.c_size_t
         lib.swa_status_string.argtypes = [ctypes.c_int]
@@ -299,4 +302,43 @@ def swa_decode(q: torch.Tensor, q_pos: torch.Tensor, cache: SwaCache, *, mode=SW
     _check("swa_decode", load().swa_decode(ctypes.byref(p), ctypes.byref(cache.desc), _ptr(q),
                                            _ptr(q_pos), _ptr(out), _ptr(workspace), ws_bytes,
                                            _stream(q.device, stream)))
+    return out
+
+
+def swa_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      q_pos: torch.Tensor, cache: SwaCache, *, mode=SWA_SOFTMAX,
+                      scale: float = 0.0, alibi_slopes: Optional[torch.Tensor] = None,
+                      rope_table: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Append one token per sequence (k_new, v_new [S, H_kv, d], key not rotated) at q_pos
+    and answer q [S, H_q, d] there, in one launch."""
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (q_pos, "q_pos")):
+        _dev(t, n)
+    if q.dim() != 3 or q.shape[0] != cache.S or q.shape[2] != cache.d:
+        raise ValueError("q must be [S, H_q, d]")
+    if tuple(k_new.shape) != (cache.S, cache.H_kv, cache.d) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [S, H_kv, d]")
+    if q.dtype != cache.dtype or k_new.dtype != cache.dtype or v_new.dtype != cache.dtype:
+        raise ValueError("q, k_new, v_new must have the cache dtype")
+    if q_pos.dtype != torch.int32 or q_pos.numel() != cache.S:
+        raise ValueError("q_pos must be int32[S]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _dev(out, "out")
+    if alibi_slopes is not None:
+        _dev(alibi_slopes, "alibi_slopes")
+    if rope_table is not None:
+        _dev(rope_table, "rope_table")
+    p = _decode_params(q.shape[1], mode, scale, alibi_slopes, rope_table, _dt(out))
+    need = int(load().swa_decode_workspace_bytes(ctypes.byref(p), ctypes.byref(cache.desc)))
+    ws_bytes = 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("swa_decode_append",
+           load().swa_decode_append(ctypes.byref(p), ctypes.byref(cache.desc), _ptr(q),
+                                    _ptr(k_new), _ptr(v_new), _ptr(q_pos), _ptr(out),
+                                    _ptr(workspace), ws_bytes, _stream(q.device, stream)))
     return out

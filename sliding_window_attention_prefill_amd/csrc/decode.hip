@@ -207,6 +207,323 @@ __global__ __launch_bounds__(256) void decode_general_kernel(DecodeGen a, const 
     }
 }
 
+// Fast decode for a bf16 cache, d in {64, 128}, up to 8 query heads per kv head. One block
+// of 256 threads per (sequence, kv head) issues every K and V load of a 128-key chunk before
+// any arithmetic, so the whole working set of the step is in flight at once:
+//   score pass: 4 threads per key, each a quarter of the row, reduced with two shuffles;
+//   weights:    one wavefront per head, keys across lanes (wavefront max / sum reductions);
+//   value pass: thread (key group, 8-column chunk) accumulates 8 columns for every head,
+//               then the key groups are summed through LDS.
+// With APPEND the block first writes the new token (rotated key, value) to its ring slot
+// and sink entry, keeps it in LDS and uses that copy for position q_pos, so the slot it
+// wrote is never read back within the launch.
+struct DecodeFast {
+    int S, Hq, Hkv, G, w, s, mode;
+    float cs;            // scale * log2(e): scores are kept in base-2 units
+    const float *slopes;
+    const float *rope;
+    int64_t rope_rows;
+    uint16_t *k_ring, *v_ring, *k_sink, *v_sink;
+};
+
+constexpr int DEC_KC = 128;  // keys per chunk
+
+template <int D>
+struct DecLds {
+    static constexpr int C8 = D / 8;          // 16-byte chunks per row
+    static constexpr int KG = 256 / C8;       // key groups of the value pass
+    static constexpr int VK = DEC_KC / KG;    // keys per thread in the value pass
+    static constexpr int QE = D / 4;          // elements per thread in the score pass
+};
+
+template <int D>
+size_t decode_fast_lds(int G) {
+    using L = DecLds<D>;
+    return sizeof(float) * ((size_t)G * D + (size_t)G * DEC_KC + 2 * D + 3 * 8 +
+                            (size_t)L::KG * G * D);
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+template <int D, int G, int OUT, bool APPEND>
+__global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const uint16_t *__restrict__ q,
+                                                          const int32_t *__restrict__ q_pos,
+                                                          void *__restrict__ o,
+                                                          const uint16_t *__restrict__ k_new,
+                                                          const uint16_t *__restrict__ v_new) {
+    using L = DecLds<D>;
+    extern __shared__ float lds[];
+    float *qs = lds;                    // [G][D] rotated queries * scale * log2(e)
+    float *sc = qs + G * D;             // [G][KC] scores, then weights
+    float *kn = sc + G * DEC_KC;        // [D] appended key (as stored)
+    float *vn = kn + D;                 // [D] appended value
+    float *ml = vn + D;                 // [3][8] max, sum, correction per head
+    float *red = ml + 24;               // [KG][G][D] partial outputs
+
+    const int sq = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int p = q_pos[sq];
+    const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
+    if (!valid) {
+        for (int idx = tid; idx < G * D; idx += 256)
+            Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G) * D + idx, qnan());
+        return;
+    }
+    const int64_t ring_base = ((int64_t)sq * a.Hkv + hk) * a.w * D;
+    const int64_t sink_base = ((int64_t)sq * a.Hkv + hk) * a.s * D;
+    const int half = D / 2;
+
+    // ---- the new token (fused append) and the queries, rotated at position p
+    if (APPEND && tid < half) {
+        const int64_t src = ((int64_t)sq * a.Hkv + hk) * D + 2 * tid;
+        float k0 = bf16_bits_to_f32(k_new[src]), k1 = bf16_bits_to_f32(k_new[src + 1]);
+        const uint32_t vv = *reinterpret_cast<const uint32_t *>(v_new + src);
+        if (a.rope) {
+            const float2 cs = reinterpret_cast<const float2 *>(a.rope)[(int64_t)p * half + tid];
+            const float r0 = fmaf(-k1, cs.y, k0 * cs.x);
+            k1 = fmaf(k0, cs.y, k1 * cs.x);
+            k0 = r0;
+        }
+        const uint32_t kk = pack_bf16x2(k0, k1);
+        *reinterpret_cast<uint32_t *>(a.k_ring + ring_base + (int64_t)(p % a.w) * D + 2 * tid) = kk;
+        *reinterpret_cast<uint32_t *>(a.v_ring + ring_base + (int64_t)(p % a.w) * D + 2 * tid) = vv;
+        if (p < a.s) {
+            *reinterpret_cast<uint32_t *>(a.k_sink + sink_base + (int64_t)p * D + 2 * tid) = kk;
+            *reinterpret_cast<uint32_t *>(a.v_sink + sink_base + (int64_t)p * D + 2 * tid) = vv;
+        }
+        kn[2 * tid] = bf16_bits_to_f32(kk & 0xffffu);
+        kn[2 * tid + 1] = bf16_bits_to_f32(kk >> 16);
+        vn[2 * tid] = bf16_bits_to_f32(vv & 0xffffu);
+        vn[2 * tid + 1] = bf16_bits_to_f32(vv >> 16);
+    }
+    for (int idx = tid; idx < G * half; idx += 256) {
+        const int g = idx / half, t = idx % half;
+        const int64_t src = ((int64_t)sq * a.Hq + hk * G + g) * D + 2 * t;
+        float x0 = bf16_bits_to_f32(q[src]), x1 = bf16_bits_to_f32(q[src + 1]);
+        if (a.rope) {
+            const float2 cs = reinterpret_cast<const float2 *>(a.rope)[(int64_t)p * half + t];
+            const float r0 = fmaf(-x1, cs.y, x0 * cs.x);
+            x1 = fmaf(x0, cs.y, x1 * cs.x);
+            x0 = r0;
+        }
+        qs[g * D + 2 * t] = x0 * a.cs;
+        qs[g * D + 2 * t + 1] = x1 * a.cs;
+    }
+    if (tid < 8) {
+        ml[tid] = -INFINITY;
+        ml[8 + tid] = 0.0f;
+        ml[16 + tid] = 1.0f;
+    }
+    const int lo = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
+    const int n_sink = a.s < lo ? a.s : lo;
+    const int n_keys = n_sink + (p - lo + 1);
+
+    // value-pass ownership: 8 columns, keys kg, kg + KG, ...
+    const int c8 = tid % L::C8, kg = tid / L::C8;
+    float acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[g][c] = 0.0f;
+    __syncthreads();
+
+    for (int c0 = 0; c0 < n_keys; c0 += DEC_KC) {
+        const int nk = n_keys - c0 < DEC_KC ? n_keys - c0 : DEC_KC;
+        // -- issue every load of the chunk: two score slots and VK value rows per thread
+        uint4 kx[2][L::QE / 8];
+        int kpos[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int slot = tid + 256 * r, e = slot / 4, qq = slot % 4;
+            const int ee = c0 + e;
+            const int P = ee < n_sink ? ee : lo + (ee - n_sink);
+            kpos[r] = P;
+            const bool from_mem = e < nk && !(APPEND && P == p);
+            const uint16_t *row = ee < n_sink ? a.k_sink + sink_base + (int64_t)P * D
+                                              : a.k_ring + ring_base + (int64_t)(P % a.w) * D;
+#pragma unroll
+            for (int u = 0; u < L::QE / 8; ++u)
+                kx[r][u] = from_mem ? ld16(row + qq * L::QE + 8 * u) : make_uint4(0, 0, 0, 0);
+        }
+        uint4 vx[L::VK];
+        int vpos[L::VK];
+#pragma unroll
+        for (int r = 0; r < L::VK; ++r) {
+            const int e = kg + L::KG * r, ee = c0 + e;
+            const int P = ee < n_sink ? ee : lo + (ee - n_sink);
+            vpos[r] = P;
+            const bool from_mem = e < nk && !(APPEND && P == p);
+            const uint16_t *row = ee < n_sink ? a.v_sink + sink_base + (int64_t)P * D
+                                              : a.v_ring + ring_base + (int64_t)(P % a.w) * D;
+            vx[r] = from_mem ? ld16(row + 8 * c8) : make_uint4(0, 0, 0, 0);
+        }
+        // -- scores (base 2): q.k * scale log2e + slope log2e (p - P)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int slot = tid + 256 * r, e = slot / 4, qq = slot % 4;
+            const int P = kpos[r];
+            float kf[L::QE];
+#pragma unroll
+            for (int u = 0; u < L::QE / 8; ++u) {
+                const uint32_t w4[4] = {kx[r][u].x, kx[r][u].y, kx[r][u].z, kx[r][u].w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    kf[8 * u + 2 * m] = __uint_as_float(w4[m] << 16);
+                    kf[8 * u + 2 * m + 1] = __uint_as_float(w4[m] & 0xffff0000u);
+                }
+            }
+            if (APPEND && P == p && e < nk) {
+#pragma unroll
+                for (int c = 0; c < L::QE; ++c) kf[c] = kn[qq * L::QE + c];
+            }
+            float part[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float acc_d = 0.0f;
+#pragma unroll
+                for (int c = 0; c < L::QE; ++c) acc_d = fmaf(qs[g * D + qq * L::QE + c], kf[c], acc_d);
+                part[g] = acc_d;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                part[g] += __shfl_xor(part[g], 1, 64);
+                part[g] += __shfl_xor(part[g], 2, 64);
+            }
+            if (qq == 0 && e < nk) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float slope = a.slopes ? a.slopes[hk * G + g] * 1.4426950408889634f : 0.0f;
+                    sc[g * DEC_KC + e] = fmaf(slope, (float)(p - P), part[g]);
+                }
+            }
+        }
+        __syncthreads();
+        // -- weights: one wavefront per head, keys across lanes
+        for (int g = wave; g < G; g += 4) {
+            float x0 = lane < nk ? sc[g * DEC_KC + lane] : -INFINITY;
+            float x1 = lane + 64 < nk ? sc[g * DEC_KC + lane + 64] : -INFINITY;
+            if (a.mode == 0) {
+                x0 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x0));
+                x1 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x1));
+            } else {
+                const float m_old = ml[g];
+                const float m_new = fmaxf(m_old, wave_max(fmaxf(x0, x1)));
+                x0 = __builtin_amdgcn_exp2f(x0 - m_new);
+                x1 = __builtin_amdgcn_exp2f(x1 - m_new);
+                const float sum = wave_sum(x0 + x1);
+                if (lane == 0) {
+                    const float corr = __builtin_amdgcn_exp2f(m_old - m_new);
+                    ml[8 + g] = ml[8 + g] * corr + sum;
+                    ml[16 + g] = corr;
+                    ml[g] = m_new;
+                }
+            }
+            if (lane < nk) sc[g * DEC_KC + lane] = x0;
+            if (lane + 64 < nk) sc[g * DEC_KC + lane + 64] = x1;
+        }
+        __syncthreads();
+        // -- values: acc[g][c] = acc * corr + sum_e w[g][e] v[e][8 c8 + c]
+        if (a.mode == 1) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float corr = ml[16 + g];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[g][c] *= corr;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < L::VK; ++r) {
+            const int e = kg + L::KG * r;
+            if (e < nk) {
+                float vf[8];
+                const uint32_t w4[4] = {vx[r].x, vx[r].y, vx[r].z, vx[r].w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    vf[2 * m] = __uint_as_float(w4[m] << 16);
+                    vf[2 * m + 1] = __uint_as_float(w4[m] & 0xffff0000u);
+                }
+                if (APPEND && vpos[r] == p) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) vf[c] = vn[8 * c8 + c];
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float wgt = sc[g * DEC_KC + e];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(wgt, vf[c], acc[g][c]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // ---- sum the key groups and normalise
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) red[(kg * G + g) * D + 8 * c8 + c] = acc[g][c];
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int g = idx / D, col = idx % D;
+        float sum = 0.0f;
+        for (int r = 0; r < L::KG; ++r) sum += red[(r * G + g) * D + col];
+        if (a.mode == 1) sum /= ml[8 + g];
+        Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + g) * D + col, sum);
+    }
+}
+
+template <int D, int G, int OUT, bool APPEND>
+hipError_t launch_fast_t(const DecodeFast &f, const void *q, const int32_t *q_pos, void *o,
+                         const void *k_new, const void *v_new, hipStream_t st) {
+    const size_t lds = decode_fast_lds<D>(G);
+    hipLaunchKernelGGL((decode_fast_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv)),
+                       dim3(256), lds, st, f, static_cast<const uint16_t *>(q), q_pos, o,
+                       static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
+    return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_fast_g(const DecodeFast &f, int out_dt, const void *q, const int32_t *q_pos,
+                         void *o, const void *k_new, const void *v_new, hipStream_t st) {
+    const bool app = k_new != nullptr;
+    if (out_dt == 0) return app ? launch_fast_t<D, G, 0, true>(f, q, q_pos, o, k_new, v_new, st)
+                                : launch_fast_t<D, G, 0, false>(f, q, q_pos, o, k_new, v_new, st);
+    return app ? launch_fast_t<D, G, 1, true>(f, q, q_pos, o, k_new, v_new, st)
+               : launch_fast_t<D, G, 1, false>(f, q, q_pos, o, k_new, v_new, st);
+}
+
+template <int D>
+hipError_t launch_fast_d(const DecodeFast &f, int out_dt, const void *q, const int32_t *q_pos,
+                         void *o, const void *k_new, const void *v_new, hipStream_t st) {
+    switch (f.G) {
+        case 1: return launch_fast_g<D, 1>(f, out_dt, q, q_pos, o, k_new, v_new, st);
+        case 2: return launch_fast_g<D, 2>(f, out_dt, q, q_pos, o, k_new, v_new, st);
+        case 4: return launch_fast_g<D, 4>(f, out_dt, q, q_pos, o, k_new, v_new, st);
+        default: return launch_fast_g<D, 8>(f, out_dt, q, q_pos, o, k_new, v_new, st);
+    }
+}
+
+bool decode_fast_ok(const DecodeArgs &a, const CacheArgs &c) {
+    const int64_t G = a.Hq / c.Hkv;
+    if (c.dt != 1 || (c.d != 64 && c.d != 128) || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
+    if (c.S * c.Hkv > 0x7fffffff || c.w > (1 << 30) || c.s > (1 << 30)) return false;
+    const size_t lds = c.d == 64 ? decode_fast_lds<64>((int)G) : decode_fast_lds<128>((int)G);
+    return lds <= 64 * 1024;
+}
+
+hipError_t launch_decode_fast(const DecodeArgs &a, const CacheArgs &c, const void *q,
+                              const int32_t *q_pos, void *o, const void *k_new, const void *v_new,
+                              hipStream_t st) {
+    DecodeFast f;
+    f.S = (int)c.S; f.Hq = (int)a.Hq; f.Hkv = (int)c.Hkv; f.G = (int)(a.Hq / c.Hkv);
+    f.w = (int)c.w; f.s = (int)c.s; f.mode = a.mode;
+    f.cs = a.scale * 1.4426950408889634f;
+    f.slopes = a.slopes; f.rope = a.rope; f.rope_rows = a.rope_rows;
+    f.k_ring = static_cast<uint16_t *>(c.k_ring); f.v_ring = static_cast<uint16_t *>(c.v_ring);
+    f.k_sink = static_cast<uint16_t *>(c.k_sink); f.v_sink = static_cast<uint16_t *>(c.v_sink);
+    if (c.d == 64) return launch_fast_d<64>(f, a.out_dt, q, q_pos, o, k_new, v_new, st);
+    return launch_fast_d<128>(f, a.out_dt, q, q_pos, o, k_new, v_new, st);
+}
+
 size_t decode_general_lds(int64_t G, int64_t d, int KC) {
     return sizeof(float) * (size_t)(G * d + 2 * KC * (d + 1) + G * KC + G * d + 3 * G) +
            sizeof(int) * (size_t)KC;
@@ -233,6 +550,7 @@ size_t decode_workspace_bytes(const DecodeArgs &, const CacheArgs &) { return 0;
 hipError_t launch_decode(const DecodeArgs &a, const CacheArgs &c, const void *q,
                          const int32_t *q_pos, void *o, void *, size_t, hipStream_t st) {
     if (c.S == 0) return hipSuccess;
+    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, nullptr, nullptr, st);
     const int64_t G = a.Hq / c.Hkv;
     int KC = 64;
     while (KC > 8 && decode_general_lds(G, c.d, KC) > 64 * 1024) KC /= 2;
@@ -250,6 +568,17 @@ hipError_t launch_decode(const DecodeArgs &a, const CacheArgs &c, const void *q,
     else
         hipLaunchKernelGGL((decode_general_kernel<1, 1>), grid, dim3(256), lds, st, g, q, q_pos, o, KC);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const DecodeArgs &a, const CacheArgs &c, const void *q,
+                                const void *k_new, const void *v_new, const int32_t *q_pos,
+                                void *o, void *ws, size_t ws_bytes, hipStream_t st) {
+    if (c.S == 0) return hipSuccess;
+    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, k_new, v_new, st);
+    // general shapes: the append kernel, then the decode kernel, in stream order
+    const hipError_t e = launch_kv_append(c, k_new, v_new, q_pos, 1, a.rope, a.rope_rows, st);
+    if (e != hipSuccess) return e;
+    return launch_decode(a, c, q, q_pos, o, ws, ws_bytes, st);
 }
 
 }  // namespace swa

@@ -161,4 +161,21 @@ swa_status swa_decode(const swa_decode_params *p, const swa_cache *c, const void
     return hip_status(e);
 }
 
+swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, const void *q,
+                             const void *k_new, const void *v_new, const int32_t *q_pos,
+                             void *o, void *workspace, size_t workspace_bytes, void *stream) {
+    swa_status st = check_decode(p, c);
+    if (st != SWA_OK) return st;
+    if (c->num_seqs > 0 && (!q || !q_pos || !o || !k_new || !v_new)) return SWA_ERR_INVALID_ARGUMENT;
+    const swa::DecodeArgs a = decode_args(p, c->d);
+    const swa::CacheArgs ca = cache_args(c);
+    const size_t need = swa::decode_workspace_bytes(a, ca);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SWA_ERR_INVALID_ARGUMENT;
+    if (c->num_seqs * c->H_kv > 0x7fffffff) return SWA_ERR_UNSUPPORTED;
+    const hipError_t e = swa::launch_decode_append(a, ca, q, k_new, v_new, q_pos, o, workspace,
+                                                   workspace_bytes, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return SWA_ERR_UNSUPPORTED;
+    return hip_status(e);
+}
+
 }  // extern "C"

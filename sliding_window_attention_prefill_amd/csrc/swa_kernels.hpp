@@ -57,5 +57,9 @@ size_t decode_workspace_bytes(const DecodeArgs &a, const CacheArgs &c);
 hipError_t launch_decode(const DecodeArgs &a, const CacheArgs &c, const void *q,
                          const int32_t *q_pos, void *o, void *ws, size_t ws_bytes,
                          hipStream_t st);
+// Append one token per sequence at q_pos, then decode (one launch where possible).
+hipError_t launch_decode_append(const DecodeArgs &a, const CacheArgs &c, const void *q,
+                                const void *k_new, const void *v_new, const int32_t *q_pos,
+                                void *o, void *ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace swa

@@ -318,3 +318,85 @@ def test_decode_c4_full_workload():
             mr, sr = assert_parity(out, ref, "bf16", "C4 step %d" % t)
             worst = (max(worst[0], mr), max(worst[1], sr))
     print("C4 worst max_rel %.2e sum_rel %.2e" % worst)
+
+
+@pytest.mark.parametrize("mode", [wl.SIGMOID, wl.SOFTMAX])
+@pytest.mark.parametrize("S,Hq,Hkv,d,w,s", [(5, 8, 2, 128, 16, 3), (3, 4, 4, 64, 7, 0),
+                                             (4, 32, 8, 128, 64, 4), (3, 16, 2, 128, 200, 2),
+                                             (2, 2, 1, 96, 33, 40), (3, 8, 1, 64, 20, 1)])
+def test_fused_append_decode_matches_oracle(mode, S, Hq, Hkv, d, w, s):
+    """swa_decode_append (one launch: append the step's token, then answer its query) equals
+    the oracle ring step by step, and leaves the same cache contents as the oracle."""
+    g = torch.Generator().manual_seed(S * 7 + w + d)
+    steps = 20
+    start = torch.randint(0, 3 * w, (S,), generator=g)
+    start[0] = 0
+    slopes = tuple(np.linspace(-0.4, 0.6, Hq).tolist())
+    theta = 1e4
+    table = swa.swa_rope_table(int(start.max()) + steps + 1, d, theta)
+    cache = swa.SwaCache.empty(S, Hkv, w, s, d, torch.bfloat16)
+    ring = oracle.Ring(S, Hkv, w, s, d)
+    sl = torch.tensor(slopes, dtype=torch.float32, device=DEV)
+    for q_ in range(S):
+        n0 = int(start[q_])
+        if n0 == 0:
+            continue
+        pos_all = torch.full((S,), -1, dtype=torch.int32)
+        pos_all[q_] = 0
+        kh = torch.randn((S, n0, Hkv, d), generator=g).to(torch.bfloat16)
+        vh = torch.randn((S, n0, Hkv, d), generator=g).to(torch.bfloat16)
+        swa.swa_kv_append(cache, kh.to(DEV), vh.to(DEV), pos_all.to(DEV), rope_table=table)
+        ring.append(kh, vh, pos_all, rope_theta=theta)
+    for step in range(steps):
+        pos = (start + step).to(torch.int32)
+        kn = torch.randn((S, Hkv, d), generator=g).to(torch.bfloat16)
+        vn = torch.randn((S, Hkv, d), generator=g).to(torch.bfloat16)
+        qn = torch.randn((S, Hq, d), generator=g).to(torch.bfloat16)
+        out = swa.swa_decode_append(qn.to(DEV), kn.to(DEV), vn.to(DEV), pos.to(DEV), cache,
+                                    mode=mode, alibi_slopes=sl, rope_table=table,
+                                    out_dtype=torch.float32)
+        ring.append(kn[:, None], vn[:, None], pos, rope_theta=theta)
+        ref = ring.decode(qn, pos, H_q=Hq, mode=mode, slopes=slopes, rope_theta=theta)
+        torch.cuda.synchronize()
+        assert_parity(out, ref, "bf16", "fused step %d" % step)
+    vr = cache.v_ring.cpu().double().numpy()
+    kr = cache.k_ring.cpu().double().numpy()
+    for q_ in range(S):
+        for t in range(w):
+            if ring.pos[q_, t] >= 0:
+                np.testing.assert_array_equal(vr[q_, :, t], ring.v[q_, :, t])
+                np.testing.assert_allclose(kr[q_, :, t], ring.k[q_, :, t], rtol=1e-2, atol=1e-2)
+
+
+def test_fused_append_decode_selection_is_bit_exact():
+    """q = k = 0, sigmoid, v = bits of the position, through the fused step: the output
+    identifies the key set exactly, across ring wrap-around and the sink store."""
+    S, Hq, Hkv, d, w, s = 2, 8, 2, 128, 16, 4
+    bits = 7
+    cache = swa.SwaCache.empty(S, Hkv, w, s, d, torch.bfloat16)
+    table = swa.swa_rope_table(200, d, 1e4)
+    for step in range(70):
+        pos = torch.tensor([step, step + 30], dtype=torch.int32)
+        if step == 0:
+            # sequence 1 receives positions 0..29 first
+            pos_all = torch.tensor([-1, 0], dtype=torch.int32)
+            vh = torch.zeros((S, 30, Hkv, d))
+            for j in range(30):
+                for c in range(bits):
+                    vh[1, j, :, c] = float((j >> c) & 1)
+            swa.swa_kv_append(cache, torch.zeros((S, 30, Hkv, d), dtype=torch.bfloat16, device=DEV),
+                              vh.to(torch.bfloat16).to(DEV), pos_all.to(DEV), rope_table=table)
+        vn = torch.zeros((S, Hkv, d))
+        for q_ in range(S):
+            for c in range(bits):
+                vn[q_, :, c] = float((int(pos[q_]) >> c) & 1)
+        out = swa.swa_decode_append(torch.zeros((S, Hq, d), dtype=torch.bfloat16, device=DEV),
+                                    torch.zeros((S, Hkv, d), dtype=torch.bfloat16, device=DEV),
+                                    vn.to(torch.bfloat16).to(DEV), pos.to(DEV), cache,
+                                    mode=swa.SWA_SIGMOID, rope_table=table,
+                                    out_dtype=torch.float32).cpu().numpy()
+        for q_ in range(S):
+            p = int(pos[q_])
+            keys = np.array([j for j in range(p + 1) if p - j < w or j < s])
+            for c in range(bits):
+                assert np.all(out[q_, :, c] == 0.5 * ((keys >> c) & 1).sum()), (step, q_, c)
