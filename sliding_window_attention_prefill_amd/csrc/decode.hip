@@ -471,9 +471,229 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
     }
 }
 
+// Whole-window decode for a bf16 cache when the ring and the sink store together hold at
+// most 128 rows (w + s <= 128, e.g. SWA(64, 4)). The rows a query can read are then known
+// without its position: every ring slot and every sink entry. So the block issues all of
+// its loads - queries, every K and V row, the new token - before the position arrives, and
+// only then decides which rows count (ring slot t holds position p - ((p - t) mod w) when
+// that is >= 0; sink j counts when the window no longer covers it) and what bias each gets.
+// Thread (row group, 16-byte column chunk) owns the same chunk of up to NS rows; scores are
+// reduced over the chunks of a row with lane shuffles, weights per head by one wavefront,
+// and value partials over rows with lane shuffles and one LDS pass.
+template <int D>
+struct WinCfg {
+    static constexpr int C8 = D / 8;           // 16-byte chunks per row: 8 or 16
+    static constexpr int RPP = 256 / C8;       // rows per pass of the block: 32 or 16
+    static constexpr int NS = 128 / RPP;       // passes for 128 rows: 4 or 8
+};
+
+template <int D, int G, int OUT, bool APPEND>
+__global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const uint16_t *__restrict__ q,
+                                                            const int32_t *__restrict__ q_pos,
+                                                            void *__restrict__ o,
+                                                            const uint16_t *__restrict__ k_new,
+                                                            const uint16_t *__restrict__ v_new) {
+    using C = WinCfg<D>;
+    __shared__ float sc[G][128];
+    __shared__ float red[4][G][D];
+    __shared__ float lsum[G];
+    const int sq = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = tid % C::C8, rbase = tid / C::C8;
+    const int NK = a.w + a.s;
+    const int64_t ring_base = ((int64_t)sq * a.Hkv + hk) * a.w * D;
+    const int64_t sink_base = ((int64_t)sq * a.Hkv + hk) * a.s * D;
+
+    // ---- everything that does not depend on the position, in flight at once
+    const int p = q_pos[sq];
+    uint4 qx[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+        qx[g] = *reinterpret_cast<const uint4 *>(q + ((int64_t)sq * a.Hq + hk * G + g) * D + 8 * col);
+    uint4 kx[C::NS], vx[C::NS];
+#pragma unroll
+    for (int r = 0; r < C::NS; ++r) {
+        const int e = rbase + C::RPP * r;   // row: ring slot e, or sink entry e - w
+        const int64_t off = e < a.w ? ring_base + (int64_t)e * D : sink_base + (int64_t)(e - a.w) * D;
+        const uint16_t *kb = e < a.w ? a.k_ring : a.k_sink;
+        const uint16_t *vb = e < a.w ? a.v_ring : a.v_sink;
+        kx[r] = e < NK ? *reinterpret_cast<const uint4 *>(kb + off + 8 * col) : make_uint4(0, 0, 0, 0);
+        vx[r] = e < NK ? *reinterpret_cast<const uint4 *>(vb + off + 8 * col) : make_uint4(0, 0, 0, 0);
+    }
+    uint4 knx = make_uint4(0, 0, 0, 0), vnx = make_uint4(0, 0, 0, 0);
+    if (APPEND) {
+        const int64_t src = ((int64_t)sq * a.Hkv + hk) * D + 8 * col;
+        knx = *reinterpret_cast<const uint4 *>(k_new + src);
+        vnx = *reinterpret_cast<const uint4 *>(v_new + src);
+    }
+
+    const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
+    if (!valid) {
+        for (int idx = tid; idx < G * D; idx += 256)
+            Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G) * D + idx, qnan());
+        return;
+    }
+    // ---- rotation of this thread's 4 pairs at position p
+    float cs8[8] = {1.f, 0.f, 1.f, 0.f, 1.f, 0.f, 1.f, 0.f};
+    if (a.rope) {
+        const float4 *t = reinterpret_cast<const float4 *>(a.rope + ((int64_t)p * (D / 2) + 4 * col) * 2);
+        const float4 t0 = t[0], t1 = t[1];
+        cs8[0] = t0.x; cs8[1] = t0.y; cs8[2] = t0.z; cs8[3] = t0.w;
+        cs8[4] = t1.x; cs8[5] = t1.y; cs8[6] = t1.z; cs8[7] = t1.w;
+    }
+    auto unpack = [](uint4 x, float (&f)[8]) {
+        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f[2 * m] = __uint_as_float(w4[m] << 16);
+            f[2 * m + 1] = __uint_as_float(w4[m] & 0xffff0000u);
+        }
+    };
+    float qf[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float f[8];
+        unpack(qx[g], f);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float c = cs8[2 * m], sn = cs8[2 * m + 1];
+            qf[g][2 * m] = fmaf(-f[2 * m + 1], sn, f[2 * m] * c) * a.cs;
+            qf[g][2 * m + 1] = fmaf(f[2 * m], sn, f[2 * m + 1] * c) * a.cs;
+        }
+    }
+    const int slot_new = p % a.w;
+    if (APPEND) {
+        // rotate the new key, round it as the cache stores it, write the ring slot (and the
+        // sink entry), and put it in place of the slot's old row
+        float f[8];
+        unpack(knx, f);
+        uint32_t kk[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float c = cs8[2 * m], sn = cs8[2 * m + 1];
+            kk[m] = pack_bf16x2(fmaf(-f[2 * m + 1], sn, f[2 * m] * c), fmaf(f[2 * m], sn, f[2 * m + 1] * c));
+        }
+        knx = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+#pragma unroll
+        for (int r = 0; r < C::NS; ++r) {
+            if (rbase + C::RPP * r == slot_new) {
+                kx[r] = knx;
+                vx[r] = vnx;
+                *reinterpret_cast<uint4 *>(a.k_ring + ring_base + (int64_t)slot_new * D + 8 * col) = knx;
+                *reinterpret_cast<uint4 *>(a.v_ring + ring_base + (int64_t)slot_new * D + 8 * col) = vnx;
+            }
+        }
+        if (p < a.s && rbase == 0) {
+            *reinterpret_cast<uint4 *>(a.k_sink + sink_base + (int64_t)p * D + 8 * col) = knx;
+            *reinterpret_cast<uint4 *>(a.v_sink + sink_base + (int64_t)p * D + 8 * col) = vnx;
+        }
+    }
+    // ---- scores of my rows: partial dot over my chunk, reduced across the row's chunks
+    const int lo = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
+#pragma unroll
+    for (int r = 0; r < C::NS; ++r) {
+        const int e = rbase + C::RPP * r;
+        float f[8];
+        unpack(kx[r], f);
+        float part[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc = fmaf(qf[g][c], f[c], acc);
+            part[g] = acc;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int off = 1; off < C::C8; off <<= 1) part[g] += __shfl_xor(part[g], off, 64);
+        if (col == 0 && e < 128) {
+            // position held by row e, and whether it belongs to the key set
+            int P;
+            bool inset;
+            if (e < a.w) {
+                P = p - ((p - e) % a.w + a.w) % a.w;
+                inset = e < NK && P >= 0;
+            } else {
+                P = e - a.w;
+                inset = e < NK && P < lo;
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float slope = a.slopes ? a.slopes[hk * G + g] * 1.4426950408889634f : 0.0f;
+                sc[g][e] = inset ? fmaf(slope, (float)(p - P), part[g]) : -INFINITY;
+            }
+        }
+    }
+    __syncthreads();
+    // ---- weights: one wavefront per head, two rows per lane
+    for (int g = wave; g < G; g += 4) {
+        float x0 = sc[g][lane], x1 = sc[g][lane + 64];
+        if (a.mode == 0) {
+            x0 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x0));
+            x1 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x1));
+        } else {
+            const float m = wave_max(fmaxf(x0, x1));
+            x0 = __builtin_amdgcn_exp2f(x0 - m);
+            x1 = __builtin_amdgcn_exp2f(x1 - m);
+            const float l = wave_sum(x0 + x1);
+            if (lane == 0) lsum[g] = l;
+        }
+        sc[g][lane] = x0;
+        sc[g][lane + 64] = x1;
+    }
+    __syncthreads();
+    // ---- values: my chunk of every row I own, summed over rows
+    float acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[g][c] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < C::NS; ++r) {
+        const int e = rbase + C::RPP * r;
+        if (e < NK) {
+            float f[8];
+            unpack(vx[r], f);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float wgt = sc[g][e];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(wgt, f[c], acc[g][c]);
+            }
+        }
+    }
+    // lanes sharing a column chunk: lane, lane ^ C8, ... within the wavefront
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int off = C::C8; off < 64; off <<= 1) acc[g][c] += __shfl_xor(acc[g][c], off, 64);
+    if (lane < C::C8) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) red[wave][g][8 * col + c] = acc[g][c];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int g = idx / D, cc = idx % D;
+        float sum = (red[0][g][cc] + red[1][g][cc]) + (red[2][g][cc] + red[3][g][cc]);
+        if (a.mode == 1) sum /= lsum[g];
+        Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + g) * D + cc, sum);
+    }
+}
+
 template <int D, int G, int OUT, bool APPEND>
 hipError_t launch_fast_t(const DecodeFast &f, const void *q, const int32_t *q_pos, void *o,
                          const void *k_new, const void *v_new, hipStream_t st) {
+    if (f.w + f.s <= 128) {
+        hipLaunchKernelGGL((decode_window_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv)),
+                           dim3(256), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
+                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
+        return hipGetLastError();
+    }
     const size_t lds = decode_fast_lds<D>(G);
     hipLaunchKernelGGL((decode_fast_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv)),
                        dim3(256), lds, st, f, static_cast<const uint16_t *>(q), q_pos, o,
