@@ -495,12 +495,13 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
                                                             const uint16_t *__restrict__ v_new) {
     using C = WinCfg<D>;
     __shared__ float sc[G][128];
-    __shared__ float red[4][G][D];
+    __shared__ __attribute__((aligned(16))) float red[C::RPP][G][D];
     __shared__ float lsum[G];
     const int sq = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = tid % C::C8, rbase = tid / C::C8;
     const int NK = a.w + a.s;
+    const int ns = (NK + C::RPP - 1) / C::RPP;   // row passes that hold any row
     const int64_t ring_base = ((int64_t)sq * a.Hkv + hk) * a.w * D;
     const int64_t sink_base = ((int64_t)sq * a.Hkv + hk) * a.s * D;
 
@@ -517,8 +518,8 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
         const int64_t off = e < a.w ? ring_base + (int64_t)e * D : sink_base + (int64_t)(e - a.w) * D;
         const uint16_t *kb = e < a.w ? a.k_ring : a.k_sink;
         const uint16_t *vb = e < a.w ? a.v_ring : a.v_sink;
-        kx[r] = e < NK ? *reinterpret_cast<const uint4 *>(kb + off + 8 * col) : make_uint4(0, 0, 0, 0);
-        vx[r] = e < NK ? *reinterpret_cast<const uint4 *>(vb + off + 8 * col) : make_uint4(0, 0, 0, 0);
+        kx[r] = e < NK ? ldg16(kb + off + 8 * col) : make_uint4(0, 0, 0, 0);
+        vx[r] = e < NK ? ldg16(vb + off + 8 * col) : make_uint4(0, 0, 0, 0);
     }
     uint4 knx = make_uint4(0, 0, 0, 0), vnx = make_uint4(0, 0, 0, 0);
     if (APPEND) {
@@ -590,8 +591,11 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
     }
     // ---- scores of my rows: partial dot over my chunk, reduced across the row's chunks
     const int lo = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
+    for (int g = tid; g < G * 128; g += 256) sc[g / 128][g % 128] = -INFINITY;
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < C::NS; ++r) {
+        if (r >= ns) break;   // uniform: rows past the key set
         const int e = rbase + C::RPP * r;
         float f[8];
         unpack(kx[r], f);
@@ -604,9 +608,7 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
             part[g] = acc;
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int off = 1; off < C::C8; off <<= 1) part[g] += __shfl_xor(part[g], off, 64);
+        for (int g = 0; g < G; ++g) part[g] = C::C8 == 16 ? group16_sum(part[g]) : group8_sum(part[g]);
         if (col == 0 && e < 128) {
             // position held by row e, and whether it belongs to the key set
             int P;
@@ -651,6 +653,7 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
         for (int c = 0; c < 8; ++c) acc[g][c] = 0.0f;
 #pragma unroll
     for (int r = 0; r < C::NS; ++r) {
+        if (r >= ns) break;
         const int e = rbase + C::RPP * r;
         if (e < NK) {
             float f[8];
@@ -663,23 +666,19 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
             }
         }
     }
-    // lanes sharing a column chunk: lane, lane ^ C8, ... within the wavefront
+    // partial sums of the RPP row groups, added through LDS
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int off = C::C8; off < 64; off <<= 1) acc[g][c] += __shfl_xor(acc[g][c], off, 64);
-    if (lane < C::C8) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) red[wave][g][8 * col + c] = acc[g][c];
+    for (int g = 0; g < G; ++g) {
+        float4 *dst = reinterpret_cast<float4 *>(&red[rbase][g][8 * col]);
+        dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+        dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
     }
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, cc = idx % D;
-        float sum = (red[0][g][cc] + red[1][g][cc]) + (red[2][g][cc] + red[3][g][cc]);
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < C::RPP; ++r) sum += red[r][g][cc];
         if (a.mode == 1) sum /= lsum[g];
         Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + g) * D + cc, sum);
     }

@@ -39,6 +39,30 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// 16-byte loads and stores in the global address space (device pointers that the compiler
+// cannot trace back to a kernel argument would otherwise become flat accesses).
+typedef unsigned int u32x4_ev __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4_ev global_cu4;
+typedef __attribute__((address_space(1))) u32x4_ev global_u4;
+__device__ __forceinline__ uint4 ldg16(const void *p) {
+    const u32x4_ev x = *(global_cu4 *)p;
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void stg16(void *p, uint4 x) {
+    const u32x4_ev v = {x.x, x.y, x.z, x.w};
+    *(global_u4 *)p = v;
+}
+
+// Eight bf16 values (16 bytes) -> eight float16 values, round to nearest even.
+__device__ __forceinline__ uint4 convert_bf16x8_to_f16x8(uint4 x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        r[m] = pack_f16x2(__uint_as_float(w[m] << 16), __uint_as_float(w[m] & 0xffff0000u));
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 // Element access for the two supported element types (0 = float32, 1 = bfloat16).
 template <int DT> struct Elem;
 template <> struct Elem<0> {
@@ -60,15 +84,54 @@ template <> struct Elem<1> {
     }
 };
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x);
+
+// Wavefront-wide sum / max: DPP within each row of 16 lanes, then the four row results
+// combined through scalar reads (no LDS permute round trips).
+__device__ __forceinline__ float row16_max(float x);
+__device__ __forceinline__ float row16_sum(float x);
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    x = row16_sum(x);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = row16_max(x);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+// Sums over aligned groups of 8 or 16 lanes with DPP lane permutations (no LDS traffic):
+// xor-1 and xor-2 quad permutes, then the half-row and row mirrors. Every lane of the group
+// ends with the group's total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float group8_sum(float x) {
+    x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);   // row_half_mirror: lane i <- lane 7 - i within each 8
+    return x;
+}
+__device__ __forceinline__ float group16_sum(float x) {
+    x = group8_sum(x);
+    x += dpp_f<0x140>(x);   // row_mirror: lane i <- lane 15 - i within each 16
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) { return group16_sum(x); }
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
     return x;
 }
 
