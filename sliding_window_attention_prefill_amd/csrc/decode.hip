@@ -480,20 +480,21 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
 // Thread (row group, 16-byte column chunk) owns the same chunk of up to NS rows; scores are
 // reduced over the chunks of a row with lane shuffles, weights per head by one wavefront,
 // and value partials over rows with lane shuffles and one LDS pass.
-template <int D>
+template <int D, int NT>
 struct WinCfg {
     static constexpr int C8 = D / 8;           // 16-byte chunks per row: 8 or 16
-    static constexpr int RPP = 256 / C8;       // rows per pass of the block: 32 or 16
-    static constexpr int NS = 128 / RPP;       // passes for 128 rows: 4 or 8
+    static constexpr int RPP = NT / C8;        // rows per pass of the block
+    static constexpr int NS = 128 / RPP;       // passes for 128 rows
+    static constexpr int NW = NT / 64;         // wavefronts
 };
 
-template <int D, int G, int OUT, bool APPEND>
-__global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const uint16_t *__restrict__ q,
+template <int D, int G, int OUT, bool APPEND, int NT>
+__global__ __launch_bounds__(NT) void decode_window_kernel(DecodeFast a, const uint16_t *__restrict__ q,
                                                             const int32_t *__restrict__ q_pos,
                                                             void *__restrict__ o,
                                                             const uint16_t *__restrict__ k_new,
                                                             const uint16_t *__restrict__ v_new) {
-    using C = WinCfg<D>;
+    using C = WinCfg<D, NT>;
     __shared__ float sc[G][128];
     __shared__ __attribute__((aligned(16))) float red[C::RPP][G][D];
     __shared__ float lsum[G];
@@ -530,7 +531,7 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
 
     const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
     if (!valid) {
-        for (int idx = tid; idx < G * D; idx += 256)
+        for (int idx = tid; idx < G * D; idx += NT)
             Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G) * D + idx, qnan());
         return;
     }
@@ -591,7 +592,7 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
     }
     // ---- scores of my rows: partial dot over my chunk, reduced across the row's chunks
     const int lo = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
-    for (int g = tid; g < G * 128; g += 256) sc[g / 128][g % 128] = -INFINITY;
+    for (int g = tid; g < G * 128; g += NT) sc[g / 128][g % 128] = -INFINITY;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < C::NS; ++r) {
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
     }
     __syncthreads();
     // ---- weights: one wavefront per head, two rows per lane
-    for (int g = wave; g < G; g += 4) {
+    for (int g = wave; g < G; g += C::NW) {
         float x0 = sc[g][lane], x1 = sc[g][lane + 64];
         if (a.mode == 0) {
             x0 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x0));
@@ -674,7 +675,7 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
         dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += 256) {
+    for (int idx = tid; idx < G * D; idx += NT) {
         const int g = idx / D, cc = idx % D;
         float sum = 0.0f;
 #pragma unroll
@@ -687,8 +688,14 @@ __global__ __launch_bounds__(256) void decode_window_kernel(DecodeFast a, const 
 template <int D, int G, int OUT, bool APPEND>
 hipError_t launch_fast_t(const DecodeFast &f, const void *q, const int32_t *q_pos, void *o,
                          const void *k_new, const void *v_new, hipStream_t st) {
+    if (f.w + f.s <= 128 && G <= 4) {
+        hipLaunchKernelGGL((decode_window_kernel<D, G, OUT, APPEND, 512>), dim3((unsigned)(f.S * f.Hkv)),
+                           dim3(512), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
+                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
+        return hipGetLastError();
+    }
     if (f.w + f.s <= 128) {
-        hipLaunchKernelGGL((decode_window_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv)),
+        hipLaunchKernelGGL((decode_window_kernel<D, G, OUT, APPEND, 256>), dim3((unsigned)(f.S * f.Hkv)),
                            dim3(256), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
                            static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
         return hipGetLastError();
