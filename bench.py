@@ -200,6 +200,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=1)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB mebibytes three times (the "
+                         "known-size kernel that scales the HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the workloads "
@@ -208,6 +211,17 @@ def main():
 
     import torch
     import swa_workloads as wl
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
 
     cfg = {"c2": wl.C2, "c3": wl.C3, "c5": wl.C5}[args.workload]
     out_dtype = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
