@@ -59,9 +59,10 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * for no bias (a zero slope also means no bias on that head). rope_table: device float
  * [rope_rows, d/2, 2] from swa_rope_table, or NULL for no rotation; rope_rows >= N.
  * bf16 inputs with d in {64, 128} and 16-byte aligned tensors run on the matrix cores,
- * which form both products from float16 operands (rotated q and k, the weights, v) with
- * float32 accumulation: those inputs must stay within the float16 range (|x| < 65504).
- * Other shapes run on a general float32 vector kernel.
+ * which form the score product from float16 operands (rotated q and k) and the value
+ * product from float16 (softmax) or bf16 (sigmoid) operands, with float32 accumulation:
+ * those inputs must stay within the float16 range (|x| < 65504). Other shapes run on a
+ * general float32 vector kernel.
  */
 typedef struct swa_prefill_params {
     int64_t B, H_q, H_kv, N, d;
@@ -76,11 +77,25 @@ typedef struct swa_prefill_params {
     int64_t rope_rows;
 } swa_prefill_params;
 
+/*
+ * workspace: device scratch of at least swa_prefill_workspace_bytes(p) bytes, 16-byte
+ * aligned (may be NULL when that is 0). The matrix-core path uses it for keys rotated once
+ * into float16 tile images (and, for softmax, values converted to float16) when a key tile
+ * is shared by many workgroups. Its contents on entry do not matter; calls that share a
+ * workspace must not overlap. A workspace that is too small or misaligned for a call that
+ * needs one is rejected with SWA_ERR_INVALID_ARGUMENT.
+ */
 swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k,
-                       const void *v, void *o, void *stream);
+                       const void *v, void *o, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Bytes of workspace swa_prefill needs for these parameters (0 when it needs none, or when
+ * the parameters are invalid). */
+size_t swa_prefill_workspace_bytes(const swa_prefill_params *p);
 
 /*
- * RoPE angle table (SWAT page, "RoPE"; the RoFormer rotation it cites):
+ * RoPE angle table (SWAT: Sliding Window Attention Training, "RoPE: Stabilizing Sigmoid
+ * Attention Training"; the RoFormer rotation it cites):
  *   table[pos][t] = (cos(pos * theta^(-2t/d)), sin(pos * theta^(-2t/d))), pos in
  *   [0, n_pos), t in [0, d/2), evaluated in float64 on the device and rounded to float32.
  * table: device float[n_pos * d/2 * 2]. Requires n_pos >= 0, d even >= 2, theta > 0.

@@ -55,7 +55,7 @@ class DecodeParams(ctypes.Structure):
                 ("rope_rows", c_i64)]
 
 
-EXPORTS = ["swa_prefill", "swa_rope_table", "swa_rope_apply", "swa_kv_append", "swa_decode",
+EXPORTS = ["swa_prefill", "swa_prefill_workspace_bytes", "swa_rope_table", "swa_rope_apply", "swa_kv_append", "swa_decode",
            "swa_decode_append", "swa_decode_workspace_bytes", "swa_status_string",
            "swa_last_hip_error", "swa_version"]
 
@@ -71,8 +71,11 @@ def load():
                               "sliding_window_attention_prefill_amd.build)")
         lib = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
-        lib.swa_prefill.argtypes = [P(PrefillParams), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr]
+        lib.swa_prefill.argtypes = [P(PrefillParams), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                                    ctypes.c_size_t, c_ptr]
         lib.swa_prefill.restype = ctypes.c_int
+        lib.swa_prefill_workspace_bytes.argtypes = [P(PrefillParams)]
+        lib.swa_prefill_workspace_bytes.restype = ctypes.c_size_t
         lib.swa_rope_table.argtypes = [c_ptr, c_i64, c_i64, ctypes.c_double, c_ptr]
         lib.swa_rope_table.restype = ctypes.c_int
         lib.swa_rope_apply.argtypes = [c_ptr, c_i64, c_i64, c_i64, c_i64, c_ptr, c_ptr, c_i64,
@@ -157,8 +160,12 @@ def swa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: int, s:
                 mode=SWA_SIGMOID, scale: float = 0.0,
                 alibi_slopes: Optional[torch.Tensor] = None,
                 rope_table: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
-    """Sliding-window attention over whole sequences. q [B,N,H_q,d], k/v [B,N,H_kv,d]."""
+                out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """Sliding-window attention over whole sequences. q [B,N,H_q,d], k/v [B,N,H_kv,d].
+
+    workspace: a device uint8 tensor of at least swa_prefill_workspace_bytes(...) bytes;
+    allocated here when it is not given and the call needs one."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n)
     if q.dim() != 4 or k.shape != v.shape or k.dim() != 4:
@@ -186,9 +193,28 @@ def swa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: int, s:
         rows = rope_table.shape[0]
     p = PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), _dt(out), scale,
                       _ptr(alibi_slopes), _ptr(rope_table), rows)
-    _check("swa_prefill", load().swa_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
-                                             _ptr(out), _stream(q.device, stream)))
+    lib = load()
+    need = lib.swa_prefill_workspace_bytes(ctypes.byref(p))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("swa_prefill", lib.swa_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                          _ptr(workspace), ws_bytes, _stream(q.device, stream)))
     return out
+
+
+def swa_prefill_workspace_bytes(q: torch.Tensor, k: torch.Tensor, *, w: int, s: int = 0,
+                                mode=SWA_SIGMOID, out_dtype: Optional[torch.dtype] = None) -> int:
+    """Workspace bytes swa_prefill needs for q [B,N,H_q,d], k [B,N,H_kv,d] and these options
+    (ALiBi and RoPE do not change it)."""
+    B, N, Hq, d = q.shape
+    out_dt = SWA_F32 if (out_dtype or q.dtype) == torch.float32 else SWA_BF16
+    p = PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), out_dt, 0.0,
+                      None, None, 0)
+    return int(load().swa_prefill_workspace_bytes(ctypes.byref(p)))
 
 
 def swa_rope_apply(x: torch.Tensor, pos0: torch.Tensor, rope_table: torch.Tensor,

@@ -1,34 +1,41 @@
 // prefill_mfma.hip - banded matrix-core prefill for bfloat16 inputs, d in {64, 128}.
 //
-// What it computes (SWAT: Sliding Window Attention Training, "Balanced ALiBi" attention
-// equation, "Sigmoid" equation; Sliding Window Attention glossary, band mask; sinks per
-// Sliding-window beats linear attention, SWA(w, s)):
+// What it computes (SWAT: Sliding Window Attention Training, "Putting It Together" attention
+// equation with the balanced ALiBi bias, "Sigmoid: Dense Attention Without Suppression";
+// Sliding Window Attention glossary, band mask; Sliding-window beats linear attention,
+// SWA(w, s)):
 //   o_i = sum_{j in K(i)} p(x_ij) v_j,  x_ij = scale (R(i)q_i).(R(j)k_j) + slope_h (i - j),
 //   K(i) = { j <= i : i - j < w or j < s },  p = sigmoid (no normalisation) or softmax.
 //
 // How (gfx950):
 //   * One workgroup (4 wavefronts) owns 128 query rows: 128/GP positions x GP query heads
-//     that share one kv head (grouped-query packing), so each K/V tile is staged once for
-//     the whole group.
-//   * It walks only the key tiles that intersect its band [q0 - w + 1, q0 + 127] plus the
-//     sink tiles the window no longer covers; every other tile is skipped (the block
-//     skipping the glossary describes for windowed exact-attention kernels). Tiles inside
-//     every row's key set run without the element predicate.
-//   * Matrix operands are float16: the bf16 inputs are widened, rotated in float32 and
-//     rounded once to float16 (11-bit significand), and the weights are rounded to float16
-//     (they are at most 2^8). Both products run at the same matrix rate as bf16 and the
-//     rounding error is several times smaller. Inputs must stay within the float16 range
-//     (|x| < 65504), which attention activations do.
-//   * K tiles are rotated on the way into LDS; V tiles are stored transposed in LDS with a
-//     key permutation that matches the register layout of the score accumulators, so the
-//     weights feed the second product straight from registers.
-//   * Each wavefront computes S^T = K Q^T (32 keys x 32 queries per v_mfma_f32_32x32x16_f16)
-//     so that a lane holds one query's scores. The scale and the ALiBi bias fold into two
-//     FMAs per score in base-2 units. Weights are computed in base 2: sigmoid as 1/(1 + 2^t), softmax online with lazily
-//     rescaled accumulators. O^T += V^T P^T accumulates in float32.
-//   * K/V tiles are fetched with buffer loads whose range check returns zeros past the
-//     sequence end; LDS is double-buffered with the next tile's loads issued before the
-//     current tile's math.
+//     that share one kv head, so each K/V tile in LDS serves the whole group.
+//   * It walks only the 64-key tiles that intersect its band [q0 - w + 1, q0 + 127] plus
+//     the sink tiles the window no longer covers (the block skipping the glossary describes
+//     for windowed exact-attention kernels). Tiles inside every row's key set run without
+//     the element predicate.
+//   * Each wavefront computes S^T = K Q^T (32 keys x 32 queries per 32x32x16 matrix
+//     instruction), so a lane holds one query's scores; the scale and the bias fold into
+//     FMAs in base-2 units; sigmoid is 1 / (1 + 2^t), softmax is online with a lazily
+//     rescaled accumulator. O^T += V^T P^T takes the weights straight from registers.
+//   * Score operands are float16: q and k are widened from bf16, rotated in float32 and
+//     rounded once (inputs must stay within the float16 range, |x| < 65504).
+//   * Tile staging, chosen per problem by the host:
+//       - K rotated on the way in: buffer loads into registers, rotation, LDS store;
+//       - K from a packed image: a pre-pass rotates every key once into float16 tile images
+//         laid out exactly as LDS holds them, and the main kernel copies them with
+//         buffer-to-LDS transfers (no registers, no vector instructions);
+//       - V as stored (bf16, sigmoid): buffer-to-LDS transfers of the input rows; the second
+//         product runs in bf16 with the weights rounded to bf16;
+//       - V from a packed float16 image (softmax): the pre-pass converts it once, and the
+//         second product runs in float16.
+//     V stays row-major in LDS; the transposing LDS read (ds_read_b64_tr_b16) delivers it in
+//     the operand layout of the second product, in the key order of the score registers.
+//   * LDS rows are XOR-swizzled in 16-byte chunks so that the row reads of K and the
+//     transposing reads of V are free of bank conflicts; the register path, the transfers
+//     and the pre-pass all write that swizzle.
+//   * LDS is double-buffered: the next tile's loads are issued before the current tile's
+//     math.
 //   * The output goes through LDS so that every global store writes whole rows.
 //   * Workgroups are numbered so that each of the 8 XCDs walks a contiguous run of query
 //     tiles of the same (batch, kv head), keeping shared K/V tiles in that XCD's L2.
@@ -41,34 +48,57 @@ namespace {
 constexpr int BK = 64;  // keys per tile
 constexpr float LOG2E = 1.4426950408889634f;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
+typedef short s16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int D>
 struct Tile {
-    static constexpr int KSTR = D + 8;             // f16 per K row in LDS (16 B pad)
-    static constexpr int VSTR = BK + 8;            // f16 per V^T row in LDS (16 B pad)
-    static constexpr int K_ELEMS = BK * KSTR;
-    static constexpr int V_ELEMS = D * VSTR;
-    static constexpr int BUF = K_ELEMS + V_ELEMS;  // one buffer, 16-bit elements
-    static constexpr int C8 = D / 8;               // 16-byte chunks per row
-    static constexpr int K_PER_T = BK * C8 / 256;  // K chunks per thread: 2 or 4
-    static constexpr int KPU = BK * C8 / 256;      // keys per V unit (one unit per thread)
-    static constexpr int KG = BK / KPU;            // key groups per tile: 32 or 16
-    static constexpr int OSTR = D + 4;             // floats per output row staged in LDS
+    static constexpr int C = D / 8;                      // 16-byte chunks per row
+    static constexpr int IMG = BK * D;                   // 16-bit elements of a K or V tile
+    static constexpr int IMG_BYTES = IMG * 2;
+    static constexpr int DMA_W = IMG_BYTES / (4 * 1024); // 1 KB transfers per wavefront
+    static constexpr int KPT = BK * C / 256;             // K chunks per thread (register path)
+    static constexpr int OSTR = D + 4;                   // floats per output row in LDS
+    static constexpr int LDS_BYTES = cmax(2 * 2 * IMG_BYTES, 4 * 32 * OSTR * 4);
 };
+
+// Chunk swizzles: chunk c of tile row r is stored at chunk c ^ swz(r) of that row.
+// K rows are read 16 rows at one chunk; V is read 4 rows x 4 chunks per 32 lanes.
+template <int D>
+__host__ __device__ __forceinline__ constexpr int kswz(int r) {
+    return D == 64 ? (r >> 1) & 7 : r & 15;
+}
+template <int D>
+__host__ __device__ __forceinline__ constexpr int vswz(int r) {
+    return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
+}
 
 struct MfmaParams {
     const uint16_t *q, *k, *v;
+    const uint16_t *kimg, *vimg;  // packed tile images, or null
     void *o;
     const float *slopes;
     const float *rope;
     int64_t N, Hq, Hkv, G;
-    int n_qtiles, n_hgroups;
+    int n_qtiles, n_hgroups, n_ktiles;
     int w, s;                 // clamped to N
     float cs;                 // scale * log2(e)
     uint32_t kv_bytes;        // bytes of one (batch, kv head) K or V slice, rows [0, N)
     uint32_t row_bytes;       // bytes between consecutive positions of K/V
     uint32_t rope_bytes;      // bytes of the rotation table
     int out_bf16;
+};
+
+struct PackParams {
+    const uint16_t *k, *v;
+    uint16_t *kimg, *vimg;
+    const float *rope;
+    int64_t N, Hkv;
+    int n_ktiles;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -87,10 +117,9 @@ __device__ __forceinline__ float4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t
                        __uint_as_float(x[3]));
 }
 
-// Storage column of key kk inside a V^T row: bits 2 and 3 swapped, which makes the eight
-// keys one lane contributes to one P.V step contiguous.
-__device__ __forceinline__ int vperm(int kk) {
-    return (kk & ~12) | ((kk & 4) << 1) | ((kk & 8) >> 1);
+__device__ __forceinline__ float4 as_float4(uint4 x) {
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                       __uint_as_float(x.w));
 }
 
 // A dword of two bf16 inputs -> two float16 matrix operands, rotated by (c, s) or not.
@@ -110,78 +139,100 @@ __device__ __forceinline__ uint4 convert_chunk(uint4 x) {
     return make_uint4(to_f16_pair(x.x), to_f16_pair(x.y), to_f16_pair(x.z), to_f16_pair(x.w));
 }
 
+// ---------------------------------------------------------------------------------------
+// Pre-pass: every 64-key tile of one (batch, kv head), once, into its LDS image.
+// K image: rotated (or converted) float16; V image (PACK_V): converted float16. Rows past
+// the sequence end are zero.
+template <int D, bool ROT, bool PACK_V>
+__global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
+    using T = Tile<D>;
+    const int bid = blockIdx.x, tid = threadIdx.x;
+    const int jt = bid % p.n_ktiles;
+    const int64_t bh = bid / p.n_ktiles;  // b * H_kv + kv head
+    const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
+    uint16_t *kdst = p.kimg + (bh * p.n_ktiles + jt) * T::IMG;
+    uint16_t *vdst = PACK_V ? p.vimg + (bh * p.n_ktiles + jt) * T::IMG : nullptr;
+#pragma unroll
+    for (int r = 0; r < T::KPT; ++r) {
+        const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+        const int64_t j = (int64_t)jt * BK + row;
+        uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
+        if (j < p.N) {
+            const int64_t off = ((b * p.N + j) * p.Hkv + hkv) * D + c * 8;
+            xk = ldg16(p.k + off);
+            if (ROT) {
+                const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
+                xk = rotate_chunk(xk, as_float4(ldg16(t)), as_float4(ldg16(t + 4)));
+            } else {
+                xk = convert_chunk(xk);
+            }
+            if (PACK_V) xv = convert_chunk(ldg16(p.v + off));
+        }
+        stg16(kdst + (row * T::C + (c ^ kswz<D>(row))) * 8, xk);
+        if (PACK_V) stg16(vdst + (row * T::C + (c ^ vswz<D>(row))) * 8, xv);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Main kernel pieces.
+
+// K tile staged through registers (rotated on the way into LDS).
 template <int D>
-struct Stage {
-    uint4 k[Tile<D>::K_PER_T];
-    float4 kcs[Tile<D>::K_PER_T][2];
-    uint4 v[Tile<D>::KPU];
+struct KStage {
+    uint4 k[Tile<D>::KPT];
+    float4 cs[Tile<D>::KPT][2];
 };
 
-struct Rsrc {
-    __amdgpu_buffer_rsrc_t k, v, t;
-};
-
-// Global -> registers for the tile of keys j0..j0+63 (rows past the end read as zero).
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D> &st, const Rsrc &rs, uint32_t row_bytes,
-                                           int j0, int tid, bool rope) {
+__device__ __forceinline__ void kstage_load(KStage<D> &st, __amdgpu_buffer_rsrc_t rk,
+                                            __amdgpu_buffer_rsrc_t rt, uint32_t row_bytes,
+                                            int j0, int tid, bool rope) {
     using T = Tile<D>;
 #pragma unroll
-    for (int r = 0; r < T::K_PER_T; ++r) {
+    for (int r = 0; r < T::KPT; ++r) {
         const int c = tid + 256 * r;
-        const int j = j0 + c / T::C8, c8 = c % T::C8;
-        st.k[r] = buf_load16(rs.k, (uint32_t)j * row_bytes + c8 * 16);
+        const int j = j0 + c / T::C, c8 = c % T::C;
+        st.k[r] = buf_load16(rk, (uint32_t)j * row_bytes + c8 * 16);
         if (rope) {
             const uint32_t toff = ((uint32_t)j * (D / 2) + c8 * 4) * 8;
-            st.kcs[r][0] = buf_load16f(rs.t, toff);
-            st.kcs[r][1] = buf_load16f(rs.t, toff + 16);
+            st.cs[r][0] = buf_load16f(rt, toff);
+            st.cs[r][1] = buf_load16f(rt, toff + 16);
         }
     }
-    const int kg = tid % T::KG, c8 = tid / T::KG;
-#pragma unroll
-    for (int r = 0; r < T::KPU; ++r)
-        st.v[r] = buf_load16(rs.v, (uint32_t)(j0 + kg * T::KPU + r) * row_bytes + c8 * 16);
 }
 
-__device__ __forceinline__ uint32_t dword_of(const uint4 &x, int m) {
-    return m == 0 ? x.x : m == 1 ? x.y : m == 2 ? x.z : x.w;
-}
-
-// Registers -> LDS: K rotated (or converted) row-major, V converted and transposed.
 template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D> &st, uint16_t *buf, int tid, bool rope) {
+__device__ __forceinline__ void kstage_store(const KStage<D> &st, uint16_t *__restrict__ dst,
+                                             int tid, bool rope) {
     using T = Tile<D>;
-    uint16_t *kl = buf;
-    uint16_t *vl = buf + T::K_ELEMS;
 #pragma unroll
-    for (int r = 0; r < T::K_PER_T; ++r) {
+    for (int r = 0; r < T::KPT; ++r) {
         const int c = tid + 256 * r;
-        const int row = c / T::C8, c8 = c % T::C8;
-        const uint4 x = rope ? rotate_chunk(st.k[r], st.kcs[r][0], st.kcs[r][1]) : convert_chunk(st.k[r]);
-        *reinterpret_cast<uint4 *>(kl + row * T::KSTR + c8 * 8) = x;
+        const int row = c / T::C, c8 = c % T::C;
+        const uint4 x = rope ? rotate_chunk(st.k[r], st.cs[r][0], st.cs[r][1]) : convert_chunk(st.k[r]);
+        *reinterpret_cast<uint4 *>(dst + (row * T::C + (c8 ^ kswz<D>(row))) * 8) = x;
     }
-    const int kg = tid % T::KG, c8 = tid / T::KG;
-    const int col = vperm(kg * T::KPU);
+}
+
+// Per-lane offsets, fixed for the whole kernel.
+template <int D>
+struct LaneOffsets {
+    int k[D / 16];                   // LDS element offset of the K row read of score step ks
+    int v[D / 32];                   // LDS element offset of the V transposing read, block db
+    uint32_t dimg[Tile<D>::DMA_W];   // source byte offset in a packed tile image, per transfer
+    uint32_t dvraw[Tile<D>::DMA_W];  // source byte offset in the V input rows, per transfer
+};
+
+// Buffer -> LDS transfers of one tile: DMA_W rounds of 1 KB per wavefront; lane l of round i
+// lands at bytes 16 l of that round's kilobyte. off[i] is this lane's source offset.
+template <int D>
+__device__ __forceinline__ void dma_tile(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t r,
+                                         uint32_t base, const uint32_t *off,
+                                         int wave) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        // element 2m (low half) and 2m+1 (high half) of each key, as float32
-        float lo[T::KPU], hi[T::KPU];
-#pragma unroll
-        for (int r = 0; r < T::KPU; ++r) {
-            const uint32_t w = dword_of(st.v[r], m);
-            lo[r] = __uint_as_float(w << 16);
-            hi[r] = __uint_as_float(w & 0xffff0000u);
-        }
-        uint16_t *row_lo = vl + (c8 * 8 + 2 * m) * T::VSTR + col;
-        uint16_t *row_hi = row_lo + T::VSTR;
-        if constexpr (T::KPU == 2) {
-            *reinterpret_cast<uint32_t *>(row_lo) = pack_f16x2(lo[0], lo[1]);
-            *reinterpret_cast<uint32_t *>(row_hi) = pack_f16x2(hi[0], hi[1]);
-        } else {
-            *reinterpret_cast<uint2 *>(row_lo) = make_uint2(pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3]));
-            *reinterpret_cast<uint2 *>(row_hi) = make_uint2(pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]));
-        }
-    }
+    for (int i = 0; i < Tile<D>::DMA_W; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void_t *)(dst + (wave * Tile<D>::DMA_W + i) * 512), 16, base + off[i], 0, 0, 0);
 }
 
 // Key offset (from j0 + 4g) of accumulator element e of score block kb.
@@ -207,22 +258,23 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
 
 // One 64-key tile for one wavefront: S^T = K Q^T, weights, O^T += V^T P^T.
 // kind: 0 = every pair in the key set, 1 = cut by the window edges, 2 = also holds sinks.
-template <int D, int MODE, bool ALIBI>
-__device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl,
-                                          const f16x8_t (&qreg)[D / 16], f32x16_t (&oacc)[D / 32],
-                                          float &m_run, float &l_run, float cs, float slope_l2,
-                                          int kind, int dq, int jb, int w, int s, int qc, int g) {
-    using T = Tile<D>;
+template <int D, int MODE, bool ALIBI, bool VF16>
+__device__ __forceinline__ void tile_math(const uint16_t *__restrict__ kl,
+                                          const uint16_t *__restrict__ vl,
+                                          const LaneOffsets<D> &lo, const f16x8_t (&qreg)[D / 16],
+                                          f32x16_t (&oacc)[D / 32], float &m_run, float &l_run,
+                                          float cs, float slope_l2, int kind, int dq, int jb,
+                                          int w, int s) {
     constexpr int KS = D / 16, DB = D / 32;
     f32x16_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const f16x8_t a0 = *reinterpret_cast<const f16x8_t *>(kl + (kb * 32 + qc) * T::KSTR + g * 8);
+        const f16x8_t a0 = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + lo.k[0]);
         const f32x16_t zero = {};
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qreg[0], zero, 0, 0, 0);
 #pragma unroll
         for (int ks = 1; ks < KS; ++ks) {
-            const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + (kb * 32 + qc) * T::KSTR + ks * 16 + g * 8);
+            const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + lo.k[ks]);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sacc[kb], 0, 0, 0);
         }
     }
@@ -282,27 +334,87 @@ __device__ __forceinline__ void tile_math(const uint16_t *kl, const uint16_t *vl
             }
         l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
-    // O^T += V^T P^T; P^T step t uses this lane's elements (t/2, 8(t%2) + 0..7)
+    // O^T += V^T P^T. Step t covers keys 16t..16t+15; this lane's P^T elements are
+    // sacc[t/2][8(t%2) + 0..7] = keys 16t + 4g + {0..3, 8..11}, and the two transposing reads
+    // deliver V^T in exactly that key order.
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int kb = t >> 1, e0 = 8 * (t & 1);
         uint4 pk;
-        pk.x = pack_f16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
-        pk.y = pack_f16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
-        pk.z = pack_f16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
-        pk.w = pack_f16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
-        const f16x8_t bp = __builtin_bit_cast(f16x8_t, pk);
+        if (VF16) {
+            pk.x = pack_f16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
+            pk.y = pack_f16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
+            pk.z = pack_f16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
+            pk.w = pack_f16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
+        } else {
+            pk.x = pack_bf16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
+            pk.y = pack_bf16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
+            pk.z = pack_bf16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
+            pk.w = pack_bf16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const f16x8_t a = *reinterpret_cast<const f16x8_t *>(vl + (db * 32 + qc) * T::VSTR + 16 * t + 8 * g);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bp, oacc[db], 0, 0, 0);
+            const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t *)(vl + 16 * t * D + lo.v[db]));
+            const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t *)(vl + (16 * t + 8) * D + lo.v[db]));
+            const s16x8_t a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (VF16)
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8_t, a8), __builtin_bit_cast(f16x8_t, pk), oacc[db], 0, 0, 0);
+            else
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8_t, a8), __builtin_bit_cast(bf16x8_t, pk), oacc[db], 0, 0, 0);
         }
     }
 }
 
-// Register budget: 3 wavefronts per SIMD at d = 64, 2 at d = 128 (the LDS double buffer
-// allows 4 and 2 workgroups per CU respectively).
-template <int D, int GP, int MODE, bool ALIBI>
+struct TileCtx {
+    __amdgpu_buffer_rsrc_t rk, rv, rt;
+    uint32_t row_bytes;
+    int tid, wave, qa, qb, i, g, w, s, N;
+    float cs, slope_l2;
+    bool rope;
+};
+
+// Loads of tile jn into buffer (nk, nv): K by transfer or into registers, V by transfer.
+template <int D, bool KPRE, bool VF16>
+__device__ __forceinline__ void issue_loads(uint16_t *__restrict__ nk, uint16_t *__restrict__ nv,
+                                            const TileCtx &cx, const LaneOffsets<D> &lo,
+                                            KStage<D> &ks, int jn) {
+    using T = Tile<D>;
+    if (KPRE) dma_tile<D>(nk, cx.rk, (uint32_t)(jn / BK) * T::IMG_BYTES, lo.dimg, cx.wave);
+    else kstage_load<D>(ks, cx.rk, cx.rt, cx.row_bytes, jn, cx.tid, cx.rope);
+    if (VF16) dma_tile<D>(nv, cx.rv, (uint32_t)(jn / BK) * T::IMG_BYTES, lo.dimg, cx.wave);
+    else dma_tile<D>(nv, cx.rv, (uint32_t)jn * cx.row_bytes, lo.dvraw, cx.wave);
+}
+
+// One step of the tile loop. The next tile's buffer and the current one are distinct
+// restrict pointers, so the reads of the current tile do not wait for the transfers into
+// the next one.
+template <int D, int MODE, bool ALIBI, bool KPRE, bool VF16>
+__device__ __forceinline__ void tile_step(uint16_t *__restrict__ nk, uint16_t *__restrict__ nv,
+                                          const uint16_t *__restrict__ ck,
+                                          const uint16_t *__restrict__ cv, const TileCtx &cx,
+                                          const LaneOffsets<D> &lo, KStage<D> &ks,
+                                          const f16x8_t (&qreg)[D / 16], f32x16_t (&oacc)[D / 32],
+                                          float &m_run, float &l_run, int j0, int jn, bool next) {
+    if (next) issue_loads<D, KPRE, VF16>(nk, nv, cx, lo, ks, jn);
+    // classify the tile for this wavefront's queries [qa, qb] (wave-uniform)
+    const bool empty = cx.qa >= cx.N || j0 > cx.qb || (cx.qa - (j0 + BK - 1) >= cx.w && j0 >= cx.s);
+    const bool full = (j0 + BK - 1 <= cx.qa) && (cx.qb - j0 < cx.w || j0 + BK - 1 < cx.s);
+    if (!empty) {
+        const int dq = cx.i - j0 - 4 * cx.g;   // element (kb, e) has i - j = dq - key_of(kb, e)
+        const int jb = j0 + 4 * cx.g;          // and key j = jb + key_of(kb, e)
+        const int kind = full ? 0 : (j0 >= cx.s ? 1 : 2);
+        tile_math<D, MODE, ALIBI, VF16>(ck, cv, lo, qreg, oacc, m_run, l_run, cx.cs, cx.slope_l2,
+                                        kind, dq, jb, cx.w, cx.s);
+    }
+    if (!KPRE && next) kstage_store<D>(ks, nk, cx.tid, cx.rope);
+}
+
+// Register budget: 3 wavefronts per SIMD at d = 64, 2 at d = 128.
+template <int D, int GP, int MODE, bool ALIBI, bool KPRE, bool VF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
 void prefill_mfma_kernel(MfmaParams p) {
     using T = Tile<D>;
@@ -310,7 +422,7 @@ void prefill_mfma_kernel(MfmaParams p) {
     constexpr int WPH = 4 / GP;   // wavefronts per query head
     constexpr int KS = D / 16;    // k-steps of the score product
     constexpr int DB = D / 32;    // 32-row blocks of the output
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::BUF];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[T::LDS_BYTES / 2];
 
     // ---- workgroup -> (batch, kv head, head group, query tile), XCD-contiguous
     const int nb = gridDim.x, bid = blockIdx.x;
@@ -332,14 +444,43 @@ void prefill_mfma_kernel(MfmaParams p) {
     const int qa = q0 + 32 * pb;                   // this wavefront's first query
     const int i = qa + qc;                         // this lane's query
     const int qe = (q0 + QP < N ? q0 + QP : N) - 1;
-    const int qb = (qa + 31 < N ? qa + 31 : N - 1);
     const bool rope = p.rope != nullptr;
 
-    Rsrc rs;
-    const int64_t kvoff = ((int64_t)b * p.N * p.Hkv + hkv) * D;
-    rs.k = make_rsrc(p.k + kvoff, p.kv_bytes);
-    rs.v = make_rsrc(p.v + kvoff, p.kv_bytes);
-    rs.t = make_rsrc(p.rope, rope ? p.rope_bytes : 0);
+    TileCtx cx;
+    {
+        const int64_t kvoff = ((int64_t)b * p.N * p.Hkv + hkv) * D;
+        const int64_t imoff = ((int64_t)b * p.Hkv + hkv) * p.n_ktiles * T::IMG;
+        const uint32_t imbytes = (uint32_t)p.n_ktiles * T::IMG_BYTES;
+        cx.rk = KPRE ? make_rsrc(p.kimg + imoff, imbytes) : make_rsrc(p.k + kvoff, p.kv_bytes);
+        cx.rv = VF16 ? make_rsrc(p.vimg + imoff, imbytes) : make_rsrc(p.v + kvoff, p.kv_bytes);
+        cx.rt = make_rsrc(p.rope, (!KPRE && rope) ? p.rope_bytes : 0);
+        cx.row_bytes = p.row_bytes;
+        cx.tid = tid; cx.wave = wave; cx.qa = qa; cx.qb = qa + 31 < N ? qa + 31 : N - 1;
+        cx.i = i; cx.g = g; cx.w = p.w; cx.s = p.s; cx.N = N;
+        cx.cs = p.cs;
+        cx.slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;  // bias in base-2 units
+        cx.rope = rope;
+    }
+
+    LaneOffsets<D> lo;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) lo.k[ks] = qc * D + (((2 * ks + g) ^ kswz<D>(qc)) * 8);
+    {
+        // transposing read: lane (G4, rr, a) supplies the row 4 (G4 / 2) + rr and the column
+        // group 16 (G4 % 2) + 4 a of the 8 x 32 block that one read covers
+        const int G4 = lane >> 4, rr = (lane >> 2) & 3, a = lane & 3;
+        const int row_l = 4 * (G4 >> 1) + rr, cb = 2 * (G4 & 1) + (a >> 1);
+        const int fq = vswz<D>(rr) >> 2;   // the V swizzle depends on row bits the lane fixes
+#pragma unroll
+        for (int db = 0; db < DB; ++db) lo.v[db] = row_l * D + (4 * (db ^ fq) + cb) * 8 + 4 * (a & 1);
+    }
+#pragma unroll
+    for (int r = 0; r < T::DMA_W; ++r) {
+        const int slot = (wave * T::DMA_W + r) * 64 + lane;  // 16-byte slot of the tile image
+        const int row = slot / T::C, c = (slot % T::C) ^ vswz<D>(row);
+        lo.dimg[r] = (uint32_t)slot * 16;
+        lo.dvraw[r] = (uint32_t)row * p.row_bytes + c * 16;
+    }
 
     // ---- this lane's query fragment (B operand of S^T = K Q^T): rotated, float16
     f16x8_t qreg[KS];
@@ -361,8 +502,6 @@ void prefill_mfma_kernel(MfmaParams p) {
         }
     }
 
-    const float slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;  // bias in base-2 units
-
     // ---- band of key tiles: sink tiles the window no longer covers, then the window
     const int lo_wg = q0 - p.w + 1 > 0 ? q0 - p.w + 1 : 0;
     const int tw_begin = lo_wg / BK, tw_end = qe / BK;
@@ -377,34 +516,20 @@ void prefill_mfma_kernel(MfmaParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
     float m_run = -1e30f, l_run = 0.0f;
-    const float cs = p.cs;
 
-    Stage<D> st;
-    stage_load<D>(st, rs, p.row_bytes, (ts_end > 0 ? 0 : tw_begin) * BK, tid, rope);
-    stage_store<D>(st, lds, tid, rope);
+    KStage<D> ks;
+    issue_loads<D, KPRE, VF16>(lds, lds + T::IMG, cx, lo, ks, (ts_end > 0 ? 0 : tw_begin) * BK);
+    if (!KPRE) kstage_store<D>(ks, lds, tid, rope);
     __syncthreads();
 
     for (int it = 0; it < n_tiles; ++it) {
         const int j0 = (it < ts_end ? it : tw_begin + (it - ts_end)) * BK;
-        if (it + 1 < n_tiles) {
-            const int jn = (it + 1 < ts_end ? it + 1 : tw_begin + (it + 1 - ts_end)) * BK;
-            stage_load<D>(st, rs, p.row_bytes, jn, tid, rope);
-        }
-        const uint16_t *kl = lds + (it & 1) * T::BUF;
-        const uint16_t *vl = kl + T::K_ELEMS;
-
-        // classify the tile for this wavefront's queries [qa, qb] (wave-uniform)
-        const bool empty = qa >= N || j0 > qb || (qa - (j0 + BK - 1) >= p.w && j0 >= p.s);
-        const bool full = (j0 + BK - 1 <= qa) && (qb - j0 < p.w || j0 + BK - 1 < p.s);
-
-        if (!empty) {
-            const int dq = i - j0 - 4 * g;   // element (kb, e) has i - j = dq - key_of(kb, e)
-            const int jb = j0 + 4 * g;       // and key j = jb + key_of(kb, e)
-            const int kind = full ? 0 : (j0 >= p.s ? 1 : 2);
-            tile_math<D, MODE, ALIBI>(kl, vl, qreg, oacc, m_run, l_run, cs, slope_l2, kind, dq,
-                                      jb, p.w, p.s, qc, g);
-        }
-        if (it + 1 < n_tiles) stage_store<D>(st, lds + ((it + 1) & 1) * T::BUF, tid, rope);
+        const bool next = it + 1 < n_tiles;
+        const int jn = (it + 1 < ts_end ? it + 1 : tw_begin + (it + 1 - ts_end)) * BK;
+        uint16_t *cur = lds + (it & 1) * 2 * T::IMG;
+        uint16_t *nxt = lds + ((it + 1) & 1) * 2 * T::IMG;
+        tile_step<D, MODE, ALIBI, KPRE, VF16>(nxt, nxt + T::IMG, cur, cur + T::IMG, cx, lo, ks,
+                                              qreg, oacc, m_run, l_run, j0, jn, next);
         __syncthreads();
     }
 
@@ -440,21 +565,57 @@ void prefill_mfma_kernel(MfmaParams p) {
     }
 }
 
-template <int D, int GP, int MODE, bool ALIBI>
-hipError_t launch_t(const MfmaParams &mp, int nblocks, hipStream_t st) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, ALIBI>), dim3((unsigned)nblocks),
-                       dim3(256), 0, st, mp);
+template <int D, int GP, int MODE, bool KPRE, bool VF16>
+hipError_t launch_main(const MfmaParams &mp, int nblocks, bool alibi, hipStream_t st) {
+    if (alibi)
+        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, true, KPRE, VF16>), dim3((unsigned)nblocks),
+                           dim3(256), 0, st, mp);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, false, KPRE, VF16>), dim3((unsigned)nblocks),
+                           dim3(256), 0, st, mp);
     return hipGetLastError();
 }
 
+// Staging plan: softmax packs K and V (float16 second product); sigmoid packs K when the
+// same key tile is reused by many workgroups (grouped heads or long windows) and otherwise
+// rotates K on the way in; sigmoid V always comes straight from the input rows.
 template <int D, int GP>
-hipError_t launch_d(const MfmaParams &mp, int nb, int mode, bool alibi, hipStream_t st) {
-    if (mode == 0)
-        return alibi ? launch_t<D, GP, 0, true>(mp, nb, st) : launch_t<D, GP, 0, false>(mp, nb, st);
-    return alibi ? launch_t<D, GP, 1, true>(mp, nb, st) : launch_t<D, GP, 1, false>(mp, nb, st);
+hipError_t launch_gp(const MfmaParams &mp, int nb, int mode, bool alibi, bool kpre, hipStream_t st) {
+    if (mode == 1) return launch_main<D, GP, 1, true, true>(mp, nb, alibi, st);
+    if constexpr (GP == 1)
+        if (!kpre) return launch_main<D, GP, 0, false, false>(mp, nb, alibi, st);
+    return launch_main<D, GP, 0, true, false>(mp, nb, alibi, st);
+}
+
+template <int D>
+hipError_t launch_pack(const PackParams &pp, int nblocks, bool rot, bool pack_v, hipStream_t st) {
+    if (rot) {
+        if (pack_v) hipLaunchKernelGGL((prefill_pack_kernel<D, true, true>), dim3((unsigned)nblocks), dim3(256), 0, st, pp);
+        else hipLaunchKernelGGL((prefill_pack_kernel<D, true, false>), dim3((unsigned)nblocks), dim3(256), 0, st, pp);
+    } else {
+        if (pack_v) hipLaunchKernelGGL((prefill_pack_kernel<D, false, true>), dim3((unsigned)nblocks), dim3(256), 0, st, pp);
+        else hipLaunchKernelGGL((prefill_pack_kernel<D, false, false>), dim3((unsigned)nblocks), dim3(256), 0, st, pp);
+    }
+    return hipGetLastError();
 }
 
 int pack_of(int64_t G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
+struct Plan {
+    bool kpre, vf16;
+    int64_t n_ktiles;
+    size_t img_bytes;  // one full set of K (or V) tile images
+};
+
+Plan plan_of(const PrefillArgs &a) {
+    Plan pl;
+    const int64_t G = a.Hq / a.Hkv;
+    pl.vf16 = a.mode == 1;
+    pl.kpre = pl.vf16 || G >= 2 || a.w > 1024;
+    pl.n_ktiles = (a.N + BK - 1) / BK;
+    pl.img_bytes = (size_t)(a.B * a.Hkv * pl.n_ktiles) * BK * (size_t)a.d * 2;
+    return pl;
+}
 
 }  // namespace
 
@@ -464,16 +625,26 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
     const int64_t nb = a.B * a.Hkv * (G / GP) * ((a.N + 128 / GP - 1) / (128 / GP));
-    // 32-bit block ids and buffer offsets: one K/V slice and the table stay below 2 GiB
+    const int64_t n_kt = (a.N + BK - 1) / BK;
+    // 32-bit block ids and buffer offsets: one K/V slice, one slice of tile images and the
+    // table stay below 2 GiB
     const int64_t slice = (a.N * a.Hkv) * a.d * 2;
+    const int64_t img_slice = n_kt * BK * a.d * 2;
     const int64_t table = a.rope ? a.rope_rows * a.d * 4 : 0;
-    return nb <= 0x7fffffff && slice < (int64_t(1) << 31) && table < (int64_t(1) << 31) &&
-           a.N < (int64_t(1) << 24);
+    return nb <= 0x7fffffff && a.B * a.Hkv * n_kt <= 0x7fffffff && slice < (int64_t(1) << 31) &&
+           img_slice < (int64_t(1) << 31) && table < (int64_t(1) << 31) && a.N < (int64_t(1) << 24);
+}
+
+size_t prefill_mfma_workspace_bytes(const PrefillArgs &a) {
+    if (a.B * a.N == 0) return 0;
+    const Plan pl = plan_of(a);
+    return (pl.kpre ? pl.img_bytes : 0) + (pl.vf16 ? pl.img_bytes : 0);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
-                               const void *v, void *o, hipStream_t st) {
+                               const void *v, void *o, void *ws, hipStream_t st) {
     if (a.B * a.N == 0) return hipSuccess;
+    const Plan pl = plan_of(a);
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
     const int64_t QP = 128 / GP;
@@ -481,12 +652,15 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.q = static_cast<const uint16_t *>(q);
     mp.k = static_cast<const uint16_t *>(k);
     mp.v = static_cast<const uint16_t *>(v);
+    mp.kimg = pl.kpre ? static_cast<const uint16_t *>(ws) : nullptr;
+    mp.vimg = pl.vf16 ? static_cast<const uint16_t *>(ws) + pl.img_bytes / 2 : nullptr;
     mp.o = o;
     mp.slopes = a.slopes;
     mp.rope = a.rope;
     mp.N = a.N; mp.Hq = a.Hq; mp.Hkv = a.Hkv; mp.G = G;
     mp.n_qtiles = (int)((a.N + QP - 1) / QP);
     mp.n_hgroups = (int)(G / GP);
+    mp.n_ktiles = (int)pl.n_ktiles;
     mp.w = (int)(a.w < a.N ? a.w : a.N);
     mp.s = (int)(a.s < a.N ? a.s : a.N);
     mp.cs = a.scale * LOG2E;
@@ -494,16 +668,28 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.row_bytes = (uint32_t)(a.Hkv * a.d * 2);
     mp.rope_bytes = (uint32_t)(a.rope ? a.rope_rows * a.d * 4 : 0);
     mp.out_bf16 = a.out_dt == 1;
+
+    if (pl.kpre) {
+        PackParams pp;
+        pp.k = mp.k; pp.v = mp.v;
+        pp.kimg = static_cast<uint16_t *>(ws);
+        pp.vimg = pl.vf16 ? static_cast<uint16_t *>(ws) + pl.img_bytes / 2 : nullptr;
+        pp.rope = a.rope; pp.N = a.N; pp.Hkv = a.Hkv; pp.n_ktiles = (int)pl.n_ktiles;
+        const int npb = (int)(a.B * a.Hkv * pl.n_ktiles);
+        const hipError_t e = a.d == 64 ? launch_pack<64>(pp, npb, a.rope != nullptr, pl.vf16, st)
+                                       : launch_pack<128>(pp, npb, a.rope != nullptr, pl.vf16, st);
+        if (e != hipSuccess) return e;
+    }
     const int nb = (int)(a.B * a.Hkv * mp.n_hgroups * mp.n_qtiles);
     const bool alibi = a.slopes != nullptr;
     if (a.d == 64) {
-        if (GP == 4) return launch_d<64, 4>(mp, nb, a.mode, alibi, st);
-        if (GP == 2) return launch_d<64, 2>(mp, nb, a.mode, alibi, st);
-        return launch_d<64, 1>(mp, nb, a.mode, alibi, st);
+        if (GP == 4) return launch_gp<64, 4>(mp, nb, a.mode, alibi, pl.kpre, st);
+        if (GP == 2) return launch_gp<64, 2>(mp, nb, a.mode, alibi, pl.kpre, st);
+        return launch_gp<64, 1>(mp, nb, a.mode, alibi, pl.kpre, st);
     }
-    if (GP == 4) return launch_d<128, 4>(mp, nb, a.mode, alibi, st);
-    if (GP == 2) return launch_d<128, 2>(mp, nb, a.mode, alibi, st);
-    return launch_d<128, 1>(mp, nb, a.mode, alibi, st);
+    if (GP == 4) return launch_gp<128, 4>(mp, nb, a.mode, alibi, pl.kpre, st);
+    if (GP == 2) return launch_gp<128, 2>(mp, nb, a.mode, alibi, pl.kpre, st);
+    return launch_gp<128, 1>(mp, nb, a.mode, alibi, pl.kpre, st);
 }
 
 }  // namespace swa

@@ -31,7 +31,7 @@ float resolve_scale(float scale, int64_t d) {
 
 extern "C" {
 
-int swa_version(void) { return 100; }
+int swa_version(void) { return 200; }
 
 const char *swa_status_string(swa_status s) {
     switch (s) {
@@ -45,8 +45,8 @@ const char *swa_status_string(swa_status s) {
 
 int swa_last_hip_error(void) { return g_last_hip_error; }
 
-swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k,
-                       const void *v, void *o, void *stream) {
+// Host-side checks shared by swa_prefill and swa_prefill_workspace_bytes.
+static swa_status check_prefill(const swa_prefill_params *p) {
     if (!p) return SWA_ERR_INVALID_ARGUMENT;
     if (p->B < 0 || p->N < 0 || p->H_q < 1 || p->H_kv < 1 || p->H_q % p->H_kv != 0)
         return SWA_ERR_INVALID_ARGUMENT;
@@ -56,21 +56,44 @@ swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k
     if (!std::isfinite(p->scale)) return SWA_ERR_INVALID_ARGUMENT;
     if (p->rope_table && p->rope_rows < p->N) return SWA_ERR_INVALID_ARGUMENT;
     if (p->d > 256) return SWA_ERR_UNSUPPORTED;
-    const int64_t elems = p->B * p->N;
-    if (elems > 0 && (!q || !k || !v || !o)) return SWA_ERR_INVALID_ARGUMENT;
     // positions travel as float-exact integers and 32-bit grid dimensions
     if (p->N > (int64_t(1) << 24)) return SWA_ERR_UNSUPPORTED;
+    return SWA_OK;
+}
 
-    swa::PrefillArgs a{p->B, p->H_q, p->H_kv, p->N, p->d, p->w, p->s, p->mode, p->in_dtype,
-                       p->out_dtype, resolve_scale(p->scale, p->d), p->alibi_slopes,
-                       p->rope_table, p->rope_table ? p->rope_rows : 0};
+static swa::PrefillArgs prefill_args(const swa_prefill_params *p) {
+    return swa::PrefillArgs{p->B, p->H_q, p->H_kv, p->N, p->d, p->w, p->s, p->mode,
+                            p->in_dtype, p->out_dtype, resolve_scale(p->scale, p->d),
+                            p->alibi_slopes, p->rope_table, p->rope_table ? p->rope_rows : 0};
+}
+
+size_t swa_prefill_workspace_bytes(const swa_prefill_params *p) {
+    if (check_prefill(p) != SWA_OK) return 0;
+    const swa::PrefillArgs a = prefill_args(p);
+    return swa::prefill_mfma_supported(a) ? swa::prefill_mfma_workspace_bytes(a) : 0;
+}
+
+swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k,
+                       const void *v, void *o, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    const swa_status chk = check_prefill(p);
+    if (chk != SWA_OK) return chk;
+    const int64_t elems = p->B * p->N;
+    if (elems > 0 && (!q || !k || !v || !o)) return SWA_ERR_INVALID_ARGUMENT;
+
+    const swa::PrefillArgs a = prefill_args(p);
     hipStream_t st = static_cast<hipStream_t>(stream);
     // the matrix-core kernel moves 16-byte vectors: it needs 16-byte aligned tensors
     const bool aligned = ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                            reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
                            reinterpret_cast<uintptr_t>(p->rope_table)) & 15) == 0;
-    if (aligned && swa::prefill_mfma_supported(a))
-        return hip_status(swa::launch_prefill_mfma(a, q, k, v, o, st));
+    if (aligned && swa::prefill_mfma_supported(a)) {
+        const size_t need = swa::prefill_mfma_workspace_bytes(a);
+        if (need > 0 && (!workspace || workspace_bytes < need ||
+                         (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
+            return SWA_ERR_INVALID_ARGUMENT;
+        return hip_status(swa::launch_prefill_mfma(a, q, k, v, o, workspace, st));
+    }
     if ((a.B * a.N * a.Hq + 3) / 4 > 0x7fffffff) return SWA_ERR_UNSUPPORTED;
     return hip_status(swa::launch_prefill_simt(a, q, k, v, o, st));
 }

@@ -37,11 +37,13 @@ struct DecodeArgs {
 hipError_t launch_prefill_simt(const PrefillArgs &a, const void *q, const void *k,
                                const void *v, void *o, hipStream_t st);
 
-// Matrix-core kernel: bfloat16 inputs, d in {64, 128}. Returns hipErrorNotSupported for
-// shapes it does not cover (the caller then uses the general kernel).
+// Matrix-core kernel: bfloat16 inputs, d in {64, 128}; prefill_mfma_supported tells
+// whether a shape is covered (the caller otherwise uses the general kernel). ws must hold
+// prefill_mfma_workspace_bytes(a) bytes (packed K/V tile images), 16-byte aligned.
 bool prefill_mfma_supported(const PrefillArgs &a);
+size_t prefill_mfma_workspace_bytes(const PrefillArgs &a);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
-                               const void *v, void *o, hipStream_t st);
+                               const void *v, void *o, void *ws, hipStream_t st);
 
 hipError_t launch_rope_table(float *table, int64_t n_pos, int64_t d, double theta,
                              hipStream_t st);

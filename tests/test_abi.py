@@ -61,13 +61,48 @@ DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails va
 ])
 def test_prefill_rejects_bad_arguments(lib, kw, status):
     p = _params(**kw)
-    assert lib.swa_prefill(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, None) == status
+    assert lib.swa_prefill(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, None, 0, None) == status
 
 
 def test_prefill_rejects_null_tensors(lib):
     p = _params()
-    assert lib.swa_prefill(ctypes.byref(p), None, DUMMY, DUMMY, DUMMY, None) == 1
-    assert lib.swa_prefill(None, DUMMY, DUMMY, DUMMY, DUMMY, None) == 1
+    assert lib.swa_prefill(ctypes.byref(p), None, DUMMY, DUMMY, DUMMY, None, 0, None) == 1
+    assert lib.swa_prefill(None, DUMMY, DUMMY, DUMMY, DUMMY, None, 0, None) == 1
+
+
+def _tile_images(B, H_kv, N, d):
+    # one float16 image of every 64-key tile of every (batch, kv head)
+    return B * H_kv * ((N + 63) // 64) * 64 * d * 2
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), "k"),                                       # sigmoid, 2 query heads per kv head
+    (dict(H_q=2, H_kv=2), 0),                            # sigmoid, one head per kv head
+    (dict(H_q=2, H_kv=2, w=2048), "k"),                  # ... with a long window
+    (dict(mode=1), "kv"),                                # softmax packs K and V
+    (dict(mode=1, N=1000, d=128), "kv"),
+    (dict(in_dtype=0), 0),                               # float32 inputs: vector kernel
+    (dict(d=96), 0),                                     # head size without a matrix path
+    (dict(B=0), 0),
+    (dict(w=0), 0),                                      # invalid parameters
+])
+def test_prefill_workspace_bytes(lib, kw, expect):
+    p = _params(**kw)
+    img = _tile_images(p.B, p.H_kv, p.N, p.d)
+    want = {0: 0, "k": img, "kv": 2 * img}[expect]
+    assert lib.swa_prefill_workspace_bytes(ctypes.byref(p)) == want
+
+
+def test_prefill_rejects_missing_or_short_workspace(lib):
+    p = _params(mode=1)
+    need = lib.swa_prefill_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert lib.swa_prefill(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, None, 0, None) == 1
+    assert lib.swa_prefill(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, need - 16,
+                           None) == 1
+    misaligned = ctypes.c_void_p(0x1008)
+    assert lib.swa_prefill(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, misaligned, need,
+                           None) == 1
 
 
 def test_rope_table_rejects_bad_arguments(lib):

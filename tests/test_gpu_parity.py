@@ -62,6 +62,11 @@ SMALL = [
     ("f32", 1, 4, 2, 400, 128, 50, 2, wl.SOFTMAX, True, 1e4),
     ("f32", 1, 2, 1, 97, 32, 20, 0, wl.SIGMOID, True, 1e4),
     ("bf16", 1, 2, 1, 150, 96, 33, 5, wl.SOFTMAX, True, 1e4),
+    # one query head per kv head with a long window: keys packed by the pre-pass
+    ("bf16", 1, 2, 2, 2600, 64, 1100, 3, wl.SIGMOID, True, 1e4),
+    ("bf16", 1, 2, 2, 1500, 128, 1030, 0, wl.SIGMOID, False, 0.0),
+    # keys rotated on the way into LDS, d = 128, no rotation table
+    ("bf16", 2, 2, 2, 450, 128, 100, 2, wl.SIGMOID, True, 0.0),
 ]
 
 
@@ -96,7 +101,8 @@ def _readout_inputs(B, N, Hq, Hkv, d, bits):
 
 @pytest.mark.parametrize("N,w,s,Hq,Hkv,d", [(300, 64, 0, 2, 2, 64), (517, 128, 5, 4, 2, 128),
                                              (260, 1, 3, 2, 1, 64), (200, 300, 0, 4, 4, 128),
-                                             (1030, 512, 7, 8, 2, 128), (900, 100, 130, 2, 2, 64)])
+                                             (1030, 512, 7, 8, 2, 128), (900, 100, 130, 2, 2, 64),
+                                             (2100, 1100, 4, 2, 2, 64), (700, 200, 3, 4, 1, 64)])
 def test_selection_is_bit_exact(N, w, s, Hq, Hkv, d):
     """q = k = 0 makes every weight exactly 1/2; with v_j[c] = bit c of j the float32 output
     is 1/2 * #{j in K(i) with bit c set}: exact small integers that identify the key set."""
