@@ -80,11 +80,14 @@ def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
     slopes = wl.slopes_tensor(cfg.slopes, device="cuda")
     table = swa.swa_rope_table(cfg.N, cfg.d, cfg.rope_theta) if cfg.rope_theta > 0 else None
     out = torch.empty((cfg.B, cfg.N, cfg.H_q, cfg.d), dtype=out_dtype, device="cuda")
+    ws_bytes = swa.swa_prefill_workspace_bytes(q, k, w=cfg.w, s=cfg.s, mode=cfg.mode,
+                                               out_dtype=out_dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
         swa.swa_prefill(q, k, v, w=cfg.w, s=cfg.s, mode=cfg.mode, alibi_slopes=slopes,
-                        rope_table=table, out=out, stream=stream)
+                        rope_table=table, out=out, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         step()

@@ -61,8 +61,8 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * bf16 inputs with d in {64, 128} and 16-byte aligned tensors run on the matrix cores,
  * which form the score product from float16 operands (rotated q and k) and the value
  * product from float16 (softmax) or bf16 (sigmoid) operands, with float32 accumulation:
- * those inputs must stay within the float16 range (|x| < 65504). Other shapes run on a
- * general float32 vector kernel.
+ * those inputs must stay within the float16 range (|x| < 65504), and |slope| / scale below
+ * 2^24. Other shapes run on a general float32 vector kernel.
  */
 typedef struct swa_prefill_params {
     int64_t B, H_q, H_kv, N, d;
@@ -79,11 +79,11 @@ typedef struct swa_prefill_params {
 
 /*
  * workspace: device scratch of at least swa_prefill_workspace_bytes(p) bytes, 16-byte
- * aligned (may be NULL when that is 0). The matrix-core path uses it for keys rotated once
- * into float16 tile images (and, for softmax, values converted to float16) when a key tile
- * is shared by many workgroups. Its contents on entry do not matter; calls that share a
- * workspace must not overlap. A workspace that is too small or misaligned for a call that
- * needs one is rejected with SWA_ERR_INVALID_ARGUMENT.
+ * aligned (may be NULL when that is 0). The matrix-core path uses it for the keys, rotated
+ * once into float16 tile images, and for softmax also the values converted to float16:
+ * B * H_kv * ceil(N / 64) * 64 * d * 2 bytes each. Its contents on entry do not matter;
+ * calls that share a workspace must not overlap. A workspace that is too small or
+ * misaligned for a call that needs one is rejected with SWA_ERR_INVALID_ARGUMENT.
  */
 swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k,
                        const void *v, void *o, void *workspace, size_t workspace_bytes,

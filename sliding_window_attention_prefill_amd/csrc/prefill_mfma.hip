@@ -20,17 +20,17 @@
 //     rescaled accumulator. O^T += V^T P^T takes the weights straight from registers.
 //   * Score operands are float16: q and k are widened from bf16, rotated in float32 and
 //     rounded once (inputs must stay within the float16 range, |x| < 65504).
-//   * Tile staging, chosen per problem by the host:
-//       - K rotated on the way in: buffer loads into registers, rotation, LDS store;
-//       - K from a packed image: a pre-pass rotates every key once into float16 tile images
-//         laid out exactly as LDS holds them, and the main kernel copies them with
-//         buffer-to-LDS transfers (no registers, no vector instructions);
-//       - V as stored (bf16, sigmoid): buffer-to-LDS transfers of the input rows; the second
-//         product runs in bf16 with the weights rounded to bf16;
-//       - V from a packed float16 image (softmax): the pre-pass converts it once, and the
-//         second product runs in float16.
-//     V stays row-major in LDS; the transposing LDS read (ds_read_b64_tr_b16) delivers it in
-//     the operand layout of the second product, in the key order of the score registers.
+//   * A pre-pass rotates every key once into float16 tile images laid out exactly as LDS
+//     holds them (for softmax it also converts V to float16 images); the main kernel copies
+//     tiles with buffer-to-LDS transfers, which take no registers and no vector
+//     instructions. Sigmoid reads V rows as stored (bf16) with the same transfers, and its
+//     second product runs in bf16 with the weights rounded to bf16; softmax's runs in
+//     float16. V stays row-major in LDS: the transposing LDS read (ds_read_b64_tr_b16)
+//     delivers it in the operand layout of the second product, in the key order of the
+//     score registers.
+//   * ALiBi: the key part of the bias enters the score accumulator through one more matrix
+//     instruction per 32-key block (exact key offsets against a two-term float16 split of
+//     the slope), so each score needs one FMA for scale and bias together.
 //   * LDS rows are XOR-swizzled in 16-byte chunks so that the row reads of K and the
 //     transposing reads of V are free of bank conflicts; the register path, the transfers
 //     and the pre-pass all write that swizzle.
@@ -89,7 +89,6 @@ struct MfmaParams {
     float cs;                 // scale * log2(e)
     uint32_t kv_bytes;        // bytes of one (batch, kv head) K or V slice, rows [0, N)
     uint32_t row_bytes;       // bytes between consecutive positions of K/V
-    uint32_t rope_bytes;      // bytes of the rotation table
     int out_bf16;
 };
 
@@ -176,44 +175,6 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
 // ---------------------------------------------------------------------------------------
 // Main kernel pieces.
 
-// K tile staged through registers (rotated on the way into LDS).
-template <int D>
-struct KStage {
-    uint4 k[Tile<D>::KPT];
-    float4 cs[Tile<D>::KPT][2];
-};
-
-template <int D>
-__device__ __forceinline__ void kstage_load(KStage<D> &st, __amdgpu_buffer_rsrc_t rk,
-                                            __amdgpu_buffer_rsrc_t rt, uint32_t row_bytes,
-                                            int j0, int tid, bool rope) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int r = 0; r < T::KPT; ++r) {
-        const int c = tid + 256 * r;
-        const int j = j0 + c / T::C, c8 = c % T::C;
-        st.k[r] = buf_load16(rk, (uint32_t)j * row_bytes + c8 * 16);
-        if (rope) {
-            const uint32_t toff = ((uint32_t)j * (D / 2) + c8 * 4) * 8;
-            st.cs[r][0] = buf_load16f(rt, toff);
-            st.cs[r][1] = buf_load16f(rt, toff + 16);
-        }
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void kstage_store(const KStage<D> &st, uint16_t *__restrict__ dst,
-                                             int tid, bool rope) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int r = 0; r < T::KPT; ++r) {
-        const int c = tid + 256 * r;
-        const int row = c / T::C, c8 = c % T::C;
-        const uint4 x = rope ? rotate_chunk(st.k[r], st.cs[r][0], st.cs[r][1]) : convert_chunk(st.k[r]);
-        *reinterpret_cast<uint4 *>(dst + (row * T::C + (c8 ^ kswz<D>(row))) * 8) = x;
-    }
-}
-
 // Per-lane offsets, fixed for the whole kernel.
 template <int D>
 struct LaneOffsets {
@@ -256,24 +217,57 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
         }
 }
 
+// Operands of one extra matrix instruction per 32-key block that puts the key part of the
+// ALiBi bias into the score accumulator: with r = slope log2(e) / cs split as
+// 2^a (hi + lo) in float16, A row m holds (2^a kappa, 2^a kappa) and every B column
+// (-hi, -lo) in k = 0, 1, so the product is -r kappa for the key kappa = 32 kb + m of the
+// tile (kappa 2^a is exact in float16, and hi + lo carries r to about 22 bits).
+struct BiasOperands {
+    f16x8_t a[2];
+    f16x8_t b;
+};
+
+__device__ __forceinline__ BiasOperands bias_operands(float r, int lane) {
+    int ex = 0;
+    (void)frexpf(r, &ex);                      // |r| = m 2^ex, m in [0.5, 1)
+    int a = ex - 1;
+    a = a < -24 ? -24 : (a > 9 ? 9 : a);       // kappa 2^a stays exact for kappa < 64
+    const float rs = ldexpf(r, -a);
+    const _Float16 hi = (_Float16)rs;
+    const _Float16 lo = (_Float16)(rs - (float)hi);
+    BiasOperands bo;
+    const f16x8_t z = {};
+    bo.a[0] = z; bo.a[1] = z; bo.b = z;
+    if (lane < 32) {
+        const _Float16 k0 = (_Float16)ldexpf((float)lane, a);
+        const _Float16 k1 = (_Float16)ldexpf((float)(lane + 32), a);
+        bo.a[0][0] = k0; bo.a[0][1] = k0;
+        bo.a[1][0] = k1; bo.a[1][1] = k1;
+        bo.b[0] = -hi; bo.b[1] = -lo;
+    }
+    return bo;
+}
+
 // One 64-key tile for one wavefront: S^T = K Q^T, weights, O^T += V^T P^T.
 // kind: 0 = every pair in the key set, 1 = cut by the window edges, 2 = also holds sinks.
 template <int D, int MODE, bool ALIBI, bool VF16>
 __device__ __forceinline__ void tile_math(const uint16_t *__restrict__ kl,
                                           const uint16_t *__restrict__ vl,
-                                          const LaneOffsets<D> &lo, const f16x8_t (&qreg)[D / 16],
+                                          const LaneOffsets<D> &lo, const BiasOperands &bo,
+                                          const f16x8_t (&qreg)[D / 16],
                                           f32x16_t (&oacc)[D / 32], float &m_run, float &l_run,
-                                          float cs, float slope_l2, int kind, int dq, int jb,
+                                          float cs, float bias_q, int kind, int dq, int jb,
                                           int w, int s) {
     constexpr int KS = D / 16, DB = D / 32;
     f32x16_t sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const f16x8_t a0 = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + lo.k[0]);
         const f32x16_t zero = {};
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, qreg[0], zero, 0, 0, 0);
+        // with ALiBi the product starts from -(slope log2(e) / cs) (j - j0), so that the
+        // score accumulator already holds the key part of the bias
+        sacc[kb] = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bo.b, zero, 0, 0, 0) : zero;
 #pragma unroll
-        for (int ks = 1; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + lo.k[ks]);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sacc[kb], 0, 0, 0);
         }
@@ -281,26 +275,23 @@ __device__ __forceinline__ void tile_math(const uint16_t *__restrict__ kl,
     if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s);
     else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s);
 
-    const float bias0 = slope_l2 * (float)dq;  // slope log2(e) (i - j) for key_of = 0
+    // x log2(e) = cs * acc + bias_q, bias_q = slope log2(e) (i - j0) (zero without ALiBi)
     if (MODE == 0) {
         // sigma(x) = 1 / (1 + 2^t) with t = -x log2(e); an excluded key has t = +inf -> 0
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                // -x log2(e) = -(cs * score + slope log2(e) (i - j)), i - j = dq - key_of
-                const float nb = ALIBI ? fmaf(slope_l2, (float)key_of(kb, e), -bias0) : 0.0f;
-                const float t = fmaf(sacc[kb][e], -cs, nb);
+                const float t = fmaf(sacc[kb][e], -cs, -bias_q);
                 sacc[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
             }
     } else {
-        // base-2 logits x = cs * score + slope log2(e) (i - j); excluded keys stay -inf
+        // base-2 logits; excluded keys stay -inf
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                sacc[kb][e] = ALIBI ? fmaf(sacc[kb][e], cs, fmaf(-slope_l2, (float)key_of(kb, e), bias0))
-                                    : sacc[kb][e] * cs;
+                sacc[kb][e] = ALIBI ? fmaf(sacc[kb][e], cs, bias_q) : sacc[kb][e] * cs;
         float mx[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -370,21 +361,19 @@ __device__ __forceinline__ void tile_math(const uint16_t *__restrict__ kl,
 }
 
 struct TileCtx {
-    __amdgpu_buffer_rsrc_t rk, rv, rt;
+    __amdgpu_buffer_rsrc_t rk, rv;
     uint32_t row_bytes;
     int tid, wave, qa, qb, i, g, w, s, N;
     float cs, slope_l2;
-    bool rope;
 };
 
-// Loads of tile jn into buffer (nk, nv): K by transfer or into registers, V by transfer.
-template <int D, bool KPRE, bool VF16>
+// Transfers of tile jn into buffer (nk, nv): the packed K image, and V as a packed image
+// (VF16) or straight from the input rows.
+template <int D, bool VF16>
 __device__ __forceinline__ void issue_loads(uint16_t *__restrict__ nk, uint16_t *__restrict__ nv,
-                                            const TileCtx &cx, const LaneOffsets<D> &lo,
-                                            KStage<D> &ks, int jn) {
+                                            const TileCtx &cx, const LaneOffsets<D> &lo, int jn) {
     using T = Tile<D>;
-    if (KPRE) dma_tile<D>(nk, cx.rk, (uint32_t)(jn / BK) * T::IMG_BYTES, lo.dimg, cx.wave);
-    else kstage_load<D>(ks, cx.rk, cx.rt, cx.row_bytes, jn, cx.tid, cx.rope);
+    dma_tile<D>(nk, cx.rk, (uint32_t)(jn / BK) * T::IMG_BYTES, lo.dimg, cx.wave);
     if (VF16) dma_tile<D>(nv, cx.rv, (uint32_t)(jn / BK) * T::IMG_BYTES, lo.dimg, cx.wave);
     else dma_tile<D>(nv, cx.rv, (uint32_t)jn * cx.row_bytes, lo.dvraw, cx.wave);
 }
@@ -392,14 +381,14 @@ __device__ __forceinline__ void issue_loads(uint16_t *__restrict__ nk, uint16_t 
 // One step of the tile loop. The next tile's buffer and the current one are distinct
 // restrict pointers, so the reads of the current tile do not wait for the transfers into
 // the next one.
-template <int D, int MODE, bool ALIBI, bool KPRE, bool VF16>
+template <int D, int MODE, bool ALIBI, bool VF16>
 __device__ __forceinline__ void tile_step(uint16_t *__restrict__ nk, uint16_t *__restrict__ nv,
                                           const uint16_t *__restrict__ ck,
                                           const uint16_t *__restrict__ cv, const TileCtx &cx,
-                                          const LaneOffsets<D> &lo, KStage<D> &ks,
+                                          const LaneOffsets<D> &lo, const BiasOperands &bo,
                                           const f16x8_t (&qreg)[D / 16], f32x16_t (&oacc)[D / 32],
                                           float &m_run, float &l_run, int j0, int jn, bool next) {
-    if (next) issue_loads<D, KPRE, VF16>(nk, nv, cx, lo, ks, jn);
+    if (next) issue_loads<D, VF16>(nk, nv, cx, lo, jn);
     // classify the tile for this wavefront's queries [qa, qb] (wave-uniform)
     const bool empty = cx.qa >= cx.N || j0 > cx.qb || (cx.qa - (j0 + BK - 1) >= cx.w && j0 >= cx.s);
     const bool full = (j0 + BK - 1 <= cx.qa) && (cx.qb - j0 < cx.w || j0 + BK - 1 < cx.s);
@@ -407,14 +396,13 @@ __device__ __forceinline__ void tile_step(uint16_t *__restrict__ nk, uint16_t *_
         const int dq = cx.i - j0 - 4 * cx.g;   // element (kb, e) has i - j = dq - key_of(kb, e)
         const int jb = j0 + 4 * cx.g;          // and key j = jb + key_of(kb, e)
         const int kind = full ? 0 : (j0 >= cx.s ? 1 : 2);
-        tile_math<D, MODE, ALIBI, VF16>(ck, cv, lo, qreg, oacc, m_run, l_run, cx.cs, cx.slope_l2,
-                                        kind, dq, jb, cx.w, cx.s);
+        tile_math<D, MODE, ALIBI, VF16>(ck, cv, lo, bo, qreg, oacc, m_run, l_run, cx.cs,
+                                        cx.slope_l2 * (float)(cx.i - j0), kind, dq, jb, cx.w, cx.s);
     }
-    if (!KPRE && next) kstage_store<D>(ks, nk, cx.tid, cx.rope);
 }
 
-// Register budget: 3 wavefronts per SIMD at d = 64, 2 at d = 128.
-template <int D, int GP, int MODE, bool ALIBI, bool KPRE, bool VF16>
+// Register budget: 3 wavefronts per SIMD at d = 64 (4 fit), 2 at d = 128.
+template <int D, int GP, int MODE, bool ALIBI, bool VF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
 void prefill_mfma_kernel(MfmaParams p) {
     using T = Tile<D>;
@@ -451,16 +439,15 @@ void prefill_mfma_kernel(MfmaParams p) {
         const int64_t kvoff = ((int64_t)b * p.N * p.Hkv + hkv) * D;
         const int64_t imoff = ((int64_t)b * p.Hkv + hkv) * p.n_ktiles * T::IMG;
         const uint32_t imbytes = (uint32_t)p.n_ktiles * T::IMG_BYTES;
-        cx.rk = KPRE ? make_rsrc(p.kimg + imoff, imbytes) : make_rsrc(p.k + kvoff, p.kv_bytes);
+        cx.rk = make_rsrc(p.kimg + imoff, imbytes);
         cx.rv = VF16 ? make_rsrc(p.vimg + imoff, imbytes) : make_rsrc(p.v + kvoff, p.kv_bytes);
-        cx.rt = make_rsrc(p.rope, (!KPRE && rope) ? p.rope_bytes : 0);
         cx.row_bytes = p.row_bytes;
         cx.tid = tid; cx.wave = wave; cx.qa = qa; cx.qb = qa + 31 < N ? qa + 31 : N - 1;
         cx.i = i; cx.g = g; cx.w = p.w; cx.s = p.s; cx.N = N;
         cx.cs = p.cs;
         cx.slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;  // bias in base-2 units
-        cx.rope = rope;
     }
+    const BiasOperands bo = bias_operands(ALIBI ? cx.slope_l2 / p.cs : 0.0f, lane);
 
     LaneOffsets<D> lo;
 #pragma unroll
@@ -517,9 +504,7 @@ void prefill_mfma_kernel(MfmaParams p) {
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
     float m_run = -1e30f, l_run = 0.0f;
 
-    KStage<D> ks;
-    issue_loads<D, KPRE, VF16>(lds, lds + T::IMG, cx, lo, ks, (ts_end > 0 ? 0 : tw_begin) * BK);
-    if (!KPRE) kstage_store<D>(ks, lds, tid, rope);
+    issue_loads<D, VF16>(lds, lds + T::IMG, cx, lo, (ts_end > 0 ? 0 : tw_begin) * BK);
     __syncthreads();
 
     for (int it = 0; it < n_tiles; ++it) {
@@ -528,8 +513,8 @@ void prefill_mfma_kernel(MfmaParams p) {
         const int jn = (it + 1 < ts_end ? it + 1 : tw_begin + (it + 1 - ts_end)) * BK;
         uint16_t *cur = lds + (it & 1) * 2 * T::IMG;
         uint16_t *nxt = lds + ((it + 1) & 1) * 2 * T::IMG;
-        tile_step<D, MODE, ALIBI, KPRE, VF16>(nxt, nxt + T::IMG, cur, cur + T::IMG, cx, lo, ks,
-                                              qreg, oacc, m_run, l_run, j0, jn, next);
+        tile_step<D, MODE, ALIBI, VF16>(nxt, nxt + T::IMG, cur, cur + T::IMG, cx, lo, bo, qreg,
+                                        oacc, m_run, l_run, j0, jn, next);
         __syncthreads();
     }
 
@@ -565,26 +550,22 @@ void prefill_mfma_kernel(MfmaParams p) {
     }
 }
 
-template <int D, int GP, int MODE, bool KPRE, bool VF16>
+template <int D, int GP, int MODE, bool VF16>
 hipError_t launch_main(const MfmaParams &mp, int nblocks, bool alibi, hipStream_t st) {
     if (alibi)
-        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, true, KPRE, VF16>), dim3((unsigned)nblocks),
+        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, true, VF16>), dim3((unsigned)nblocks),
                            dim3(256), 0, st, mp);
     else
-        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, false, KPRE, VF16>), dim3((unsigned)nblocks),
+        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, false, VF16>), dim3((unsigned)nblocks),
                            dim3(256), 0, st, mp);
     return hipGetLastError();
 }
 
-// Staging plan: softmax packs K and V (float16 second product); sigmoid packs K when the
-// same key tile is reused by many workgroups (grouped heads or long windows) and otherwise
-// rotates K on the way in; sigmoid V always comes straight from the input rows.
+// Softmax packs V to float16 as well (float16 second product); sigmoid reads V as stored.
 template <int D, int GP>
-hipError_t launch_gp(const MfmaParams &mp, int nb, int mode, bool alibi, bool kpre, hipStream_t st) {
-    if (mode == 1) return launch_main<D, GP, 1, true, true>(mp, nb, alibi, st);
-    if constexpr (GP == 1)
-        if (!kpre) return launch_main<D, GP, 0, false, false>(mp, nb, alibi, st);
-    return launch_main<D, GP, 0, true, false>(mp, nb, alibi, st);
+hipError_t launch_gp(const MfmaParams &mp, int nb, int mode, bool alibi, hipStream_t st) {
+    if (mode == 1) return launch_main<D, GP, 1, true>(mp, nb, alibi, st);
+    return launch_main<D, GP, 0, false>(mp, nb, alibi, st);
 }
 
 template <int D>
@@ -602,16 +583,14 @@ hipError_t launch_pack(const PackParams &pp, int nblocks, bool rot, bool pack_v,
 int pack_of(int64_t G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 
 struct Plan {
-    bool kpre, vf16;
+    bool vf16;
     int64_t n_ktiles;
     size_t img_bytes;  // one full set of K (or V) tile images
 };
 
 Plan plan_of(const PrefillArgs &a) {
     Plan pl;
-    const int64_t G = a.Hq / a.Hkv;
     pl.vf16 = a.mode == 1;
-    pl.kpre = pl.vf16 || G >= 2 || a.w > 1024;
     pl.n_ktiles = (a.N + BK - 1) / BK;
     pl.img_bytes = (size_t)(a.B * a.Hkv * pl.n_ktiles) * BK * (size_t)a.d * 2;
     return pl;
@@ -638,7 +617,7 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
 size_t prefill_mfma_workspace_bytes(const PrefillArgs &a) {
     if (a.B * a.N == 0) return 0;
     const Plan pl = plan_of(a);
-    return (pl.kpre ? pl.img_bytes : 0) + (pl.vf16 ? pl.img_bytes : 0);
+    return pl.img_bytes + (pl.vf16 ? pl.img_bytes : 0);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
@@ -652,7 +631,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.q = static_cast<const uint16_t *>(q);
     mp.k = static_cast<const uint16_t *>(k);
     mp.v = static_cast<const uint16_t *>(v);
-    mp.kimg = pl.kpre ? static_cast<const uint16_t *>(ws) : nullptr;
+    mp.kimg = static_cast<const uint16_t *>(ws);
     mp.vimg = pl.vf16 ? static_cast<const uint16_t *>(ws) + pl.img_bytes / 2 : nullptr;
     mp.o = o;
     mp.slopes = a.slopes;
@@ -666,10 +645,9 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.cs = a.scale * LOG2E;
     mp.kv_bytes = (uint32_t)(((a.N - 1) * a.Hkv + 1) * a.d * 2);
     mp.row_bytes = (uint32_t)(a.Hkv * a.d * 2);
-    mp.rope_bytes = (uint32_t)(a.rope ? a.rope_rows * a.d * 4 : 0);
     mp.out_bf16 = a.out_dt == 1;
 
-    if (pl.kpre) {
+    {
         PackParams pp;
         pp.k = mp.k; pp.v = mp.v;
         pp.kimg = static_cast<uint16_t *>(ws);
@@ -683,13 +661,13 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     const int nb = (int)(a.B * a.Hkv * mp.n_hgroups * mp.n_qtiles);
     const bool alibi = a.slopes != nullptr;
     if (a.d == 64) {
-        if (GP == 4) return launch_gp<64, 4>(mp, nb, a.mode, alibi, pl.kpre, st);
-        if (GP == 2) return launch_gp<64, 2>(mp, nb, a.mode, alibi, pl.kpre, st);
-        return launch_gp<64, 1>(mp, nb, a.mode, alibi, pl.kpre, st);
+        if (GP == 4) return launch_gp<64, 4>(mp, nb, a.mode, alibi, st);
+        if (GP == 2) return launch_gp<64, 2>(mp, nb, a.mode, alibi, st);
+        return launch_gp<64, 1>(mp, nb, a.mode, alibi, st);
     }
-    if (GP == 4) return launch_gp<128, 4>(mp, nb, a.mode, alibi, pl.kpre, st);
-    if (GP == 2) return launch_gp<128, 2>(mp, nb, a.mode, alibi, pl.kpre, st);
-    return launch_gp<128, 1>(mp, nb, a.mode, alibi, pl.kpre, st);
+    if (GP == 4) return launch_gp<128, 4>(mp, nb, a.mode, alibi, st);
+    if (GP == 2) return launch_gp<128, 2>(mp, nb, a.mode, alibi, st);
+    return launch_gp<128, 1>(mp, nb, a.mode, alibi, st);
 }
 
 }  // namespace swa

@@ -77,8 +77,7 @@ def _tile_images(B, H_kv, N, d):
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(), "k"),                                       # sigmoid, 2 query heads per kv head
-    (dict(H_q=2, H_kv=2), 0),                            # sigmoid, one head per kv head
-    (dict(H_q=2, H_kv=2, w=2048), "k"),                  # ... with a long window
+    (dict(H_q=2, H_kv=2), "k"),                          # sigmoid, one head per kv head
     (dict(mode=1), "kv"),                                # softmax packs K and V
     (dict(mode=1, N=1000, d=128), "kv"),
     (dict(in_dtype=0), 0),                               # float32 inputs: vector kernel
