@@ -8,10 +8,10 @@
 //   K(i) = { j <= i : i - j < w or j < s },  p = sigmoid (no normalisation) or softmax.
 //
 // How (gfx950):
-//   * One workgroup (4 wavefronts) owns 128 query rows: 128/GP positions x GP query heads
-//     that share one kv head, so each K/V tile in LDS serves the whole group.
-//   * It walks only the 64-key tiles that intersect its band [q0 - w + 1, q0 + 127] plus
-//     the sink tiles the window no longer covers (the block skipping the glossary describes
+//   * One workgroup (4 wavefronts at d = 64, 8 at d = 128) owns 32 query rows per wavefront:
+//     positions x GP query heads that share one kv head, so each K/V tile in LDS serves the
+//     whole group and is fetched by fewer workgroups.
+//   * It walks only the 64-key tiles that intersect its band of keys plus the sink tiles the window no longer covers (the block skipping the glossary describes
 //     for windowed exact-attention kernels). Tiles inside every row's key set run without
 //     the element predicate.
 //   * Each wavefront computes S^T = K Q^T (32 keys x 32 queries per 32x32x16 matrix
@@ -57,12 +57,14 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int D>
 struct Tile {
+    static constexpr int NW = 4;                         // wavefronts per workgroup
     static constexpr int C = D / 8;                      // 16-byte chunks per row
     static constexpr int IMG = BK * D;                   // 16-bit elements of a K or V tile
     static constexpr int IMG_BYTES = IMG * 2;
-    static constexpr int DMA_W = IMG_BYTES / (4 * 1024); // 1 KB transfers per wavefront
-    static constexpr int KPT = BK * C / 256;             // K chunks per thread (register path)
+    static constexpr int DMA_W = IMG_BYTES / (NW * 1024); // 1 KB transfers per wavefront
+    static constexpr int KPT = BK * C / 256;             // chunks per thread of the pre-pass
     static constexpr int OSTR = D + 4;                   // floats per output row in LDS
+    // four wavefronts stage their output rows at a time
     static constexpr int LDS_BYTES = cmax(2 * 2 * IMG_BYTES, 4 * 32 * OSTR * 4);
 };
 
@@ -248,45 +250,39 @@ __device__ __forceinline__ BiasOperands bias_operands(float r, int lane) {
     return bo;
 }
 
-// One 64-key tile for one wavefront: S^T = K Q^T, weights, O^T += V^T P^T.
-// kind: 0 = every pair in the key set, 1 = cut by the window edges, 2 = also holds sinks.
-template <int D, int MODE, bool ALIBI, bool VF16>
-__device__ __forceinline__ void tile_math(const uint16_t *__restrict__ kl,
-                                          const uint16_t *__restrict__ vl,
-                                          const LaneOffsets<D> &lo, const BiasOperands &bo,
-                                          const f16x8_t (&qreg)[D / 16],
-                                          f32x16_t (&oacc)[D / 32], float &m_run, float &l_run,
-                                          float cs, float bias_q, int kind, int dq, int jb,
-                                          int w, int s) {
-    constexpr int KS = D / 16, DB = D / 32;
-    f32x16_t sacc[2];
+// S^T = K Q^T for the 64 keys of one tile (two 32-key blocks, whose chains alternate); with
+// ALiBi each block starts from the key part of the bias.
+template <int D, bool ALIBI>
+__device__ __forceinline__ void qk_tile(const uint16_t *__restrict__ kl, const LaneOffsets<D> &lo,
+                                        const BiasOperands &bo, const f16x8_t (&qreg)[D / 16],
+                                        f32x16_t (&sacc)[2]) {
+    constexpr int KS = D / 16;
+    const f32x16_t zero = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const f32x16_t zero = {};
-        // with ALiBi the product starts from -(slope log2(e) / cs) (j - j0), so that the
-        // score accumulator already holds the key part of the bias
+    for (int kb = 0; kb < 2; ++kb)
         sacc[kb] = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bo.b, zero, 0, 0, 0) : zero;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
             const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + lo.k[ks]);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sacc[kb], 0, 0, 0);
         }
-    }
+}
+
+// Scores of one tile made ready for weighting (run in the step that formed them): edge
+// masking, and for softmax the base-2 logits x log2(e) = cs * acc + bias_q
+// (bias_q = slope log2(e) (i - j0), zero without ALiBi) with the running maximum and the
+// lazy rescale of the accumulator.
+template <int D, int MODE, bool ALIBI>
+__device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
+                                            float &m_run, float &l_run, float cs, float bias_q,
+                                            int kind, int dq, int jb, int w, int s) {
+    constexpr int DB = D / 32;
     if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s);
     else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s);
-
-    // x log2(e) = cs * acc + bias_q, bias_q = slope log2(e) (i - j0) (zero without ALiBi)
-    if (MODE == 0) {
-        // sigma(x) = 1 / (1 + 2^t) with t = -x log2(e); an excluded key has t = +inf -> 0
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float t = fmaf(sacc[kb][e], -cs, -bias_q);
-                sacc[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
-            }
-    } else {
-        // base-2 logits; excluded keys stay -inf
+    if (MODE == 1) {
+        // excluded keys stay -inf
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -302,8 +298,8 @@ __device__ __forceinline__ void tile_math(const uint16_t *__restrict__ kl,
         float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m_run, mt);
-        // lazy rescale: keep the stale maximum while the new one exceeds it by less than 8
-        // (weights stay below 2^8); the final division uses the same maximum.
+        // keep the stale maximum while the new one exceeds it by less than 8 (weights stay
+        // below 2^8); the final division uses the same maximum.
         const bool need = m_new > m_run + 8.0f;
         if (__any(need)) {
             const float corr = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -314,6 +310,25 @@ __device__ __forceinline__ void tile_math(const uint16_t *__restrict__ kl,
             l_run *= corr;
             m_run = need ? m_new : m_run;
         }
+    }
+}
+
+// Weights of one prepared tile, then O^T += V^T P^T.
+template <int D, int MODE, bool VF16>
+__device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const LaneOffsets<D> &lo,
+                                         f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
+                                         float m_run, float &l_run, float cs, float bias_q) {
+    constexpr int DB = D / 32;
+    if (MODE == 0) {
+        // sigma(x) = 1 / (1 + 2^t) with t = -x log2(e); an excluded key has t = +inf -> 0
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float t = fmaf(sacc[kb][e], -cs, -bias_q);
+                sacc[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
+            }
+    } else {
         float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -364,53 +379,79 @@ struct TileCtx {
     __amdgpu_buffer_rsrc_t rk, rv;
     uint32_t row_bytes;
     int tid, wave, qa, qb, i, g, w, s, N;
+    int n_tiles, ts_end, tw_begin;  // the walk: sink tiles [0, ts_end), then window tiles
     float cs, slope_l2;
+
+    __device__ __forceinline__ int j0_of(int t) const {
+        return (t < ts_end ? t : tw_begin + (t - ts_end)) * BK;
+    }
+    // 0 = every pair in the key set, 1 = cut by the window edges, 2 = also holds sinks,
+    // -1 = no pair in the key set (wave-uniform: this wavefront's queries [qa, qb])
+    __device__ __forceinline__ int kind_of(int j0) const {
+        if (qa >= N || j0 > qb || (qa - (j0 + BK - 1) >= w && j0 >= s)) return -1;
+        if ((j0 + BK - 1 <= qa) && (qb - j0 < w || j0 + BK - 1 < s)) return 0;
+        return j0 >= s ? 1 : 2;
+    }
 };
 
-// Transfers of tile jn into buffer (nk, nv): the packed K image, and V as a packed image
-// (VF16) or straight from the input rows.
+// Transfers into a K or V tile buffer: packed images, or V straight from the input rows.
+template <int D>
+__device__ __forceinline__ void load_k(uint16_t *__restrict__ dst, const TileCtx &cx,
+                                       const LaneOffsets<D> &lo, int j0) {
+    dma_tile<D>(dst, cx.rk, (uint32_t)(j0 / BK) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
+}
 template <int D, bool VF16>
-__device__ __forceinline__ void issue_loads(uint16_t *__restrict__ nk, uint16_t *__restrict__ nv,
-                                            const TileCtx &cx, const LaneOffsets<D> &lo, int jn) {
-    using T = Tile<D>;
-    dma_tile<D>(nk, cx.rk, (uint32_t)(jn / BK) * T::IMG_BYTES, lo.dimg, cx.wave);
-    if (VF16) dma_tile<D>(nv, cx.rv, (uint32_t)(jn / BK) * T::IMG_BYTES, lo.dimg, cx.wave);
-    else dma_tile<D>(nv, cx.rv, (uint32_t)jn * cx.row_bytes, lo.dvraw, cx.wave);
+__device__ __forceinline__ void load_v(uint16_t *__restrict__ dst, const TileCtx &cx,
+                                       const LaneOffsets<D> &lo, int j0) {
+    if (VF16) dma_tile<D>(dst, cx.rv, (uint32_t)(j0 / BK) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
+    else dma_tile<D>(dst, cx.rv, (uint32_t)j0 * cx.row_bytes, lo.dvraw, cx.wave);
 }
 
-// One step of the tile loop. The next tile's buffer and the current one are distinct
-// restrict pointers, so the reads of the current tile do not wait for the transfers into
-// the next one.
+// Step t of the software pipeline. On entry s_cur holds the prepared scores of tile t, K
+// buffer k_next holds tile t + 1 and V buffer v_cur tile t. The step starts the transfers of
+// K tile t + 2 (into k_fill, free since tile t's scores were formed) and V tile t + 1 (into
+// v_fill, free since tile t - 1's product), forms the scores of tile t + 1 while it weighs
+// tile t, and prepares tile t + 1's scores.
+// The four buffers are distinct restrict pointers, so no LDS read here waits for the
+// transfers this step starts.
 template <int D, int MODE, bool ALIBI, bool VF16>
-__device__ __forceinline__ void tile_step(uint16_t *__restrict__ nk, uint16_t *__restrict__ nv,
-                                          const uint16_t *__restrict__ ck,
-                                          const uint16_t *__restrict__ cv, const TileCtx &cx,
+__device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
+                                          uint16_t *__restrict__ v_fill,
+                                          const uint16_t *__restrict__ k_next,
+                                          const uint16_t *__restrict__ v_cur, const TileCtx &cx,
                                           const LaneOffsets<D> &lo, const BiasOperands &bo,
-                                          const f16x8_t (&qreg)[D / 16], f32x16_t (&oacc)[D / 32],
-                                          float &m_run, float &l_run, int j0, int jn, bool next) {
-    if (next) issue_loads<D, VF16>(nk, nv, cx, lo, jn);
-    // classify the tile for this wavefront's queries [qa, qb] (wave-uniform)
-    const bool empty = cx.qa >= cx.N || j0 > cx.qb || (cx.qa - (j0 + BK - 1) >= cx.w && j0 >= cx.s);
-    const bool full = (j0 + BK - 1 <= cx.qa) && (cx.qb - j0 < cx.w || j0 + BK - 1 < cx.s);
-    if (!empty) {
-        const int dq = cx.i - j0 - 4 * cx.g;   // element (kb, e) has i - j = dq - key_of(kb, e)
-        const int jb = j0 + 4 * cx.g;          // and key j = jb + key_of(kb, e)
-        const int kind = full ? 0 : (j0 >= cx.s ? 1 : 2);
-        tile_math<D, MODE, ALIBI, VF16>(ck, cv, lo, bo, qreg, oacc, m_run, l_run, cx.cs,
-                                        cx.slope_l2 * (float)(cx.i - j0), kind, dq, jb, cx.w, cx.s);
-    }
+                                          const f16x8_t (&qreg)[D / 16], f32x16_t (&s_cur)[2],
+                                          f32x16_t (&s_next)[2], f32x16_t (&oacc)[D / 32],
+                                          float &m_run, float &l_run, int t) {
+    const bool has1 = t + 1 < cx.n_tiles;
+    if (t + 2 < cx.n_tiles) load_k<D>(k_fill, cx, lo, cx.j0_of(t + 2));
+    const int j0 = cx.j0_of(t), j1 = cx.j0_of(t + 1);
+    if (has1) load_v<D, VF16>(v_fill, cx, lo, j1);
+    const int kind0 = cx.kind_of(j0);
+    const int kind1 = has1 ? cx.kind_of(j1) : -1;
+    const float bq0 = cx.slope_l2 * (float)(cx.i - j0);
+    if (kind1 >= 0) qk_tile<D, ALIBI>(k_next, lo, bo, qreg, s_next);
+    if (kind0 >= 0) weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run, cx.cs, bq0);
+    if (kind1 >= 0)
+        prep_scores<D, MODE, ALIBI>(s_next, oacc, m_run, l_run, cx.cs,
+                                    cx.slope_l2 * (float)(cx.i - j1), kind1,
+                                    cx.i - j1 - 4 * cx.g, j1 + 4 * cx.g, cx.w, cx.s);
 }
 
-// Register budget: 3 wavefronts per SIMD at d = 64 (4 fit), 2 at d = 128.
+// Register budget: 3 wavefronts per SIMD at d = 64 (2 with four heads per workgroup, which
+// keeps more per-head state), 2 at d = 128.
 template <int D, int GP, int MODE, bool ALIBI, bool VF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
+__global__ __launch_bounds__(64 * Tile<D>::NW)
+__attribute__((amdgpu_waves_per_eu(D == 64 && GP < 4 ? 3 : 2)))
 void prefill_mfma_kernel(MfmaParams p) {
     using T = Tile<D>;
-    constexpr int QP = 128 / GP;  // query positions per workgroup
-    constexpr int WPH = 4 / GP;   // wavefronts per query head
+    constexpr int QP = 32 * T::NW / GP;  // query positions per workgroup
+    constexpr int WPH = T::NW / GP;      // wavefronts per query head
     constexpr int KS = D / 16;    // k-steps of the score product
     constexpr int DB = D / 32;    // 32-row blocks of the output
     __shared__ __attribute__((aligned(16))) uint16_t lds[T::LDS_BYTES / 2];
+    uint16_t *const kbuf0 = lds, *const kbuf1 = lds + T::IMG;
+    uint16_t *const vbuf0 = lds + 2 * T::IMG, *const vbuf1 = lds + 3 * T::IMG;
 
     // ---- workgroup -> (batch, kv head, head group, query tile), XCD-contiguous
     const int nb = gridDim.x, bid = blockIdx.x;
@@ -434,6 +475,13 @@ void prefill_mfma_kernel(MfmaParams p) {
     const int qe = (q0 + QP < N ? q0 + QP : N) - 1;
     const bool rope = p.rope != nullptr;
 
+    // ---- band of key tiles: sink tiles the window no longer covers, then the window
+    const int lo_wg = q0 - p.w + 1 > 0 ? q0 - p.w + 1 : 0;
+    const int tw_begin = lo_wg / BK, tw_end = qe / BK;
+    const int n_sink_keys = p.s < lo_wg ? p.s : lo_wg;
+    int ts_end = (n_sink_keys + BK - 1) / BK;
+    if (ts_end > tw_begin) ts_end = tw_begin;
+
     TileCtx cx;
     {
         const int64_t kvoff = ((int64_t)b * p.N * p.Hkv + hkv) * D;
@@ -444,6 +492,8 @@ void prefill_mfma_kernel(MfmaParams p) {
         cx.row_bytes = p.row_bytes;
         cx.tid = tid; cx.wave = wave; cx.qa = qa; cx.qb = qa + 31 < N ? qa + 31 : N - 1;
         cx.i = i; cx.g = g; cx.w = p.w; cx.s = p.s; cx.N = N;
+        cx.n_tiles = ts_end + (tw_end - tw_begin + 1);
+        cx.ts_end = ts_end; cx.tw_begin = tw_begin;
         cx.cs = p.cs;
         cx.slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;  // bias in base-2 units
     }
@@ -489,14 +539,6 @@ void prefill_mfma_kernel(MfmaParams p) {
         }
     }
 
-    // ---- band of key tiles: sink tiles the window no longer covers, then the window
-    const int lo_wg = q0 - p.w + 1 > 0 ? q0 - p.w + 1 : 0;
-    const int tw_begin = lo_wg / BK, tw_end = qe / BK;
-    const int n_sink_keys = p.s < lo_wg ? p.s : lo_wg;
-    int ts_end = (n_sink_keys + BK - 1) / BK;
-    if (ts_end > tw_begin) ts_end = tw_begin;
-    const int n_tiles = ts_end + (tw_end - tw_begin + 1);
-
     f32x16_t oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -504,49 +546,72 @@ void prefill_mfma_kernel(MfmaParams p) {
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
     float m_run = -1e30f, l_run = 0.0f;
 
-    issue_loads<D, VF16>(lds, lds + T::IMG, cx, lo, (ts_end > 0 ? 0 : tw_begin) * BK);
+    // ---- prologue: K tiles 0 and 1, V tile 0; scores of tile 0
+    f32x16_t sa[2], sb[2];
+    load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
+    load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
+    if (cx.n_tiles > 1) load_k<D>(kbuf1, cx, lo, cx.j0_of(1));
+    __syncthreads();
+    {
+        const int j0 = cx.j0_of(0), kind0 = cx.kind_of(j0);
+        if (kind0 >= 0) {
+            qk_tile<D, ALIBI>(kbuf0, lo, bo, qreg, sa);
+            prep_scores<D, MODE, ALIBI>(sa, oacc, m_run, l_run, cx.cs,
+                                        cx.slope_l2 * (float)(i - j0), kind0, i - j0 - 4 * g,
+                                        j0 + 4 * g, cx.w, cx.s);
+        }
+    }
     __syncthreads();
 
-    for (int it = 0; it < n_tiles; ++it) {
-        const int j0 = (it < ts_end ? it : tw_begin + (it - ts_end)) * BK;
-        const bool next = it + 1 < n_tiles;
-        const int jn = (it + 1 < ts_end ? it + 1 : tw_begin + (it + 1 - ts_end)) * BK;
-        uint16_t *cur = lds + (it & 1) * 2 * T::IMG;
-        uint16_t *nxt = lds + ((it + 1) & 1) * 2 * T::IMG;
-        tile_step<D, MODE, ALIBI, VF16>(nxt, nxt + T::IMG, cur, cur + T::IMG, cx, lo, bo, qreg,
-                                        oacc, m_run, l_run, j0, jn, next);
+    // ---- tile t lives in K/V buffer t % 2; two steps per trip keep the score registers put
+    for (int t = 0; t < cx.n_tiles; t += 2) {
+        pipe_step<D, MODE, ALIBI, VF16>(kbuf0, vbuf1, kbuf1, vbuf0, cx, lo, bo, qreg, sa, sb, oacc,
+                                        m_run, l_run, t);
+        __syncthreads();
+        if (t + 1 >= cx.n_tiles) break;
+        pipe_step<D, MODE, ALIBI, VF16>(kbuf1, vbuf0, kbuf0, vbuf1, cx, lo, bo, qreg, sb, sa, oacc,
+                                        m_run, l_run, t + 1);
         __syncthreads();
     }
 
-    // ---- epilogue: normalise, stage O row-major in LDS, store whole rows
+    // ---- epilogue: normalise, stage O row-major in LDS (four wavefronts at a time), store
+    // whole rows
     const float l_tot = MODE == 1 ? l_run + __shfl_xor(l_run, 32, 64) : 1.0f;
     const float inv = MODE == 1 ? 1.0f / l_tot : 1.0f;
-    float *ol = reinterpret_cast<float *>(lds) + wave * (32 * T::OSTR);
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d0 = 32 * db + 8 * r + 4 * g;
-            *reinterpret_cast<float4 *>(ol + qc * T::OSTR + d0) =
-                make_float4(oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv,
-                            oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv);
-        }
-    __syncthreads();
+    float *ol = reinterpret_cast<float *>(lds) + (wave & 3) * (32 * T::OSTR);
     constexpr int C4 = D / 4;  // 4-float chunks per row
 #pragma unroll
-    for (int rr = 0; rr < 32 * C4 / 64; ++rr) {
-        const int ch = lane + 64 * rr;
-        const int qrow = ch / C4, c4 = ch % C4;
-        const int iq = qa + qrow;
-        if (iq < N) {
-            const float4 x = *reinterpret_cast<const float4 *>(ol + qrow * T::OSTR + 4 * c4);
-            const int64_t off = (((int64_t)b * p.N + iq) * p.Hq + h) * D + 4 * c4;
-            if (p.out_bf16)
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.o) + off) =
-                    make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
-            else
-                *reinterpret_cast<float4 *>(static_cast<float *>(p.o) + off) = x;
+    for (int round = 0; round < T::NW / 4; ++round) {
+        if ((wave >> 2) == round) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d0 = 32 * db + 8 * r + 4 * g;
+                    *reinterpret_cast<float4 *>(ol + qc * T::OSTR + d0) =
+                        make_float4(oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv,
+                                    oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv);
+                }
         }
+        __syncthreads();
+        if ((wave >> 2) == round) {
+#pragma unroll
+            for (int rr = 0; rr < 32 * C4 / 64; ++rr) {
+                const int ch = lane + 64 * rr;
+                const int qrow = ch / C4, c4 = ch % C4;
+                const int iq = qa + qrow;
+                if (iq < N) {
+                    const float4 x = *reinterpret_cast<const float4 *>(ol + qrow * T::OSTR + 4 * c4);
+                    const int64_t off = (((int64_t)b * p.N + iq) * p.Hq + h) * D + 4 * c4;
+                    if (p.out_bf16)
+                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.o) + off) =
+                            make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+                    else
+                        *reinterpret_cast<float4 *>(static_cast<float *>(p.o) + off) = x;
+                }
+            }
+        }
+        if (round + 1 < T::NW / 4) __syncthreads();
     }
 }
 
@@ -554,10 +619,10 @@ template <int D, int GP, int MODE, bool VF16>
 hipError_t launch_main(const MfmaParams &mp, int nblocks, bool alibi, hipStream_t st) {
     if (alibi)
         hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, true, VF16>), dim3((unsigned)nblocks),
-                           dim3(256), 0, st, mp);
+                           dim3(64 * Tile<D>::NW), 0, st, mp);
     else
         hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, false, VF16>), dim3((unsigned)nblocks),
-                           dim3(256), 0, st, mp);
+                           dim3(64 * Tile<D>::NW), 0, st, mp);
     return hipGetLastError();
 }
 
@@ -603,7 +668,8 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
     if (a.B * a.N == 0) return true;
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
-    const int64_t nb = a.B * a.Hkv * (G / GP) * ((a.N + 128 / GP - 1) / (128 / GP));
+    const int64_t QP = 32 * (a.d == 128 ? Tile<128>::NW : Tile<64>::NW) / GP;
+    const int64_t nb = a.B * a.Hkv * (G / GP) * ((a.N + QP - 1) / QP);
     const int64_t n_kt = (a.N + BK - 1) / BK;
     // 32-bit block ids and buffer offsets: one K/V slice, one slice of tile images and the
     // table stay below 2 GiB
@@ -626,7 +692,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     const Plan pl = plan_of(a);
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
-    const int64_t QP = 128 / GP;
+    const int64_t QP = 32 * (a.d == 128 ? Tile<128>::NW : Tile<64>::NW) / GP;
     MfmaParams mp;
     mp.q = static_cast<const uint16_t *>(q);
     mp.k = static_cast<const uint16_t *>(k);
