@@ -58,6 +58,7 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 template <int D>
 struct Tile {
     static constexpr int NW = 4;                         // wavefronts per workgroup
+    static constexpr bool PIPE = D == 128;               // software-pipelined tile loop
     static constexpr int C = D / 8;                      // 16-byte chunks per row
     static constexpr int IMG = BK * D;                   // 16-bit elements of a K or V tile
     static constexpr int IMG_BYTES = IMG * 2;
@@ -438,11 +439,38 @@ __device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
                                     cx.i - j1 - 4 * cx.g, j1 + 4 * cx.g, cx.w, cx.s);
 }
 
-// Register budget: 3 wavefronts per SIMD at d = 64 (2 with four heads per workgroup, which
+// Step t without pipelining: start the transfers of tile t + 1 (K and V) into the other
+// buffer pair, then form, prepare and weigh tile t. Fewer live registers than pipe_step.
+template <int D, int MODE, bool ALIBI, bool VF16>
+__device__ __forceinline__ void plain_step(uint16_t *__restrict__ k_fill,
+                                           uint16_t *__restrict__ v_fill,
+                                           const uint16_t *__restrict__ k_cur,
+                                           const uint16_t *__restrict__ v_cur, const TileCtx &cx,
+                                           const LaneOffsets<D> &lo, const BiasOperands &bo,
+                                           const f16x8_t (&qreg)[D / 16], f32x16_t (&oacc)[D / 32],
+                                           float &m_run, float &l_run, int t) {
+    if (t + 1 < cx.n_tiles) {
+        const int j1 = cx.j0_of(t + 1);
+        load_k<D>(k_fill, cx, lo, j1);
+        load_v<D, VF16>(v_fill, cx, lo, j1);
+    }
+    const int j0 = cx.j0_of(t);
+    const int kind = cx.kind_of(j0);
+    if (kind >= 0) {
+        f32x16_t sacc[2];
+        const float bq = cx.slope_l2 * (float)(cx.i - j0);
+        qk_tile<D, ALIBI>(k_cur, lo, bo, qreg, sacc);
+        prep_scores<D, MODE, ALIBI>(sacc, oacc, m_run, l_run, cx.cs, bq, kind,
+                                    cx.i - j0 - 4 * cx.g, j0 + 4 * cx.g, cx.w, cx.s);
+        weigh_pv<D, MODE, VF16>(v_cur, lo, sacc, oacc, m_run, l_run, cx.cs, bq);
+    }
+}
+
+// Register budget: 4 wavefronts per SIMD at d = 64 (3 with four heads per workgroup, which
 // keeps more per-head state), 2 at d = 128.
 template <int D, int GP, int MODE, bool ALIBI, bool VF16>
 __global__ __launch_bounds__(64 * Tile<D>::NW)
-__attribute__((amdgpu_waves_per_eu(D == 64 && GP < 4 ? 3 : 2)))
+__attribute__((amdgpu_waves_per_eu(D == 64 ? (GP < 4 ? 4 : 3) : 2)))
 void prefill_mfma_kernel(MfmaParams p) {
     using T = Tile<D>;
     constexpr int QP = 32 * T::NW / GP;  // query positions per workgroup
@@ -546,32 +574,47 @@ void prefill_mfma_kernel(MfmaParams p) {
         for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
     float m_run = -1e30f, l_run = 0.0f;
 
-    // ---- prologue: K tiles 0 and 1, V tile 0; scores of tile 0
-    f32x16_t sa[2], sb[2];
-    load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
-    load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
-    if (cx.n_tiles > 1) load_k<D>(kbuf1, cx, lo, cx.j0_of(1));
-    __syncthreads();
-    {
-        const int j0 = cx.j0_of(0), kind0 = cx.kind_of(j0);
-        if (kind0 >= 0) {
-            qk_tile<D, ALIBI>(kbuf0, lo, bo, qreg, sa);
-            prep_scores<D, MODE, ALIBI>(sa, oacc, m_run, l_run, cx.cs,
-                                        cx.slope_l2 * (float)(i - j0), kind0, i - j0 - 4 * g,
-                                        j0 + 4 * g, cx.w, cx.s);
+    if constexpr (T::PIPE) {
+        // ---- prologue: K tiles 0 and 1, V tile 0; scores of tile 0
+        f32x16_t sa[2], sb[2];
+        load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
+        load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
+        if (cx.n_tiles > 1) load_k<D>(kbuf1, cx, lo, cx.j0_of(1));
+        __syncthreads();
+        {
+            const int j0 = cx.j0_of(0), kind0 = cx.kind_of(j0);
+            if (kind0 >= 0) {
+                qk_tile<D, ALIBI>(kbuf0, lo, bo, qreg, sa);
+                prep_scores<D, MODE, ALIBI>(sa, oacc, m_run, l_run, cx.cs,
+                                            cx.slope_l2 * (float)(i - j0), kind0, i - j0 - 4 * g,
+                                            j0 + 4 * g, cx.w, cx.s);
+            }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- tile t lives in K/V buffer t % 2; two steps per trip keep the score registers put
-    for (int t = 0; t < cx.n_tiles; t += 2) {
-        pipe_step<D, MODE, ALIBI, VF16>(kbuf0, vbuf1, kbuf1, vbuf0, cx, lo, bo, qreg, sa, sb, oacc,
-                                        m_run, l_run, t);
+        // ---- tile t lives in K/V buffer t % 2; two steps per trip keep the score registers
+        for (int t = 0; t < cx.n_tiles; t += 2) {
+            pipe_step<D, MODE, ALIBI, VF16>(kbuf0, vbuf1, kbuf1, vbuf0, cx, lo, bo, qreg, sa, sb,
+                                            oacc, m_run, l_run, t);
+            __syncthreads();
+            if (t + 1 >= cx.n_tiles) break;
+            pipe_step<D, MODE, ALIBI, VF16>(kbuf1, vbuf0, kbuf0, vbuf1, cx, lo, bo, qreg, sb, sa,
+                                            oacc, m_run, l_run, t + 1);
+            __syncthreads();
+        }
+    } else {
+        load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
+        load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
         __syncthreads();
-        if (t + 1 >= cx.n_tiles) break;
-        pipe_step<D, MODE, ALIBI, VF16>(kbuf1, vbuf0, kbuf0, vbuf1, cx, lo, bo, qreg, sb, sa, oacc,
-                                        m_run, l_run, t + 1);
-        __syncthreads();
+        for (int t = 0; t < cx.n_tiles; t += 2) {
+            plain_step<D, MODE, ALIBI, VF16>(kbuf1, vbuf1, kbuf0, vbuf0, cx, lo, bo, qreg, oacc,
+                                             m_run, l_run, t);
+            __syncthreads();
+            if (t + 1 >= cx.n_tiles) break;
+            plain_step<D, MODE, ALIBI, VF16>(kbuf0, vbuf0, kbuf1, vbuf1, cx, lo, bo, qreg, oacc,
+                                             m_run, l_run, t + 1);
+            __syncthreads();
+        }
     }
 
     // ---- epilogue: normalise, stage O row-major in LDS (four wavefronts at a time), store
