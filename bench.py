@@ -202,7 +202,7 @@ def main():
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-batches", type=int, default=1)
+    ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes three times (the "
                          "known-size kernel that scales the HBM byte counters), then exit")
