@@ -10,7 +10,9 @@ The JSON line also carries:
   roofline      the prefill kernel against the bf16 matrix-core peak, with its average
                 launch duration timed by HIP events on the launch stream;
   decode        the SWA(64, 4) decode workload (64 sequences, 256 steps of ring append +
-                decode) in tokens/s and algorithmic GB/s against HBM peak;
+                decode) in tokens/s and algorithmic GB/s against HBM peak, with the cache
+                resident in the last-level cache (as specified) and, as decode_cold, with 18
+                cache copies in rotation so that the rings come from HBM;
   cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -107,18 +109,21 @@ def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
     return wall, kernel_ms
 
 
-def bench_decode(cfg, out_dtype):
+def bench_decode(cfg, out_dtype, copies=1):
     """256 steps of ring append + decode over 64 sequences (one fused launch per step),
     captured once in a HIP graph so the launches replay without host overhead; timed over
-    the whole replay."""
+    the whole replay. With copies > 1, step t works on cache copy t % copies, so that the
+    copies together outgrow the 256 MB last-level cache and each step reads its ring from
+    HBM (the step's work is the same: every sequence is past w + s tokens)."""
     import torch
     import sliding_window_attention_prefill_amd as swa
     import swa_workloads as wl
 
     st = wl.decode_inputs(cfg, device="cuda")
     T, S = cfg.steps, cfg.num_seqs
-    cache = swa.SwaCache(st.k_ring.clone(), st.v_ring.clone(), st.k_sink.clone(),
-                         st.v_sink.clone())
+    caches = [swa.SwaCache(st.k_ring.clone(), st.v_ring.clone(), st.k_sink.clone(),
+                           st.v_sink.clone()) for _ in range(copies)]
+    cache = caches[0]
     table = swa.swa_rope_table(cfg.len_hi + T + 1, cfg.d, cfg.rope_theta)
     pos = torch.stack([(st.lengths + t).to(torch.int32) for t in range(T)]).contiguous()
     out = torch.empty((T, S, cfg.H_q, cfg.d), dtype=out_dtype, device="cuda")
@@ -132,9 +137,9 @@ def bench_decode(cfg, out_dtype):
     def run_all():
         # one launch per step: append the step's token and answer its query
         for t in range(T):
-            swa.swa_decode_append(st.q_steps[t], k_steps[t], v_steps[t], pos[t], cache,
-                                  mode=cfg.mode, rope_table=table, out=out[t], workspace=ws,
-                                  stream=stream)
+            swa.swa_decode_append(st.q_steps[t], k_steps[t], v_steps[t], pos[t],
+                                  caches[t % copies], mode=cfg.mode, rope_table=table,
+                                  out=out[t], workspace=ws, stream=stream)
 
     with torch.cuda.stream(stream):
         run_all()                     # warm-up, eager
@@ -155,6 +160,8 @@ def bench_decode(cfg, out_dtype):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     el = 2
+    cache_bytes = sum(t.numel() * t.element_size() for t in
+                      (cache.k_ring, cache.v_ring, cache.k_sink, cache.v_sink) if t is not None)
     ob = 4 if out_dtype == torch.float32 else 2
     n_keys = cfg.w + cfg.s  # every sequence is past w + s tokens
     per_step = (S * cfg.H_kv * n_keys * cfg.d * el * 2      # ring + sink K and V read
@@ -169,7 +176,10 @@ def bench_decode(cfg, out_dtype):
         "tok_per_s": round(S * T / secs, 1),
         "algorithmic_bytes_per_step": per_step,
         "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-        "note": "cache stays resident in the 256 MB last-level cache across steps",
+        "cache_copies": copies,
+        "note": ("cache stays resident in the 256 MB last-level cache across steps" if copies == 1
+                 else "%d cache copies (%.0f MB) in rotation: rings are read from HBM"
+                 % (copies, copies * cache_bytes / 1e6)),
     }
 
 
@@ -248,6 +258,7 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = bench_decode(wl.C4, torch.float32)
+        result["decode_cold"] = bench_decode(wl.C4, torch.float32, copies=18)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_batches)
     print(json.dumps(result), flush=True)
