@@ -217,8 +217,15 @@ __global__ __launch_bounds__(256) void decode_general_kernel(DecodeGen a, const 
 // With APPEND the block first writes the new token (rotated key, value) to its ring slot
 // and sink entry, keeps it in LDS and uses that copy for position q_pos, so the slot it
 // wrote is never read back within the launch.
+// Split-KV: with nsplit > 1 the key list of a query is cut into nsplit contiguous, chunk-
+// aligned ranges, one block each; a block writes its unnormalised partial output with its
+// running maximum and sum to the workspace, and decode_combine_kernel merges the partials
+// (log-sum-exp rescaling for softmax, a plain sum for sigmoid). Only the block whose range
+// holds the query's own position appends the new token.
 struct DecodeFast {
     int S, Hq, Hkv, G, w, s, mode;
+    int nsplit;          // key ranges per (sequence, kv head); 1 = no split
+    float *part;         // workspace: [S, Hkv, nsplit, G] x (D outputs, max, sum), or null
     float cs;            // scale * log2(e): scores are kept in base-2 units
     const float *slopes;
     const float *rope;
@@ -260,21 +267,31 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
     float *ml = vn + D;                 // [3][8] max, sum, correction per head
     float *red = ml + 24;               // [KG][G][D] partial outputs
 
-    const int sq = blockIdx.x / a.Hkv, hk = blockIdx.x % a.Hkv;
+    const int split = blockIdx.x % a.nsplit, bsh = blockIdx.x / a.nsplit;
+    const int sq = bsh / a.Hkv, hk = bsh % a.Hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = q_pos[sq];
     const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
     if (!valid) {
-        for (int idx = tid; idx < G * D; idx += 256)
-            Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G) * D + idx, qnan());
+        // the combine kernel flags split outputs itself
+        if (a.nsplit == 1)
+            for (int idx = tid; idx < G * D; idx += 256)
+                Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G) * D + idx, qnan());
         return;
     }
+    // this block's range of the query's key list (sinks first, then the window)
+    const int lo_w = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
+    const int n_all = (a.s < lo_w ? a.s : lo_w) + (p - lo_w + 1);
+    const int per = ((n_all + a.nsplit - 1) / a.nsplit + DEC_KC - 1) / DEC_KC * DEC_KC;
+    const int k_begin = split * per < n_all ? split * per : n_all;
+    const int k_end = k_begin + per < n_all ? k_begin + per : n_all;
+    const bool owns_new = k_begin <= n_all - 1 && n_all - 1 < k_end;   // the query's own key
     const int64_t ring_base = ((int64_t)sq * a.Hkv + hk) * a.w * D;
     const int64_t sink_base = ((int64_t)sq * a.Hkv + hk) * a.s * D;
     const int half = D / 2;
 
     // ---- the new token (fused append) and the queries, rotated at position p
-    if (APPEND && tid < half) {
+    if (APPEND && owns_new && tid < half) {
         const int64_t src = ((int64_t)sq * a.Hkv + hk) * D + 2 * tid;
         float k0 = bf16_bits_to_f32(k_new[src]), k1 = bf16_bits_to_f32(k_new[src + 1]);
         const uint32_t vv = *reinterpret_cast<const uint32_t *>(v_new + src);
@@ -314,9 +331,9 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
         ml[8 + tid] = 0.0f;
         ml[16 + tid] = 1.0f;
     }
-    const int lo = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
+    const int lo = lo_w;
     const int n_sink = a.s < lo ? a.s : lo;
-    const int n_keys = n_sink + (p - lo + 1);
+    const int n_keys = k_end;
 
     // value-pass ownership: 8 columns, keys kg, kg + KG, ...
     const int c8 = tid % L::C8, kg = tid / L::C8;
@@ -327,7 +344,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
         for (int c = 0; c < 8; ++c) acc[g][c] = 0.0f;
     __syncthreads();
 
-    for (int c0 = 0; c0 < n_keys; c0 += DEC_KC) {
+    for (int c0 = k_begin; c0 < n_keys; c0 += DEC_KC) {
         const int nk = n_keys - c0 < DEC_KC ? n_keys - c0 : DEC_KC;
         // -- issue every load of the chunk: two score slots and VK value rows per thread
         uint4 kx[2][L::QE / 8];
@@ -462,12 +479,56 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
 #pragma unroll
         for (int c = 0; c < 8; ++c) red[(kg * G + g) * D + 8 * c8 + c] = acc[g][c];
     __syncthreads();
+    float *pp = a.nsplit > 1 ? a.part + (((int64_t)bsh * a.nsplit + split) * G) * (D + 2) : nullptr;
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, col = idx % D;
         float sum = 0.0f;
         for (int r = 0; r < L::KG; ++r) sum += red[(r * G + g) * D + col];
-        if (a.mode == 1) sum /= ml[8 + g];
-        Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + g) * D + col, sum);
+        if (a.nsplit > 1) {
+            pp[g * (D + 2) + col] = sum;
+        } else {
+            if (a.mode == 1) sum /= ml[8 + g];
+            Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + g) * D + col, sum);
+        }
+    }
+    if (a.nsplit > 1 && tid < G) {
+        pp[tid * (D + 2) + D] = ml[tid];          // running maximum (base 2), -inf if empty
+        pp[tid * (D + 2) + D + 1] = ml[8 + tid];  // running sum
+    }
+}
+
+// Merge of the split partials of decode_fast_kernel: one block per (sequence, kv head).
+// softmax: o = sum_k acc_k 2^(m_k - M) / sum_k l_k 2^(m_k - M) with M the largest m_k;
+// sigmoid: o = sum_k acc_k. A query whose position cannot be served gets NaN.
+template <int D, int G, int OUT>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFast a,
+                                                             const int32_t *__restrict__ q_pos,
+                                                             void *__restrict__ o) {
+    const int bsh = blockIdx.x, sq = bsh / a.Hkv, hk = bsh % a.Hkv;
+    const int p = q_pos[sq];
+    const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
+    const float *pp = a.part + (int64_t)bsh * a.nsplit * G * (D + 2);
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+        const int g = idx / D, col = idx % D;
+        float out;
+        if (!valid) {
+            out = qnan();
+        } else if (a.mode == 0) {
+            out = 0.0f;
+            for (int k = 0; k < a.nsplit; ++k) out += pp[(k * G + g) * (D + 2) + col];
+        } else {
+            float M = -INFINITY;
+            for (int k = 0; k < a.nsplit; ++k) M = fmaxf(M, pp[(k * G + g) * (D + 2) + D]);
+            float num = 0.0f, den = 0.0f;
+            for (int k = 0; k < a.nsplit; ++k) {
+                const float *e = pp + (k * G + g) * (D + 2);
+                const float f = __builtin_amdgcn_exp2f(e[D] - M);  // empty range: 2^-inf = 0
+                num = fmaf(e[col], f, num);
+                den = fmaf(e[D + 1], f, den);
+            }
+            out = num / den;
+        }
+        Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + g) * D + col, out);
     }
 }
 
@@ -701,9 +762,15 @@ hipError_t launch_fast_t(const DecodeFast &f, const void *q, const int32_t *q_po
         return hipGetLastError();
     }
     const size_t lds = decode_fast_lds<D>(G);
-    hipLaunchKernelGGL((decode_fast_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv)),
+    hipLaunchKernelGGL((decode_fast_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv * f.nsplit)),
                        dim3(256), lds, st, f, static_cast<const uint16_t *>(q), q_pos, o,
                        static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
+    if (f.nsplit > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((decode_combine_kernel<D, G, OUT>), dim3((unsigned)(f.S * f.Hkv)),
+                           dim3(256), 0, st, f, q_pos, o);
+    }
     return hipGetLastError();
 }
 
@@ -731,17 +798,32 @@ hipError_t launch_fast_d(const DecodeFast &f, int out_dt, const void *q, const i
 bool decode_fast_ok(const DecodeArgs &a, const CacheArgs &c) {
     const int64_t G = a.Hq / c.Hkv;
     if (c.dt != 1 || (c.d != 64 && c.d != 128) || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
-    if (c.S * c.Hkv > 0x7fffffff || c.w > (1 << 30) || c.s > (1 << 30)) return false;
+    if (c.S * c.Hkv * 64 > 0x7fffffff || c.w > (1 << 30) || c.s > (1 << 30)) return false;
     const size_t lds = c.d == 64 ? decode_fast_lds<64>((int)G) : decode_fast_lds<128>((int)G);
     return lds <= 64 * 1024;
 }
 
+// Key ranges per (sequence, kv head) for the chunked decode: about two blocks per CU in
+// total, and at least 512 keys per range.
+int64_t decode_nsplit(const CacheArgs &c) {
+    if (c.w + c.s <= 128) return 1;            // whole-window kernel
+    const int64_t bh = c.S * c.Hkv;
+    if (bh <= 0) return 1;
+    int64_t ns = (512 + bh - 1) / bh;
+    const int64_t by_keys = (c.w + c.s) / 512;
+    if (ns > by_keys) ns = by_keys;
+    if (ns > 64) ns = 64;
+    return ns < 1 ? 1 : ns;
+}
+
 hipError_t launch_decode_fast(const DecodeArgs &a, const CacheArgs &c, const void *q,
                               const int32_t *q_pos, void *o, const void *k_new, const void *v_new,
-                              hipStream_t st) {
+                              void *ws, hipStream_t st) {
     DecodeFast f;
     f.S = (int)c.S; f.Hq = (int)a.Hq; f.Hkv = (int)c.Hkv; f.G = (int)(a.Hq / c.Hkv);
     f.w = (int)c.w; f.s = (int)c.s; f.mode = a.mode;
+    f.nsplit = (int)decode_nsplit(c);
+    f.part = static_cast<float *>(ws);
     f.cs = a.scale * 1.4426950408889634f;
     f.slopes = a.slopes; f.rope = a.rope; f.rope_rows = a.rope_rows;
     f.k_ring = static_cast<uint16_t *>(c.k_ring); f.v_ring = static_cast<uint16_t *>(c.v_ring);
@@ -771,12 +853,17 @@ hipError_t launch_kv_append(const CacheArgs &c, const void *k_new, const void *v
     return hipGetLastError();
 }
 
-size_t decode_workspace_bytes(const DecodeArgs &, const CacheArgs &) { return 0; }
+size_t decode_workspace_bytes(const DecodeArgs &a, const CacheArgs &c) {
+    if (c.S == 0 || !decode_fast_ok(a, c)) return 0;
+    const int64_t ns = decode_nsplit(c);
+    if (ns <= 1) return 0;
+    return sizeof(float) * (size_t)(c.S * c.Hkv * ns * (a.Hq / c.Hkv) * (c.d + 2));
+}
 
 hipError_t launch_decode(const DecodeArgs &a, const CacheArgs &c, const void *q,
-                         const int32_t *q_pos, void *o, void *, size_t, hipStream_t st) {
+                         const int32_t *q_pos, void *o, void *ws, size_t, hipStream_t st) {
     if (c.S == 0) return hipSuccess;
-    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, nullptr, nullptr, st);
+    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, nullptr, nullptr, ws, st);
     const int64_t G = a.Hq / c.Hkv;
     int KC = 64;
     while (KC > 8 && decode_general_lds(G, c.d, KC) > 64 * 1024) KC /= 2;
@@ -800,7 +887,7 @@ hipError_t launch_decode_append(const DecodeArgs &a, const CacheArgs &c, const v
                                 const void *k_new, const void *v_new, const int32_t *q_pos,
                                 void *o, void *ws, size_t ws_bytes, hipStream_t st) {
     if (c.S == 0) return hipSuccess;
-    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, k_new, v_new, st);
+    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, k_new, v_new, ws, st);
     // general shapes: the append kernel, then the decode kernel, in stream order
     const hipError_t e = launch_kv_append(c, k_new, v_new, q_pos, 1, a.rope, a.rope_rows, st);
     if (e != hipSuccess) return e;

@@ -146,3 +146,19 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(swa, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         swa.load()
+
+
+def test_decode_workspace_bytes_split_kv(lib):
+    """Long windows with few (sequence, kv head) pairs are split over several blocks; the
+    workspace holds one partial output (d values, maximum, sum) per head and range."""
+    def wsb(S, H_kv, w, s, d, Hq, mode=1):
+        c = _cache(num_seqs=S, H_kv=H_kv, w=w, s=s, d=d)
+        p = swa.DecodeParams(Hq, mode, 0, 0.0, 0, None, None, 0)
+        return lib.swa_decode_workspace_bytes(ctypes.byref(p), ctypes.byref(c))
+    # whole-window kernel (w + s <= 128) and plenty of blocks: no workspace
+    assert wsb(64, 8, 64, 4, 128, 32) == 0
+    assert wsb(64, 8, 1024, 0, 128, 32) == 0          # 512 blocks already
+    # 1 sequence x 8 kv heads, 4096 keys: min(ceil(512 / 8), 4096 / 512) = 8 ranges
+    assert wsb(1, 8, 4096, 0, 128, 32) == 4 * 1 * 8 * 8 * 4 * (128 + 2)
+    # at most 64 ranges
+    assert wsb(1, 1, 1 << 20, 0, 64, 2) == 4 * 1 * 1 * 64 * 2 * (64 + 2)

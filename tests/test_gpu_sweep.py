@@ -122,3 +122,57 @@ def test_fused_decode_random_shapes(case):
         ref = ring.decode(qn, pos, H_q=Hq, mode=mode, slopes=slopes, rope_theta=theta)
         torch.cuda.synchronize()
         assert_parity(out, ref, "bf16", "decode sweep case %d step %d" % (idx, step))
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,w,s,mode", [
+    (1, 8, 2, 128, 3000, 0, wl.SOFTMAX), (2, 4, 4, 64, 2500, 4, wl.SIGMOID),
+    (1, 32, 8, 128, 4096, 0, wl.SOFTMAX), (3, 2, 1, 64, 1100, 7, wl.SOFTMAX),
+    (1, 8, 2, 128, 5000, 0, wl.SIGMOID), (2, 8, 8, 128, 1400, 3, wl.SOFTMAX)])
+@pytest.mark.parametrize("fused", [False, True], ids=["decode", "fused"])
+def test_split_kv_decode_long_windows(S, Hq, Hkv, d, w, s, mode, fused):
+    """Long windows with few sequences run split over several blocks per (sequence, kv
+    head) and merged by the combine kernel; outputs match the oracle ring at positions
+    inside the first window and after it has wrapped."""
+    g = torch.Generator().manual_seed(S * 7 + w)
+    cache = swa.SwaCache.empty(S, Hkv, w, s, d, torch.bfloat16)
+    ring = oracle.Ring(S, Hkv, w, s, d)
+    # history: sequence q_ has start[q_] tokens (some shorter than w, some past it)
+    start = torch.tensor([(w // 3) if q_ % 2 == 0 else (w + 57 + 31 * q_) for q_ in range(S)])
+    theta = 1e4
+    steps = 3
+    table = swa.swa_rope_table(int(start.max()) + steps + 1, d, theta)
+    for q_ in range(S):
+        n0 = int(start[q_])
+        pos_all = torch.full((S,), -1, dtype=torch.int32)
+        pos_all[q_] = 0
+        kh = torch.randn((S, n0, Hkv, d), generator=g).to(torch.bfloat16)
+        vh = torch.randn((S, n0, Hkv, d), generator=g).to(torch.bfloat16)
+        swa.swa_kv_append(cache, kh.to(DEV), vh.to(DEV), pos_all.to(DEV), rope_table=table)
+        ring.append(kh, vh, pos_all, rope_theta=theta)
+    need = swa.swa_decode_workspace_bytes(cache, Hq, mode=mode, out_dtype=torch.float32)
+    assert need > 0  # these shapes take the split path
+    slopes = tuple(np.linspace(-0.3, 0.3, Hq).tolist())
+    sl = torch.tensor(slopes, dtype=torch.float32, device=DEV)
+    for step in range(steps):
+        pos = (start + step).to(torch.int32)
+        kn = torch.randn((S, Hkv, d), generator=g).to(torch.bfloat16)
+        vn = torch.randn((S, Hkv, d), generator=g).to(torch.bfloat16)
+        qn = torch.randn((S, Hq, d), generator=g).to(torch.bfloat16)
+        if fused:
+            out = swa.swa_decode_append(qn.to(DEV), kn.to(DEV), vn.to(DEV), pos.to(DEV), cache,
+                                        mode=mode, alibi_slopes=sl, rope_table=table,
+                                        out_dtype=torch.float32)
+        else:
+            swa.swa_kv_append(cache, kn[:, None].to(DEV), vn[:, None].to(DEV), pos.to(DEV),
+                              rope_table=table)
+            out = swa.swa_decode(qn.to(DEV), pos.to(DEV), cache, mode=mode, alibi_slopes=sl,
+                                 rope_table=table, out_dtype=torch.float32)
+        ring.append(kn[:, None], vn[:, None], pos, rope_theta=theta)
+        ref = ring.decode(qn, pos, H_q=Hq, mode=mode, slopes=slopes, rope_theta=theta)
+        torch.cuda.synchronize()
+        assert_parity(out, ref, "bf16", "split decode step %d" % step)
+    # an invalid position gives NaN rows on the split path too
+    bad = torch.full((S,), -3, dtype=torch.int32, device=DEV)
+    qn = torch.randn((S, Hq, d), generator=g).to(torch.bfloat16).to(DEV)
+    out = swa.swa_decode(qn, bad, cache, mode=mode, rope_table=table, out_dtype=torch.float32)
+    assert torch.isnan(out).all()
