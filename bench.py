@@ -12,7 +12,8 @@ The JSON line also carries:
   decode        the SWA(64, 4) decode workload (64 sequences, 256 steps of ring append +
                 decode) in tokens/s and algorithmic GB/s against HBM peak, with the cache
                 resident in the last-level cache (as specified) and, as decode_cold, with 18
-                cache copies in rotation so that the rings come from HBM;
+                cache copies in rotation so that the rings come from HBM; decode_long adds
+                two long-window decode workloads whose caches live in HBM;
   cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -121,8 +122,9 @@ def bench_decode(cfg, out_dtype, copies=1):
 
     st = wl.decode_inputs(cfg, device="cuda")
     T, S = cfg.steps, cfg.num_seqs
-    caches = [swa.SwaCache(st.k_ring.clone(), st.v_ring.clone(), st.k_sink.clone(),
-                           st.v_sink.clone()) for _ in range(copies)]
+    clone = lambda t: None if t is None else t.clone()
+    caches = [swa.SwaCache(clone(st.k_ring), clone(st.v_ring), clone(st.k_sink),
+                           clone(st.v_sink)) for _ in range(copies)]
     cache = caches[0]
     table = swa.swa_rope_table(cfg.len_hi + T + 1, cfg.d, cfg.rope_theta)
     pos = torch.stack([(st.lengths + t).to(torch.int32) for t in range(T)]).contiguous()
@@ -177,9 +179,11 @@ def bench_decode(cfg, out_dtype, copies=1):
         "algorithmic_bytes_per_step": per_step,
         "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "cache_copies": copies,
-        "note": ("cache stays resident in the 256 MB last-level cache across steps" if copies == 1
-                 else "%d cache copies (%.0f MB) in rotation: rings are read from HBM"
-                 % (copies, copies * cache_bytes / 1e6)),
+        "cache_mb": round(copies * cache_bytes / 1e6, 1),
+        "note": ("cache (%.0f MB) %s the 256 MB last-level cache" % (
+                     cache_bytes / 1e6, "fits in" if cache_bytes < 200e6 else "outgrows")
+                 if copies == 1 else "%d cache copies in rotation: rings are read from HBM"
+                 % copies),
     }
 
 
@@ -259,6 +263,8 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(wl.C4, torch.float32)
         result["decode_cold"] = bench_decode(wl.C4, torch.float32, copies=18)
+        result["decode_long"] = [bench_decode(c, torch.float32)
+                                 for c in (wl.DECODE_W4096, wl.DECODE_W32K)]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_batches)
     print(json.dumps(result), flush=True)

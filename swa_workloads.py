@@ -102,6 +102,18 @@ C5 = PrefillConfig("gemma3_local_bf16_Hq16_Hkv8_N131072_d128_w1024", "bf16", B=1
                    N=131072, d=128, w=1024, s=0, mode=SIGMOID, rope_theta=1e4,
                    slopes=tuple(balanced_alibi_slopes(16)), heavy_k_frac=0.01, seed=5)
 
+# Decode at long windows (measurement only): the C3 layer shape with its 4,096-token window
+# over 64 sequences, and a global-attention-style 32K window over 8 sequences, which runs
+# split over several blocks per (sequence, kv head). Both caches outgrow the last-level cache.
+DECODE_W4096 = DecodeConfig("mistral7b_window_decode_bf16_S64_Hq32_Hkv8_d128_w4096", "bf16",
+                            num_seqs=64, H_q=32, H_kv=8, d=128, w=4096, s=0, mode=SOFTMAX,
+                            rope_theta=1e6, slopes=None, len_lo=8192, len_hi=32768, steps=32,
+                            seed=6)
+DECODE_W32K = DecodeConfig("global_window_decode_bf16_S8_Hq32_Hkv8_d128_w32768", "bf16",
+                           num_seqs=8, H_q=32, H_kv=8, d=128, w=32768, s=0, mode=SOFTMAX,
+                           rope_theta=1e6, slopes=None, len_lo=40000, len_hi=60000, steps=32,
+                           seed=7)
+
 PREFILL_CONFIGS = {c.name: c for c in (C1, C2, C3, C5)}
 
 
