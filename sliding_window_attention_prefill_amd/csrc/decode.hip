@@ -252,6 +252,13 @@ size_t decode_fast_lds(int G) {
 
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// Block barrier that orders LDS accesses only: global loads in flight stay in flight.
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int D, int G, int OUT, bool APPEND>
 __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const uint16_t *__restrict__ q,
                                                           const int32_t *__restrict__ q_pos,
@@ -344,15 +351,19 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
         for (int c = 0; c < 8; ++c) acc[g][c] = 0.0f;
     __syncthreads();
 
-    for (int c0 = k_begin; c0 < n_keys; c0 += DEC_KC) {
-        const int nk = n_keys - c0 < DEC_KC ? n_keys - c0 : DEC_KC;
-        // -- issue every load of the chunk: two score slots and VK value rows per thread
-        uint4 kx[2][L::QE / 8];
-        int kpos[2];
+    // K rows of the next chunk are requested as soon as this chunk's scores are formed, V rows
+    // as soon as its values are added; the block barriers inside a chunk order LDS only, so
+    // those loads stay in flight across them.
+    uint4 kx[2][L::QE / 8];
+    int kpos[2];
+    uint4 vx[L::VK];
+    int vpos[L::VK];
+    auto load_k = [&](int cc) {
+        const int nk = n_keys - cc < DEC_KC ? n_keys - cc : DEC_KC;
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int slot = tid + 256 * r, e = slot / 4, qq = slot % 4;
-            const int ee = c0 + e;
+            const int ee = cc + e;
             const int P = ee < n_sink ? ee : lo + (ee - n_sink);
             kpos[r] = P;
             const bool from_mem = e < nk && !(APPEND && P == p);
@@ -362,11 +373,12 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
             for (int u = 0; u < L::QE / 8; ++u)
                 kx[r][u] = from_mem ? ld16(row + qq * L::QE + 8 * u) : make_uint4(0, 0, 0, 0);
         }
-        uint4 vx[L::VK];
-        int vpos[L::VK];
+    };
+    auto load_v = [&](int cc) {
+        const int nk = n_keys - cc < DEC_KC ? n_keys - cc : DEC_KC;
 #pragma unroll
         for (int r = 0; r < L::VK; ++r) {
-            const int e = kg + L::KG * r, ee = c0 + e;
+            const int e = kg + L::KG * r, ee = cc + e;
             const int P = ee < n_sink ? ee : lo + (ee - n_sink);
             vpos[r] = P;
             const bool from_mem = e < nk && !(APPEND && P == p);
@@ -374,6 +386,14 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
                                               : a.v_ring + ring_base + (int64_t)(P % a.w) * D;
             vx[r] = from_mem ? ld16(row + 8 * c8) : make_uint4(0, 0, 0, 0);
         }
+    };
+    if (k_begin < n_keys) {
+        load_k(k_begin);
+        load_v(k_begin);
+    }
+    for (int c0 = k_begin; c0 < n_keys; c0 += DEC_KC) {
+        const int nk = n_keys - c0 < DEC_KC ? n_keys - c0 : DEC_KC;
+        const bool more = c0 + DEC_KC < n_keys;
         // -- scores (base 2): q.k * scale log2e + slope log2e (p - P)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
@@ -414,7 +434,8 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
                 }
             }
         }
-        __syncthreads();
+        if (more) load_k(c0 + DEC_KC);
+        lds_sync();
         // -- weights: one wavefront per head, keys across lanes
         for (int g = wave; g < G; g += 4) {
             float x0 = lane < nk ? sc[g * DEC_KC + lane] : -INFINITY;
@@ -438,7 +459,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
             if (lane < nk) sc[g * DEC_KC + lane] = x0;
             if (lane + 64 < nk) sc[g * DEC_KC + lane + 64] = x1;
         }
-        __syncthreads();
+        lds_sync();
         // -- values: acc[g][c] = acc * corr + sum_e w[g][e] v[e][8 c8 + c]
         if (a.mode == 1) {
 #pragma unroll
@@ -471,7 +492,8 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
                 }
             }
         }
-        __syncthreads();
+        if (more) load_v(c0 + DEC_KC);
+        lds_sync();
     }
     // ---- sum the key groups and normalise
 #pragma unroll
