@@ -142,36 +142,51 @@ __device__ __forceinline__ uint4 convert_chunk(uint4 x) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Pre-pass: every 64-key tile of one (batch, kv head), once, into its LDS image.
+// Pre-pass: every 64-key tile, once, into its LDS image. One block per (batch, tile, group of
+// up to four kv heads): the rotation angles of a position are read once for the group.
 // K image: rotated (or converted) float16; V image (PACK_V): converted float16. Rows past
 // the sequence end are zero.
+constexpr int PACK_HG = 4;  // kv heads per pre-pass block
+
 template <int D, bool ROT, bool PACK_V>
 __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
     using T = Tile<D>;
+    const int n_hg = (int)((p.Hkv + PACK_HG - 1) / PACK_HG);
     const int bid = blockIdx.x, tid = threadIdx.x;
-    const int jt = bid % p.n_ktiles;
-    const int64_t bh = bid / p.n_ktiles;  // b * H_kv + kv head
-    const int64_t b = bh / p.Hkv, hkv = bh % p.Hkv;
-    uint16_t *kdst = p.kimg + (bh * p.n_ktiles + jt) * T::IMG;
-    uint16_t *vdst = PACK_V ? p.vimg + (bh * p.n_ktiles + jt) * T::IMG : nullptr;
+    const int hg = bid % n_hg;
+    const int rest = bid / n_hg;
+    const int jt = rest % p.n_ktiles;
+    const int64_t b = rest / p.n_ktiles;
+    const int64_t h0 = (int64_t)hg * PACK_HG;
+    const int nh = p.Hkv - h0 < PACK_HG ? (int)(p.Hkv - h0) : PACK_HG;
 #pragma unroll
     for (int r = 0; r < T::KPT; ++r) {
         const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
         const int64_t j = (int64_t)jt * BK + row;
-        uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
-        if (j < p.N) {
-            const int64_t off = ((b * p.N + j) * p.Hkv + hkv) * D + c * 8;
-            xk = ldg16(p.k + off);
-            if (ROT) {
-                const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
-                xk = rotate_chunk(xk, as_float4(ldg16(t)), as_float4(ldg16(t + 4)));
-            } else {
-                xk = convert_chunk(xk);
-            }
-            if (PACK_V) xv = convert_chunk(ldg16(p.v + off));
+        const bool in = j < p.N;
+        float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
+        if (ROT && in) {
+            const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
+            t0 = as_float4(ldg16(t));
+            t1 = as_float4(ldg16(t + 4));
         }
-        stg16(kdst + (row * T::C + (c ^ kswz<D>(row))) * 8, xk);
-        if (PACK_V) stg16(vdst + (row * T::C + (c ^ vswz<D>(row))) * 8, xv);
+        const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
+        const int vslot = (row * T::C + (c ^ vswz<D>(row))) * 8;
+#pragma unroll
+        for (int u = 0; u < PACK_HG; ++u) {
+            if (u >= nh) break;
+            const int64_t hkv = h0 + u;
+            uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
+            if (in) {
+                const int64_t off = ((b * p.N + j) * p.Hkv + hkv) * D + c * 8;
+                xk = ldg16(p.k + off);
+                xk = ROT ? rotate_chunk(xk, t0, t1) : convert_chunk(xk);
+                if (PACK_V) xv = convert_chunk(ldg16(p.v + off));
+            }
+            const int64_t img = ((b * p.Hkv + hkv) * p.n_ktiles + jt) * T::IMG;
+            stg16(p.kimg + img + kslot, xk);
+            if (PACK_V) stg16(p.vimg + img + vslot, xv);
+        }
     }
 }
 
@@ -762,7 +777,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
         pp.kimg = static_cast<uint16_t *>(ws);
         pp.vimg = pl.vf16 ? static_cast<uint16_t *>(ws) + pl.img_bytes / 2 : nullptr;
         pp.rope = a.rope; pp.N = a.N; pp.Hkv = a.Hkv; pp.n_ktiles = (int)pl.n_ktiles;
-        const int npb = (int)(a.B * a.Hkv * pl.n_ktiles);
+        const int npb = (int)(a.B * pl.n_ktiles * ((a.Hkv + PACK_HG - 1) / PACK_HG));
         const hipError_t e = a.d == 64 ? launch_pack<64>(pp, npb, a.rope != nullptr, pl.vf16, st)
                                        : launch_pack<128>(pp, npb, a.rope != nullptr, pl.vf16, st);
         if (e != hipSuccess) return e;
