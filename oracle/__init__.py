@@ -5,8 +5,8 @@ CPU-baseline leg. The product path never imports it, and it imports nothing of t
 product (no kernels, headers, tables or helpers are shared).
 
 Two independent implementations of the same definition, both in float64:
-  * `prefill`, `decode`, `append`: a plain C windowed loop (swa_oracle.c), one query row
-    at a time, OpenMP across rows;
+  * `prefill`, `Ring.decode`, `Ring.append`, `Ring.chunk`: a plain C windowed loop
+    (swa_oracle.c), one query row at a time, OpenMP across rows;
   * `dense.prefill_dense`: numpy, a full [N, N] score matrix masked with the boolean band
     mask built as in the Sliding Window Attention glossary's example.
 
@@ -58,6 +58,9 @@ def bind(path: str):
     lib.swa_oracle_decode.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, dbl, dp,
                                       dbl, dp, ip, dp, dp, ip, dp, dp, dp]
     lib.swa_oracle_decode.restype = ctypes.c_int
+    lib.swa_oracle_chunk.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, dbl, dp,
+                                     dbl, dp, dp, dp, ip, ip, i64, dp, dp, ip, dp, dp, dp]
+    lib.swa_oracle_chunk.restype = ctypes.c_int
     lib.swa_oracle_ring_fill_positions.argtypes = [i64, i64, ip]
     lib.swa_oracle_ring_fill_positions.restype = None
     lib.swa_oracle_threads.argtypes = []
@@ -184,6 +187,42 @@ class Ring:
                                        _ptr(self.k_sink), _ptr(self.v_sink), _ptr(out))
         if rc != 0:
             raise ValueError("oracle decode rejected its arguments")
+        return out
+
+    def chunk(self, q, k_new, v_new, cu_seqlens, pos0, *, H_q: int, mode: int,
+              scale: float = 0.0, slopes=None, rope_theta: float = 0.0,
+              append: bool = True) -> np.ndarray:
+        """Chunked prefill over this ring (swa_oracle_chunk): packed rows, sequence q owns
+        rows cu_seqlens[q] .. cu_seqlens[q+1]-1 at positions pos0[q], pos0[q]+1, ...
+        q [T, H_q, d], k_new/v_new [T, H_kv, d] (keys not rotated) -> float64 [T, H_q, d].
+        With append, the chunk is then appended, one sequence at a time, as append does."""
+        qq, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
+        cu, p0 = _i64(cu_seqlens), _i64(pos0)
+        T = qq.shape[0]
+        assert qq.shape == (T, H_q, self.d) and kn.shape == (T, self.H_kv, self.d)
+        assert vn.shape == kn.shape and cu.shape == (self.S + 1,) and p0.shape == (self.S,)
+        sl = None if slopes is None else _f64(slopes)
+        out = np.zeros((T, H_q, self.d))
+        rc = _load().swa_oracle_chunk(self.S, H_q, self.H_kv, self.d, self.w, self.s, mode,
+                                      float(scale), _ptr(sl), float(rope_theta), _ptr(qq),
+                                      _ptr(kn), _ptr(vn), _ptr(cu), _ptr(p0), T,
+                                      _ptr(self.k), _ptr(self.v), _ptr(self.pos),
+                                      _ptr(self.k_sink), _ptr(self.v_sink), _ptr(out))
+        if rc == -2:
+            raise ValueError("oracle chunk: the ring does not hold a key the chunk needs")
+        if rc != 0:
+            raise ValueError("oracle chunk rejected its arguments")
+        if append:
+            for sq in range(self.S):
+                a, b = int(cu[sq]), int(cu[sq + 1])
+                if b == a:
+                    continue
+                kpad = np.zeros((self.S, b - a, self.H_kv, self.d))
+                vpad = np.zeros_like(kpad)
+                kpad[sq], vpad[sq] = kn[a:b], vn[a:b]
+                only = np.full(self.S, -1, dtype=np.int64)
+                only[sq] = p0[sq]
+                self.append(kpad, vpad, only, rope_theta=rope_theta)
         return out
 
 

@@ -294,3 +294,106 @@ int swa_oracle_decode(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, 
     free(qt); free(x); free(vv);
     return 0;
 }
+
+/*
+ * Chunked prefill over the ring (a serving step between whole-sequence prefill and
+ * single-token decode; Sliding Window Attention glossary, ring-buffer paragraph: the cache
+ * keeps the last w tokens, so a new chunk needs nothing older than that besides the sinks).
+ * Sequence q contributes the packed rows cu[q] .. cu[q+1]-1 of q, k_new, v_new and o; row
+ * cu[q] + r is the token at position pos0[q] + r. Query i of the chunk attends to the key set
+ * K(i) of the prefill definition; key j is read from
+ *   - the chunk itself when j >= pos0[q] (row cu[q] + j - pos0[q], rotated at j here),
+ *   - else the ring slot j mod w when that slot records position j,
+ *   - else the sink store when j < s.
+ * A key found in none of them means the cache does not hold the sequence's history: the
+ * call fails (-2). The ring is only read here (appending the chunk is a separate step).
+ * q, o [T, H_q, d]; k_new, v_new [T, H_kv, d]; rings and sinks as in swa_oracle_append.
+ * pos0[q] >= 0 for every sequence. Returns 0, -1 on bad arguments, -2 on missing history.
+ */
+int swa_oracle_chunk(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, int64_t s,
+                     int mode, double scale, const double *slopes, double theta,
+                     const double *q, const double *k_new, const double *v_new,
+                     const int64_t *cu, const int64_t *pos0, int64_t T, const double *k_ring,
+                     const double *v_ring, const int64_t *ring_pos, const double *k_sink,
+                     const double *v_sink, double *o) {
+    if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || w < 1 || s < 0 || T < 0)
+        return -1;
+    if (theta > 0.0 && d % 2 != 0) return -1;
+    if (s > 0 && (!k_sink || !v_sink)) return -1;
+    for (int64_t sq = 0; sq < S; ++sq)
+        if (pos0[sq] < 0 || cu[sq] < 0 || cu[sq] > cu[sq + 1] || cu[sq + 1] > T) return -1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    int64_t group = Hq / Hkv;
+    int64_t total = T * Hq;
+    int status = 0;
+
+#pragma omp parallel
+    {
+        double *qt = (double *)malloc(sizeof(double) * (size_t)d);
+        double *kt = (double *)malloc(sizeof(double) * (size_t)d);
+        double *x = (double *)malloc(sizeof(double) * (size_t)(w + s + 1));
+        const double **vv = (const double **)malloc(sizeof(double *) * (size_t)(w + s + 1));
+        if (!qt || !kt || !x || !vv) {
+#pragma omp atomic write
+            status = -1;
+        } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t idx = 0; idx < total; ++idx) {
+                int64_t h = idx % Hq, row = idx / Hq;
+                int64_t sq = -1;
+                for (int64_t t = 0; t < S; ++t)
+                    if (cu[t] <= row && row < cu[t + 1]) { sq = t; break; }
+                if (sq < 0) continue;  /* a row no sequence claims is left as it is */
+                int64_t p0 = pos0[sq];
+                int64_t i = p0 + (row - cu[sq]);
+                int64_t hk = h / group;
+                const double *qi = q + (row * Hq + h) * d;
+                if (theta > 0.0) rotate_direct(qi, qt, d, i, theta);
+                else memcpy(qt, qi, sizeof(double) * (size_t)d);
+
+                /* K(i) as two disjoint ranges: sinks [0, min(s, lo)) and window [lo, i]. */
+                int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;
+                int64_t n_sink = s < lo ? s : lo;
+                int64_t n = 0;
+                int missing = 0;
+                for (int64_t e = 0; e < n_sink + (i - lo + 1); ++e) {
+                    int64_t j = e < n_sink ? e : lo + (e - n_sink);
+                    const double *kj;
+                    if (j >= p0) {
+                        int64_t src = cu[sq] + (j - p0);
+                        const double *kn = k_new + (src * Hkv + hk) * d;
+                        if (theta > 0.0) rotate_direct(kn, kt, d, j, theta);
+                        else memcpy(kt, kn, sizeof(double) * (size_t)d);
+                        kj = kt;
+                        vv[n] = v_new + (src * Hkv + hk) * d;
+                    } else if (ring_pos[sq * w + j % w] == j) {
+                        int64_t slot = j % w;
+                        kj = k_ring + ((sq * Hkv + hk) * w + slot) * d;
+                        vv[n] = v_ring + ((sq * Hkv + hk) * w + slot) * d;
+                    } else if (j < s) {
+                        kj = k_sink + ((sq * Hkv + hk) * s + j) * d;
+                        vv[n] = v_sink + ((sq * Hkv + hk) * s + j) * d;
+                    } else {
+                        missing = 1;
+                        break;
+                    }
+                    double bias = slopes ? slopes[h] * (double)(i - j) : 0.0;
+                    x[n] = scale * dot(qt, kj, d) + bias;
+                    ++n;
+                }
+                if (missing) {
+#pragma omp atomic write
+                    status = -2;
+                    continue;
+                }
+                weights(x, n, mode);
+                double *oi = o + (row * Hq + h) * d;
+                for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
+                for (int64_t e = 0; e < n; ++e)
+                    for (int64_t c = 0; c < d; ++c) oi[c] += x[e] * vv[e][c];
+            }
+        }
+        free(qt); free(kt); free(x); free(vv);
+    }
+    return status;
+}

@@ -1,7 +1,7 @@
 """Planted mistakes: each test compiles a copy of the C oracle with one plausible slip and
 checks that the pin suite rejects it. This shows the pins constrain every part of the
 definition (selection, sinks, bias sign, rotation, frequency, weights, scale, head map,
-ring slot), not only the parts a random-input comparison would notice. CPU only."""
+ring slot, chunk offsets), not only the parts a random-input comparison would notice. CPU only."""
 import os
 import subprocess
 
@@ -31,6 +31,11 @@ MUTANTS = [
     ("ring_slot", "int64_t slot = p % w;", "int64_t slot = (p + 1) % w;"),
     ("scale", "if (scale <= 0.0) scale = 1.0 / sqrt((double)d);\n    int64_t nr",
      "if (scale <= 0.0) scale = 1.0 / (double)d;\n    int64_t nr"),
+    ("chunk_query_position", "int64_t i = p0 + (row - cu[sq]);", "int64_t i = row - cu[sq];"),
+    ("chunk_key_row", "int64_t src = cu[sq] + (j - p0);", "int64_t src = j - p0;"),
+    ("chunk_key_rotation", "rotate_direct(kn, kt, d, j, theta);",
+     "rotate_direct(kn, kt, d, p0, theta);"),
+    ("chunk_boundary", "if (j >= p0) {", "if (j > p0) {"),
 ]
 
 PIN_TESTS = [
@@ -49,6 +54,7 @@ PIN_TESTS = [
     (pins.test_ring_slot_closed_form, dict(w=7)),
     (pins.test_append_writes_position_mod_w, dict(w=3)),
     (pins.test_decode_equals_prefill_row_by_row, dict(mode=oracle.SIGMOID, w=5, s=2)),
+    (pins.test_chunked_prefill_equals_whole_prefill, dict(mode=oracle.SOFTMAX, w=6, s=2)),
 ]
 
 
@@ -60,7 +66,8 @@ def test_unmutated_oracle_passes_the_mutant_harness():
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_reject_planted_mistake(name, old, new, tmp_path, monkeypatch):
     src = open(SRC).read()
-    assert src.count(old) == 1, "mutation anchor not found exactly once: " + name
+    # an anchor shared by several functions is mutated in all of them
+    assert src.count(old) >= 1, "mutation anchor not found: " + name
     mutant_c = tmp_path / ("oracle_%s.c" % name)
     mutant_c.write_text(src.replace(old, new))
     so = tmp_path / ("liboracle_%s.so" % name)

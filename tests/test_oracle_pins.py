@@ -380,3 +380,70 @@ def test_append_writes_position_mod_w(w):
             assert ring.pos[0, t] == (held if held >= 0 else -1)
             if held >= 0:
                 assert ring.v[0, 0, t, 0] == float(held)
+
+
+# ----------------------------------------------------------------------------- chunked prefill
+
+def _chunk_schedule(S, N, seed):
+    """Ragged split points per sequence: round r hands sequence q the tokens
+    [cuts[q][r], cuts[q][r+1]) (possibly none)."""
+    rng = np.random.default_rng(seed)
+    cuts = []
+    for _ in range(S):
+        inner = np.sort(rng.choice(np.arange(1, N), size=3, replace=False))
+        cuts.append([0] + inner.tolist() + [N])
+    return cuts
+
+
+@pytest.mark.parametrize("mode", [oracle.SIGMOID, oracle.SOFTMAX])
+@pytest.mark.parametrize("w,s", [(5, 0), (6, 2), (9, 4), (40, 1), (3, 7)])
+def test_chunked_prefill_equals_whole_prefill(mode, w, s):
+    """Feeding each sequence in ragged chunks (packed rows, different chunk lengths per
+    sequence in one call, empty chunks included), each chunk reading its history from the
+    ring and then appended, reproduces the whole-sequence prefill row for row: the ring keeps
+    exactly the history a window needs (Sliding Window Attention glossary, ring buffer)."""
+    S, N, Hq, Hkv, d, theta = 3, 26, 4, 2, 8, 1e4
+    q, k, v = _rand((S, N, Hq, d), 30), _rand((S, N, Hkv, d), 31), _rand((S, N, Hkv, d), 32)
+    slopes = [-0.3, -0.1, 0.3, 0.1]
+    ref = oracle.prefill(q, k, v, w=w, s=s, mode=mode, slopes=slopes, rope_theta=theta)
+    cuts = _chunk_schedule(S, N, seed=w * 10 + s)
+    ring = oracle.Ring(S, Hkv, w, s, d)
+    got = np.full_like(ref, np.nan)
+    for r in range(4):
+        lens = [cuts[sq][r + 1] - cuts[sq][r] for sq in range(S)]
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        pos0 = np.array([cuts[sq][r] for sq in range(S)])
+        rows = lambda a: np.concatenate([a[sq, cuts[sq][r]:cuts[sq][r + 1]] for sq in range(S)])
+        o = ring.chunk(rows(q), rows(k), rows(v), cu, pos0, H_q=Hq, mode=mode, slopes=slopes,
+                       rope_theta=theta)
+        for sq in range(S):
+            got[sq, cuts[sq][r]:cuts[sq][r + 1]] = o[cu[sq]:cu[sq + 1]]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode", [oracle.SIGMOID, oracle.SOFTMAX])
+def test_chunk_of_one_token_equals_decode(mode):
+    """A one-token chunk is a decode step: same output as appending it and calling decode."""
+    S, Hq, Hkv, d, w, s, theta = 2, 4, 2, 8, 6, 2, 1e4
+    hist = 11
+    k, v = _rand((S, hist + 1, Hkv, d), 40), _rand((S, hist + 1, Hkv, d), 41)
+    qn = _rand((S, Hq, d), 42)
+    a, b = oracle.Ring(S, Hkv, w, s, d), oracle.Ring(S, Hkv, w, s, d)
+    for ring in (a, b):
+        ring.append(k[:, :hist], v[:, :hist], np.zeros(S, dtype=np.int64), rope_theta=theta)
+    pos = np.full(S, hist)
+    o_chunk = a.chunk(qn, k[:, hist], v[:, hist], np.arange(S + 1), pos, H_q=Hq, mode=mode,
+                      rope_theta=theta)
+    b.append(k[:, hist:], v[:, hist:], pos, rope_theta=theta)
+    o_dec = b.decode(qn, pos, H_q=Hq, mode=mode, rope_theta=theta)
+    np.testing.assert_allclose(o_chunk, o_dec, rtol=1e-12, atol=1e-13)
+    for x, y in [(a.k, b.k), (a.v, b.v), (a.pos, b.pos), (a.k_sink, b.k_sink)]:
+        np.testing.assert_array_equal(x, y)
+
+
+def test_chunk_without_history_is_rejected():
+    """A chunk that starts past position 0 needs its window's history in the ring."""
+    ring = oracle.Ring(1, 1, 4, 0, 2)
+    with pytest.raises(ValueError, match="does not hold"):
+        ring.chunk(np.ones((2, 1, 2)), np.ones((2, 1, 2)), np.ones((2, 1, 2)), [0, 2], [5],
+                   H_q=1, mode=oracle.SOFTMAX)
