@@ -183,6 +183,43 @@ swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, con
 /* Bytes of workspace swa_decode needs for this problem (0 when it needs none). */
 size_t swa_decode_workspace_bytes(const swa_decode_params *p, const swa_cache *c);
 
+/*
+ * Chunked prefill over the ring cache, variable-length batch (a new chunk of each sequence
+ * attends to its cached history and to itself; Sliding Window Attention glossary: the ring
+ * buffer keeps the last w tokens, which is all a chunk's window can reach besides the sinks).
+ * Sequence q owns the packed rows cu_seqlens[q] .. cu_seqlens[q+1]-1 of q, k_new, v_new
+ * and o; row cu_seqlens[q] + r is the token at position pos0[q] + r. The cache must hold
+ * positions 0 .. pos0[q]-1 of that sequence, appended earlier (swa_kv_append, an earlier
+ * chunk, or decode steps). Every query i of the chunk is answered over the key set K(i)
+ * of swa_prefill, reading keys j < pos0[q] from the ring or the sink store and keys
+ * j >= pos0[q] from the chunk; scores, bias and weights are as in swa_prefill. After the
+ * attention the chunk is appended to the cache exactly as swa_kv_append would append it.
+ *   q, o         : [total_rows, H_q, d]    (q not rotated)
+ *   k_new, v_new : [total_rows, H_kv, d]   (cache dtype, keys not rotated)
+ *   cu_seqlens   : device int32[num_seqs + 1]   pos0: device int32[num_seqs]
+ *   max_seqlen   : host bound on cu_seqlens[q+1] - cu_seqlens[q]
+ * p: as for swa_decode (its out_dtype is the dtype of o). A sequence with no rows is a no-op.
+ * A sequence whose pos0 is negative, whose row count exceeds max_seqlen, or whose last
+ * position lies outside the rotation table gets NaN rows and its cache is left untouched;
+ * rows outside [0, total_rows) are never written (such a sequence is skipped). Sequences'
+ * row ranges must not overlap.
+ * Requirements: a bf16 cache with d in {64, 128} and 16-byte aligned tensors (else
+ * SWA_ERR_UNSUPPORTED). The attention runs on the matrix cores as in swa_prefill, with the
+ * same operand ranges. workspace: device scratch of swa_prefill_chunk_workspace_bytes bytes,
+ * 16-byte aligned, holding float16 tile images of each sequence's sinks and of the window
+ * positions the chunk can reach: about 2 * num_seqs * H_kv * (s + w + max_seqlen) * d * 2
+ * bytes (fewer when the rotation table bounds the positions).
+ */
+swa_status swa_prefill_chunk(const swa_decode_params *p, const swa_cache *c, const void *q,
+                             const void *k_new, const void *v_new, const int32_t *cu_seqlens,
+                             const int32_t *pos0, int64_t total_rows, int64_t max_seqlen,
+                             void *o, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace swa_prefill_chunk needs (0 when it needs none or the arguments are
+ * invalid or unsupported). */
+size_t swa_prefill_chunk_workspace_bytes(const swa_decode_params *p, const swa_cache *c,
+                                         int64_t total_rows, int64_t max_seqlen);
+
 /* Static, human-readable text for a status code. */
 const char *swa_status_string(swa_status s);
 

@@ -59,7 +59,8 @@ def bind(path: str):
                                       dbl, dp, ip, dp, dp, ip, dp, dp, dp]
     lib.swa_oracle_decode.restype = ctypes.c_int
     lib.swa_oracle_chunk.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, dbl, dp,
-                                     dbl, dp, dp, dp, ip, ip, i64, dp, dp, ip, dp, dp, dp]
+                                     dbl, dp, dp, dp, ip, ip, i64, dp, dp, ip, dp, dp, ip, i64,
+                                     dp]
     lib.swa_oracle_chunk.restype = ctypes.c_int
     lib.swa_oracle_ring_fill_positions.argtypes = [i64, i64, ip]
     lib.swa_oracle_ring_fill_positions.restype = None
@@ -191,23 +192,26 @@ class Ring:
 
     def chunk(self, q, k_new, v_new, cu_seqlens, pos0, *, H_q: int, mode: int,
               scale: float = 0.0, slopes=None, rope_theta: float = 0.0,
-              append: bool = True) -> np.ndarray:
+              append: bool = True, rows=None) -> np.ndarray:
         """Chunked prefill over this ring (swa_oracle_chunk): packed rows, sequence q owns
         rows cu_seqlens[q] .. cu_seqlens[q+1]-1 at positions pos0[q], pos0[q]+1, ...
         q [T, H_q, d], k_new/v_new [T, H_kv, d] (keys not rotated) -> float64 [T, H_q, d].
-        With append, the chunk is then appended, one sequence at a time, as append does."""
+        With append, the chunk is then appended, one sequence at a time, as append does.
+        rows: optional list of packed rows; then the result is [len(rows), H_q, d]."""
         qq, kn, vn = _f64(q), _f64(k_new), _f64(v_new)
         cu, p0 = _i64(cu_seqlens), _i64(pos0)
         T = qq.shape[0]
         assert qq.shape == (T, H_q, self.d) and kn.shape == (T, self.H_kv, self.d)
         assert vn.shape == kn.shape and cu.shape == (self.S + 1,) and p0.shape == (self.S,)
         sl = None if slopes is None else _f64(slopes)
-        out = np.zeros((T, H_q, self.d))
+        r = None if rows is None else _i64(rows)
+        out = np.zeros((T if r is None else r.shape[0], H_q, self.d))
         rc = _load().swa_oracle_chunk(self.S, H_q, self.H_kv, self.d, self.w, self.s, mode,
                                       float(scale), _ptr(sl), float(rope_theta), _ptr(qq),
                                       _ptr(kn), _ptr(vn), _ptr(cu), _ptr(p0), T,
                                       _ptr(self.k), _ptr(self.v), _ptr(self.pos),
-                                      _ptr(self.k_sink), _ptr(self.v_sink), _ptr(out))
+                                      _ptr(self.k_sink), _ptr(self.v_sink), _ptr(r),
+                                      0 if r is None else r.shape[0], _ptr(out))
         if rc == -2:
             raise ValueError("oracle chunk: the ring does not hold a key the chunk needs")
         if rc != 0:

@@ -307,24 +307,30 @@ int swa_oracle_decode(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, 
  *   - else the sink store when j < s.
  * A key found in none of them means the cache does not hold the sequence's history: the
  * call fails (-2). The ring is only read here (appending the chunk is a separate step).
- * q, o [T, H_q, d]; k_new, v_new [T, H_kv, d]; rings and sinks as in swa_oracle_append.
- * pos0[q] >= 0 for every sequence. Returns 0, -1 on bad arguments, -2 on missing history.
+ * q [T, H_q, d]; k_new, v_new [T, H_kv, d]; rings and sinks as in swa_oracle_append.
+ * rows == NULL: o is [T, H_q, d]; otherwise only the listed packed rows are computed and o
+ * is [n_rows, H_q, d] in list order. pos0[q] >= 0 for every sequence.
+ * Returns 0, -1 on bad arguments, -2 on missing history.
  */
 int swa_oracle_chunk(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, int64_t s,
                      int mode, double scale, const double *slopes, double theta,
                      const double *q, const double *k_new, const double *v_new,
                      const int64_t *cu, const int64_t *pos0, int64_t T, const double *k_ring,
                      const double *v_ring, const int64_t *ring_pos, const double *k_sink,
-                     const double *v_sink, double *o) {
+                     const double *v_sink, const int64_t *rows, int64_t n_rows, double *o) {
     if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || w < 1 || s < 0 || T < 0)
         return -1;
+    if (rows) {
+        for (int64_t r = 0; r < n_rows; ++r) if (rows[r] < 0 || rows[r] >= T) return -1;
+    }
     if (theta > 0.0 && d % 2 != 0) return -1;
     if (s > 0 && (!k_sink || !v_sink)) return -1;
     for (int64_t sq = 0; sq < S; ++sq)
         if (pos0[sq] < 0 || cu[sq] < 0 || cu[sq] > cu[sq + 1] || cu[sq + 1] > T) return -1;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
     int64_t group = Hq / Hkv;
-    int64_t total = T * Hq;
+    int64_t nr = rows ? n_rows : T;
+    int64_t total = nr * Hq;
     int status = 0;
 
 #pragma omp parallel
@@ -339,7 +345,8 @@ int swa_oracle_chunk(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, i
         } else {
 #pragma omp for schedule(dynamic, 16)
             for (int64_t idx = 0; idx < total; ++idx) {
-                int64_t h = idx % Hq, row = idx / Hq;
+                int64_t h = idx % Hq, r_out = idx / Hq;
+                int64_t row = rows ? rows[r_out] : r_out;
                 int64_t sq = -1;
                 for (int64_t t = 0; t < S; ++t)
                     if (cu[t] <= row && row < cu[t + 1]) { sq = t; break; }
@@ -387,7 +394,7 @@ int swa_oracle_chunk(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, i
                     continue;
                 }
                 weights(x, n, mode);
-                double *oi = o + (row * Hq + h) * d;
+                double *oi = o + (r_out * Hq + h) * d;
                 for (int64_t c = 0; c < d; ++c) oi[c] = 0.0;
                 for (int64_t e = 0; e < n; ++e)
                     for (int64_t c = 0; c < d; ++c) oi[c] += x[e] * vv[e][c];

@@ -56,7 +56,8 @@ class DecodeParams(ctypes.Structure):
 
 
 EXPORTS = ["swa_prefill", "swa_prefill_workspace_bytes", "swa_rope_table", "swa_rope_apply", "swa_kv_append", "swa_decode",
-           "swa_decode_append", "swa_decode_workspace_bytes", "swa_status_string",
+           "swa_decode_append", "swa_decode_workspace_bytes", "swa_prefill_chunk",
+           "swa_prefill_chunk_workspace_bytes", "swa_status_string",
            "swa_last_hip_error", "swa_version"]
 
 _lib = None
@@ -92,6 +93,13 @@ def load():
         lib.swa_decode_append.restype = ctypes.c_int
         lib.swa_decode_workspace_bytes.argtypes = [P(DecodeParams), P(CacheDesc)]
         lib.swa_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.swa_prefill_chunk.argtypes = [P(DecodeParams), P(CacheDesc), c_ptr, c_ptr, c_ptr,
+                                          c_ptr, c_ptr, c_i64, c_i64, c_ptr, c_ptr,
+                                          ctypes.c_size_t, c_ptr]
+        lib.swa_prefill_chunk.restype = ctypes.c_int
+        lib.swa_prefill_chunk_workspace_bytes.argtypes = [P(DecodeParams), P(CacheDesc), c_i64,
+                                                          c_i64]
+        lib.swa_prefill_chunk_workspace_bytes.restype = ctypes.c_size_t
         lib.swa_status_string.argtypes = [ctypes.c_int]
         lib.swa_status_string.restype = ctypes.c_char_p
         lib.swa_last_hip_error.argtypes = []
@@ -367,4 +375,62 @@ def swa_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
            load().swa_decode_append(ctypes.byref(p), ctypes.byref(cache.desc), _ptr(q),
                                     _ptr(k_new), _ptr(v_new), _ptr(q_pos), _ptr(out),
                                     _ptr(workspace), ws_bytes, _stream(q.device, stream)))
+    return out
+
+
+def swa_prefill_chunk_workspace_bytes(cache: SwaCache, H_q: int, total_rows: int,
+                                      max_seqlen: int, *, mode=SWA_SOFTMAX,
+                                      rope_table: Optional[torch.Tensor] = None) -> int:
+    """Workspace bytes swa_prefill_chunk needs (the rotation table, when given, bounds the
+    positions and can shrink it)."""
+    p = _decode_params(H_q, mode, 0.0, None, rope_table, SWA_F32)
+    return int(load().swa_prefill_chunk_workspace_bytes(ctypes.byref(p), ctypes.byref(cache.desc),
+                                                        int(total_rows), int(max_seqlen)))
+
+
+def swa_prefill_chunk(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                      cu_seqlens: torch.Tensor, pos0: torch.Tensor, cache: SwaCache, *,
+                      max_seqlen: int, mode=SWA_SOFTMAX, scale: float = 0.0,
+                      alibi_slopes: Optional[torch.Tensor] = None,
+                      rope_table: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Chunked prefill over the ring cache. Packed rows: sequence s owns rows
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 of q [T, H_q, d] and k_new/v_new [T, H_kv, d] (keys
+    not rotated), at positions pos0[s], pos0[s]+1, ...; the cache holds each sequence's
+    positions below pos0[s]. Returns o [T, H_q, d]; the chunk is appended to the cache."""
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (cu_seqlens, "cu_seqlens"),
+                 (pos0, "pos0")):
+        _dev(t, n)
+    T = q.shape[0]
+    if q.dim() != 3 or q.shape[2] != cache.d:
+        raise ValueError("q must be [T, H_q, d]")
+    if tuple(k_new.shape) != (T, cache.H_kv, cache.d) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [T, H_kv, d]")
+    if q.dtype != cache.dtype or k_new.dtype != cache.dtype or v_new.dtype != cache.dtype:
+        raise ValueError("q, k_new, v_new must have the cache dtype")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.numel() != cache.S + 1:
+        raise ValueError("cu_seqlens must be int32[S + 1]")
+    if pos0.dtype != torch.int32 or pos0.numel() != cache.S:
+        raise ValueError("pos0 must be int32[S]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    _dev(out, "out")
+    if alibi_slopes is not None:
+        _dev(alibi_slopes, "alibi_slopes")
+    if rope_table is not None:
+        _dev(rope_table, "rope_table")
+    p = _decode_params(q.shape[1], mode, scale, alibi_slopes, rope_table, _dt(out))
+    need = int(load().swa_prefill_chunk_workspace_bytes(ctypes.byref(p), ctypes.byref(cache.desc),
+                                                        T, int(max_seqlen)))
+    ws_bytes = 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("swa_prefill_chunk",
+           load().swa_prefill_chunk(ctypes.byref(p), ctypes.byref(cache.desc), _ptr(q),
+                                    _ptr(k_new), _ptr(v_new), _ptr(cu_seqlens), _ptr(pos0), T,
+                                    int(max_seqlen), _ptr(out), _ptr(workspace), ws_bytes,
+                                    _stream(q.device, stream)))
     return out

@@ -80,6 +80,49 @@ __host__ __device__ __forceinline__ constexpr int vswz(int r) {
     return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
 }
 
+// A chunked call (prefill over the ring cache): sequence b owns the packed rows
+// cu[b] .. cu[b+1]-1, the tokens at positions pos0[b], pos0[b] + 1, ...
+struct ChunkGeom {
+    const int32_t *cu, *pos0;
+    int64_t T;        // packed rows of q, k_new, v_new and o
+    int max_q;        // rows of the longest sequence the launch covers
+    int pos_limit;    // positions must stay below this (rotation table rows, float-exact)
+    int w;            // window (clamped to the position range)
+    int ns_img;       // sink tiles at the front of every sequence's tile images
+};
+
+// Where sequence b's rows and key tiles are. Its images hold the sink tiles [0, ns_img)
+// (whole 64-position tiles) and then the window tiles the chunk's queries can reach,
+// [max(lo, ns_img), hi) with lo the tile of position p0 - w + 1 and hi the tile past the
+// chunk's last position; window tile t >= ns_img is image tile t - shift.
+struct ChunkSeq {
+    bool rows_ok;     // the row range lies inside [0, T): rows may be written
+    bool valid;       // the sequence runs (else its rows become NaN, its cache is untouched)
+    int p0, n;
+    int64_t row0;
+    int shift, n_img;
+};
+
+__device__ __forceinline__ ChunkSeq chunk_seq(const ChunkGeom &g, int64_t b) {
+    ChunkSeq c;
+    const int64_t c0 = g.cu[b], c1 = g.cu[b + 1], p0 = g.pos0[b];
+    c.rows_ok = c0 >= 0 && c0 <= c1 && c1 <= g.T;
+    c.valid = c.rows_ok && p0 >= 0 && c1 - c0 <= g.max_q && p0 + (c1 - c0) <= g.pos_limit;
+    c.p0 = (int)p0;
+    c.n = (int)(c1 - c0);
+    c.row0 = c0;
+    c.shift = 0;
+    c.n_img = 0;
+    if (c.valid) {
+        const int lo_pos = c.p0 - g.w + 1 > 0 ? c.p0 - g.w + 1 : 0;
+        const int lo = lo_pos / BK > g.ns_img ? lo_pos / BK : g.ns_img;
+        const int hi = (c.p0 + c.n + BK - 1) / BK;
+        c.shift = lo - g.ns_img;
+        c.n_img = g.ns_img + (hi > lo ? hi - lo : 0);
+    }
+    return c;
+}
+
 struct MfmaParams {
     const uint16_t *q, *k, *v;
     const uint16_t *kimg, *vimg;  // packed tile images, or null
@@ -93,6 +136,8 @@ struct MfmaParams {
     uint32_t kv_bytes;        // bytes of one (batch, kv head) K or V slice, rows [0, N)
     uint32_t row_bytes;       // bytes between consecutive positions of K/V
     int out_bf16;
+    int chunked;              // 1: rows and positions per sequence from cg; V from vimg
+    ChunkGeom cg;
 };
 
 struct PackParams {
@@ -186,6 +231,140 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
             const int64_t img = ((b * p.Hkv + hkv) * p.n_ktiles + jt) * T::IMG;
             stg16(p.kimg + img + kslot, xk);
             if (PACK_V) stg16(p.vimg + img + vslot, xv);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Chunked calls. The gather pre-pass builds each sequence's tile images from three sources:
+// position j >= p0 is the chunk's own row (key rotated here), p0 - w <= j < p0 is the ring
+// slot j mod w (keys stored rotated), j < s the sink store; anything else (positions no query
+// of the chunk can see, or past the chunk) is zero. K images are float16 with the K swizzle;
+// V images are float16 with the V swizzle (softmax) or bf16 row-major without swizzle
+// (sigmoid, read by the same transfers as V input rows).
+struct GatherParams {
+    ChunkGeom cg;
+    const uint16_t *k_new, *v_new;    // [T, Hkv, D]
+    const uint16_t *k_ring, *v_ring;  // [S, Hkv, w_ring, D]
+    const uint16_t *k_sink, *v_sink;  // [S, Hkv, s, D]
+    uint16_t *kimg, *vimg;
+    const float *rope;
+    int64_t Hkv, w_ring, s;
+    int n_ktiles;                      // image tiles per (sequence, kv head)
+};
+
+template <int D, bool ROT, bool VF16>
+__global__ __launch_bounds__(256) void chunk_gather_kernel(GatherParams p) {
+    using T = Tile<D>;
+    const int n_hg = (int)((p.Hkv + PACK_HG - 1) / PACK_HG);
+    const int bid = blockIdx.x, tid = threadIdx.x;
+    const int hg = bid % n_hg;
+    const int rest = bid / n_hg;
+    const int u = rest % p.n_ktiles;
+    const int64_t b = rest / p.n_ktiles;
+    const ChunkSeq cs = chunk_seq(p.cg, b);
+    if (!cs.valid || u >= cs.n_img) return;
+    const int64_t t = u < p.cg.ns_img ? u : u + cs.shift;
+    const int64_t h0 = (int64_t)hg * PACK_HG;
+    const int nh = p.Hkv - h0 < PACK_HG ? (int)(p.Hkv - h0) : PACK_HG;
+#pragma unroll
+    for (int r = 0; r < T::KPT; ++r) {
+        const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+        const int64_t j = t * BK + row;
+        // 0: zero, 1: chunk row, 2: ring slot, 3: sink entry
+        const int src = j >= cs.p0 + cs.n ? 0
+                        : j >= cs.p0 ? 1
+                        : (j >= cs.p0 - p.w_ring && j >= 0) ? 2
+                        : j < p.s ? 3 : 0;
+        float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
+        if (ROT && src == 1) {
+            const float *tb = p.rope + (j * (D / 2) + c * 4) * 2;
+            t0 = as_float4(ldg16(tb));
+            t1 = as_float4(ldg16(tb + 4));
+        }
+        const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
+        const int vslot = VF16 ? (row * T::C + (c ^ vswz<D>(row))) * 8 : (row * T::C + c) * 8;
+#pragma unroll
+        for (int e = 0; e < PACK_HG; ++e) {
+            if (e >= nh) break;
+            const int64_t hkv = h0 + e;
+            uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
+            if (src == 1) {
+                const int64_t off = ((cs.row0 + (j - cs.p0)) * p.Hkv + hkv) * D + c * 8;
+                xk = ldg16(p.k_new + off);
+                xk = ROT ? rotate_chunk(xk, t0, t1) : convert_chunk(xk);
+                xv = ldg16(p.v_new + off);
+            } else if (src == 2) {
+                const int64_t off = ((b * p.Hkv + hkv) * p.w_ring + j % p.w_ring) * D + c * 8;
+                xk = convert_chunk(ldg16(p.k_ring + off));
+                xv = ldg16(p.v_ring + off);
+            } else if (src == 3) {
+                const int64_t off = ((b * p.Hkv + hkv) * p.s + j) * D + c * 8;
+                xk = convert_chunk(ldg16(p.k_sink + off));
+                xv = ldg16(p.v_sink + off);
+            }
+            if (VF16) xv = convert_chunk(xv);
+            const int64_t img = ((b * p.Hkv + hkv) * p.n_ktiles + u) * T::IMG;
+            stg16(p.kimg + img + kslot, xk);
+            stg16(p.vimg + img + vslot, xv);
+        }
+    }
+}
+
+// After the attention, the chunk joins the cache: row r of a sequence with n rows goes to
+// ring slot (p0 + r) mod w when it is among the last w rows (a later row of the same call
+// would overwrite it), and to the sink store when p0 + r < s. Keys are rotated at their
+// position in float32 and rounded once to bf16, as the single-token append stores them.
+// One block per (sequence, 64 rows); a thread moves 8 elements of one (row, kv head).
+struct ChunkAppendParams {
+    ChunkGeom cg;
+    const uint16_t *k_new, *v_new;
+    uint16_t *k_ring, *v_ring, *k_sink, *v_sink;
+    const float *rope;
+    int64_t Hkv, w_ring, s;
+    int n_rtiles;                      // 64-row tiles per sequence in the grid
+};
+
+__device__ __forceinline__ uint32_t rotate_pair_bf16(uint32_t w, float c, float s) {
+    const float a = __uint_as_float(w << 16);
+    const float b = __uint_as_float(w & 0xffff0000u);
+    return pack_bf16x2(fmaf(-b, s, a * c), fmaf(a, s, b * c));
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void chunk_append_kernel(ChunkAppendParams p) {
+    constexpr int C = D / 8;
+    const int64_t b = blockIdx.x / p.n_rtiles;
+    const int rt = blockIdx.x % p.n_rtiles;
+    const ChunkSeq cs = chunk_seq(p.cg, b);
+    if (!cs.valid || rt * BK >= cs.n) return;
+    const int rows = cs.n - rt * BK < BK ? cs.n - rt * BK : BK;
+    const int64_t per_row = p.Hkv * C;
+    for (int64_t e = threadIdx.x; e < rows * per_row; e += 256) {
+        const int r = rt * BK + (int)(e / per_row);
+        const int64_t hkv = (e % per_row) / C;
+        const int c = (int)(e % C);
+        const int64_t pos = (int64_t)cs.p0 + r;
+        const bool to_ring = r >= cs.n - p.w_ring, to_sink = pos < p.s;
+        if (!to_ring && !to_sink) continue;
+        const int64_t src = ((cs.row0 + r) * p.Hkv + hkv) * D + c * 8;
+        uint4 xk = ldg16(p.k_new + src);
+        const uint4 xv = ldg16(p.v_new + src);
+        if (p.rope) {
+            const float4 t0 = as_float4(ldg16(p.rope + (pos * (D / 2) + c * 4) * 2));
+            const float4 t1 = as_float4(ldg16(p.rope + (pos * (D / 2) + c * 4) * 2 + 4));
+            xk = make_uint4(rotate_pair_bf16(xk.x, t0.x, t0.y), rotate_pair_bf16(xk.y, t0.z, t0.w),
+                            rotate_pair_bf16(xk.z, t1.x, t1.y), rotate_pair_bf16(xk.w, t1.z, t1.w));
+        }
+        if (to_ring) {
+            const int64_t dst = ((b * p.Hkv + hkv) * p.w_ring + pos % p.w_ring) * D + c * 8;
+            stg16(p.k_ring + dst, xk);
+            stg16(p.v_ring + dst, xv);
+        }
+        if (to_sink) {
+            const int64_t dst = ((b * p.Hkv + hkv) * p.s + pos) * D + c * 8;
+            stg16(p.k_sink + dst, xk);
+            stg16(p.v_sink + dst, xv);
         }
     }
 }
@@ -396,7 +575,14 @@ struct TileCtx {
     uint32_t row_bytes;
     int tid, wave, qa, qb, i, g, w, s, N;
     int n_tiles, ts_end, tw_begin;  // the walk: sink tiles [0, ts_end), then window tiles
+    int ns_img, shift;              // tile t of the key positions is image tile img_of(t)
+    uint32_t vtile_bytes;           // bytes between V tiles read as rows
     float cs, slope_l2;
+
+    __device__ __forceinline__ uint32_t img_of(int j0) const {
+        const int t = j0 / BK;
+        return (uint32_t)(t >= ns_img ? t - shift : t);
+    }
 
     __device__ __forceinline__ int j0_of(int t) const {
         return (t < ts_end ? t : tw_begin + (t - ts_end)) * BK;
@@ -414,13 +600,13 @@ struct TileCtx {
 template <int D>
 __device__ __forceinline__ void load_k(uint16_t *__restrict__ dst, const TileCtx &cx,
                                        const LaneOffsets<D> &lo, int j0) {
-    dma_tile<D>(dst, cx.rk, (uint32_t)(j0 / BK) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
+    dma_tile<D>(dst, cx.rk, cx.img_of(j0) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
 }
 template <int D, bool VF16>
 __device__ __forceinline__ void load_v(uint16_t *__restrict__ dst, const TileCtx &cx,
                                        const LaneOffsets<D> &lo, int j0) {
-    if (VF16) dma_tile<D>(dst, cx.rv, (uint32_t)(j0 / BK) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
-    else dma_tile<D>(dst, cx.rv, (uint32_t)j0 * cx.row_bytes, lo.dvraw, cx.wave);
+    if (VF16) dma_tile<D>(dst, cx.rv, cx.img_of(j0) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
+    else dma_tile<D>(dst, cx.rv, cx.img_of(j0) * cx.vtile_bytes, lo.dvraw, cx.wave);
 }
 
 // Step t of the software pipeline. On entry s_cur holds the prepared scores of tile t, K
@@ -481,6 +667,23 @@ __device__ __forceinline__ void plain_step(uint16_t *__restrict__ k_fill,
     }
 }
 
+// Rows of a sequence a chunked call cannot serve: NaN for this workgroup's query heads
+// h_first .. h_first + GP - 1, on the query tiles qt0, qt0 + QP * n_qtiles, ...
+template <int D, int GP>
+__device__ void nan_rows(const MfmaParams &p, const ChunkSeq &cs, int r_first, int QP,
+                         int64_t h_first) {
+    const int64_t stride = (int64_t)p.n_qtiles * QP;
+    for (int64_t r0 = r_first; r0 < cs.n; r0 += stride) {
+        const int rows = cs.n - r0 < QP ? (int)(cs.n - r0) : QP;
+        for (int e = threadIdx.x; e < rows * GP * D; e += blockDim.x) {
+            const int rr = e / (GP * D), hp = (e / D) % GP, c = e % D;
+            const int64_t off = ((cs.row0 + r0 + rr) * p.Hq + h_first + hp) * D + c;
+            if (p.out_bf16) static_cast<uint16_t *>(p.o)[off] = 0x7fc0;
+            else static_cast<float *>(p.o)[off] = qnan();
+        }
+    }
+}
+
 // Register budget: 4 wavefronts per SIMD at d = 64 (3 with four heads per workgroup, which
 // keeps more per-head state), 2 at d = 128.
 template <int D, int GP, int MODE, bool ALIBI, bool VF16>
@@ -511,8 +714,21 @@ void prefill_mfma_kernel(MfmaParams p) {
     const int qc = lane & 31, g = lane >> 5;
     const int hp = wave / WPH, pb = wave % WPH;
     const int64_t h = (int64_t)hkv * p.G + hg * GP + hp;
-    const int N = (int)p.N;
-    const int q0 = qt * QP;
+    // query rows: positions [qpos0, N) at rows qrow0 + (position - qpos0)
+    int qpos0 = 0, nq = (int)p.N, shift = 0, ns_img = 0;
+    int64_t qrow0 = (int64_t)b * p.N;
+    if (p.chunked) {
+        const ChunkSeq cs = chunk_seq(p.cg, b);
+        if (!cs.rows_ok) return;
+        if (!cs.valid) {
+            nan_rows<D, GP>(p, cs, qt * QP, QP, h - hp);
+            return;
+        }
+        if (qt * QP >= cs.n) return;
+        qpos0 = cs.p0; nq = cs.n; qrow0 = cs.row0; shift = cs.shift; ns_img = p.cg.ns_img;
+    }
+    const int N = qpos0 + nq;
+    const int q0 = qpos0 + qt * QP;
     const int qa = q0 + 32 * pb;                   // this wavefront's first query
     const int i = qa + qc;                         // this lane's query
     const int qe = (q0 + QP < N ? q0 + QP : N) - 1;
@@ -531,8 +747,11 @@ void prefill_mfma_kernel(MfmaParams p) {
         const int64_t imoff = ((int64_t)b * p.Hkv + hkv) * p.n_ktiles * T::IMG;
         const uint32_t imbytes = (uint32_t)p.n_ktiles * T::IMG_BYTES;
         cx.rk = make_rsrc(p.kimg + imoff, imbytes);
-        cx.rv = VF16 ? make_rsrc(p.vimg + imoff, imbytes) : make_rsrc(p.v + kvoff, p.kv_bytes);
+        cx.rv = (VF16 || p.chunked) ? make_rsrc(p.vimg + imoff, imbytes)
+                                    : make_rsrc(p.v + kvoff, p.kv_bytes);
         cx.row_bytes = p.row_bytes;
+        cx.ns_img = ns_img; cx.shift = shift;
+        cx.vtile_bytes = p.chunked ? (uint32_t)T::IMG_BYTES : (uint32_t)BK * p.row_bytes;
         cx.tid = tid; cx.wave = wave; cx.qa = qa; cx.qb = qa + 31 < N ? qa + 31 : N - 1;
         cx.i = i; cx.g = g; cx.w = p.w; cx.s = p.s; cx.N = N;
         cx.n_tiles = ts_end + (tw_end - tw_begin + 1);
@@ -559,13 +778,13 @@ void prefill_mfma_kernel(MfmaParams p) {
         const int slot = (wave * T::DMA_W + r) * 64 + lane;  // 16-byte slot of the tile image
         const int row = slot / T::C, c = (slot % T::C) ^ vswz<D>(row);
         lo.dimg[r] = (uint32_t)slot * 16;
-        lo.dvraw[r] = (uint32_t)row * p.row_bytes + c * 16;
+        lo.dvraw[r] = (uint32_t)row * (p.chunked ? (uint32_t)(2 * D) : p.row_bytes) + c * 16;
     }
 
     // ---- this lane's query fragment (B operand of S^T = K Q^T): rotated, float16
     f16x8_t qreg[KS];
     {
-        const uint16_t *qrow = p.q + (((int64_t)b * p.N + i) * p.Hq + h) * D;
+        const uint16_t *qrow = p.q + ((qrow0 + (i - qpos0)) * p.Hq + h) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0);
@@ -660,7 +879,7 @@ void prefill_mfma_kernel(MfmaParams p) {
                 const int iq = qa + qrow;
                 if (iq < N) {
                     const float4 x = *reinterpret_cast<const float4 *>(ol + qrow * T::OSTR + 4 * c4);
-                    const int64_t off = (((int64_t)b * p.N + iq) * p.Hq + h) * D + 4 * c4;
+                    const int64_t off = ((qrow0 + (iq - qpos0)) * p.Hq + h) * D + 4 * c4;
                     if (p.out_bf16)
                         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.o) + off) =
                             make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
@@ -751,7 +970,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
     const int64_t QP = 32 * (a.d == 128 ? Tile<128>::NW : Tile<64>::NW) / GP;
-    MfmaParams mp;
+    MfmaParams mp = {};  // chunked = 0: whole sequences, no chunk geometry
     mp.q = static_cast<const uint16_t *>(q);
     mp.k = static_cast<const uint16_t *>(k);
     mp.v = static_cast<const uint16_t *>(v);
@@ -772,7 +991,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.out_bf16 = a.out_dt == 1;
 
     {
-        PackParams pp;
+        PackParams pp = {};
         pp.k = mp.k; pp.v = mp.v;
         pp.kimg = static_cast<uint16_t *>(ws);
         pp.vimg = pl.vf16 ? static_cast<uint16_t *>(ws) + pl.img_bytes / 2 : nullptr;
@@ -792,6 +1011,158 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     if (GP == 4) return launch_gp<128, 4>(mp, nb, a.mode, alibi, st);
     if (GP == 2) return launch_gp<128, 2>(mp, nb, a.mode, alibi, st);
     return launch_gp<128, 1>(mp, nb, a.mode, alibi, st);
+}
+
+}  // namespace swa
+
+// ---------------------------------------------------------------------------------------
+// Chunked prefill over the ring cache: gather, banded attention, append.
+namespace swa {
+namespace {
+
+constexpr int64_t POS_LIMIT = int64_t(1) << 24;  // positions stay float-exact integers
+
+struct ChunkPlan {
+    int w_k, s_k;        // window and sinks clamped to the position range
+    int64_t ns_img;      // sink tiles at the front of each sequence's images
+    int64_t n_ktiles;    // image tiles per (sequence, kv head)
+    int64_t pos_limit;
+    size_t img_bytes;    // one full set of K (or V) images
+};
+
+ChunkPlan chunk_plan(const DecodeArgs &a, const CacheArgs &c, int64_t max_q) {
+    ChunkPlan pl;
+    pl.w_k = (int)(c.w < POS_LIMIT + BK ? c.w : POS_LIMIT + BK);
+    pl.s_k = (int)(c.s < POS_LIMIT + BK ? c.s : POS_LIMIT + BK);
+    pl.pos_limit = a.rope && a.rope_rows < POS_LIMIT ? a.rope_rows : POS_LIMIT;
+    pl.ns_img = (pl.s_k + BK - 1) / BK;
+    // window tiles a chunk can reach: fewer than (max_q + w - 1) / 64 + 2, and never more
+    // than the tiles of all admissible positions
+    const int64_t by_window = (max_q + pl.w_k + 62) / BK + 1;
+    const int64_t by_pos = (pl.pos_limit + BK - 1) / BK;
+    pl.n_ktiles = pl.ns_img + (by_window < by_pos ? by_window : by_pos);
+    pl.img_bytes = (size_t)(c.S * c.Hkv * pl.n_ktiles) * BK * (size_t)c.d * 2;
+    return pl;
+}
+
+int64_t chunk_qp(const CacheArgs &c, int64_t G) {
+    return 32 * (c.d == 128 ? Tile<128>::NW : Tile<64>::NW) / pack_of(G);
+}
+
+template <int D>
+hipError_t launch_gather(const GatherParams &gp, int nblocks, bool rot, bool vf16, hipStream_t st) {
+    if (rot) {
+        if (vf16) hipLaunchKernelGGL((chunk_gather_kernel<D, true, true>), dim3((unsigned)nblocks), dim3(256), 0, st, gp);
+        else hipLaunchKernelGGL((chunk_gather_kernel<D, true, false>), dim3((unsigned)nblocks), dim3(256), 0, st, gp);
+    } else {
+        if (vf16) hipLaunchKernelGGL((chunk_gather_kernel<D, false, true>), dim3((unsigned)nblocks), dim3(256), 0, st, gp);
+        else hipLaunchKernelGGL((chunk_gather_kernel<D, false, false>), dim3((unsigned)nblocks), dim3(256), 0, st, gp);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_chunk_supported(const DecodeArgs &a, const CacheArgs &c, int64_t T, int64_t max_q) {
+    if (c.dt != 1 || (c.d != 64 && c.d != 128)) return false;
+    if (c.S == 0 || T == 0 || max_q == 0) return true;
+    if (max_q >= POS_LIMIT) return false;
+    const ChunkPlan pl = chunk_plan(a, c, max_q);
+    const int64_t G = a.Hq / c.Hkv;
+    const int64_t QP = chunk_qp(c, G);
+    const int64_t nb = c.S * c.Hkv * (G / pack_of(G)) * ((max_q + QP - 1) / QP);
+    const int64_t ngather = c.S * pl.n_ktiles * ((c.Hkv + PACK_HG - 1) / PACK_HG);
+    const int64_t nappend = c.S * ((max_q + BK - 1) / BK);
+    const int64_t img_slice = pl.n_ktiles * BK * c.d * 2;
+    const int64_t table = a.rope ? a.rope_rows * c.d * 4 : 0;
+    return nb <= 0x7fffffff && ngather <= 0x7fffffff && nappend <= 0x7fffffff &&
+           img_slice < (int64_t(1) << 31) && table < (int64_t(1) << 31);
+}
+
+size_t prefill_chunk_workspace_bytes(const DecodeArgs &a, const CacheArgs &c, int64_t T,
+                                     int64_t max_q) {
+    if (c.S == 0 || T == 0 || max_q == 0) return 0;
+    return 2 * chunk_plan(a, c, max_q).img_bytes;
+}
+
+hipError_t launch_prefill_chunk(const DecodeArgs &a, const CacheArgs &c, const void *q,
+                                const void *k_new, const void *v_new, const int32_t *cu,
+                                const int32_t *pos0, int64_t T, int64_t max_q, void *o,
+                                void *ws, hipStream_t st) {
+    if (c.S == 0 || T == 0 || max_q == 0) return hipSuccess;
+    const ChunkPlan pl = chunk_plan(a, c, max_q);
+    const int64_t G = a.Hq / c.Hkv;
+    const int GP = pack_of(G);
+    const int64_t QP = chunk_qp(c, G);
+    const bool vf16 = a.mode == 1;
+    uint16_t *kimg = static_cast<uint16_t *>(ws);
+    uint16_t *vimg = kimg + pl.img_bytes / 2;
+
+    ChunkGeom cg = {};
+    cg.cu = cu; cg.pos0 = pos0; cg.T = T; cg.max_q = (int)max_q;
+    cg.pos_limit = (int)pl.pos_limit; cg.w = pl.w_k; cg.ns_img = (int)pl.ns_img;
+    {
+        GatherParams gp = {};
+        gp.cg = cg;
+        gp.k_new = static_cast<const uint16_t *>(k_new);
+        gp.v_new = static_cast<const uint16_t *>(v_new);
+        gp.k_ring = static_cast<const uint16_t *>(c.k_ring);
+        gp.v_ring = static_cast<const uint16_t *>(c.v_ring);
+        gp.k_sink = static_cast<const uint16_t *>(c.k_sink);
+        gp.v_sink = static_cast<const uint16_t *>(c.v_sink);
+        gp.kimg = kimg; gp.vimg = vimg;
+        gp.rope = a.rope;
+        gp.Hkv = c.Hkv; gp.w_ring = c.w; gp.s = c.s;
+        gp.n_ktiles = (int)pl.n_ktiles;
+        const int nb = (int)(c.S * pl.n_ktiles * ((c.Hkv + PACK_HG - 1) / PACK_HG));
+        const hipError_t e = c.d == 64 ? launch_gather<64>(gp, nb, a.rope != nullptr, vf16, st)
+                                       : launch_gather<128>(gp, nb, a.rope != nullptr, vf16, st);
+        if (e != hipSuccess) return e;
+    }
+    {
+        MfmaParams mp = {};
+        mp.q = static_cast<const uint16_t *>(q);
+        mp.kimg = kimg; mp.vimg = vimg;
+        mp.o = o;
+        mp.slopes = a.slopes;
+        mp.rope = a.rope;
+        mp.N = 0; mp.Hq = a.Hq; mp.Hkv = c.Hkv; mp.G = G;
+        mp.n_qtiles = (int)((max_q + QP - 1) / QP);
+        mp.n_hgroups = (int)(G / GP);
+        mp.n_ktiles = (int)pl.n_ktiles;
+        mp.w = pl.w_k; mp.s = pl.s_k;
+        mp.cs = a.scale * LOG2E;
+        mp.out_bf16 = a.out_dt == 1;
+        mp.chunked = 1;
+        mp.cg = cg;
+        const int nb = (int)(c.S * c.Hkv * mp.n_hgroups * mp.n_qtiles);
+        const bool alibi = a.slopes != nullptr;
+        hipError_t e;
+        if (c.d == 64)
+            e = GP == 4 ? launch_gp<64, 4>(mp, nb, a.mode, alibi, st)
+              : GP == 2 ? launch_gp<64, 2>(mp, nb, a.mode, alibi, st)
+                        : launch_gp<64, 1>(mp, nb, a.mode, alibi, st);
+        else
+            e = GP == 4 ? launch_gp<128, 4>(mp, nb, a.mode, alibi, st)
+              : GP == 2 ? launch_gp<128, 2>(mp, nb, a.mode, alibi, st)
+                        : launch_gp<128, 1>(mp, nb, a.mode, alibi, st);
+        if (e != hipSuccess) return e;
+    }
+    ChunkAppendParams ap = {};
+    ap.cg = cg;
+    ap.k_new = static_cast<const uint16_t *>(k_new);
+    ap.v_new = static_cast<const uint16_t *>(v_new);
+    ap.k_ring = static_cast<uint16_t *>(c.k_ring);
+    ap.v_ring = static_cast<uint16_t *>(c.v_ring);
+    ap.k_sink = static_cast<uint16_t *>(c.k_sink);
+    ap.v_sink = static_cast<uint16_t *>(c.v_sink);
+    ap.rope = a.rope;
+    ap.Hkv = c.Hkv; ap.w_ring = c.w; ap.s = c.s;
+    ap.n_rtiles = (int)((max_q + BK - 1) / BK);
+    const int nb = (int)(c.S * ap.n_rtiles);
+    if (c.d == 64) hipLaunchKernelGGL(chunk_append_kernel<64>, dim3((unsigned)nb), dim3(256), 0, st, ap);
+    else hipLaunchKernelGGL(chunk_append_kernel<128>, dim3((unsigned)nb), dim3(256), 0, st, ap);
+    return hipGetLastError();
 }
 
 }  // namespace swa

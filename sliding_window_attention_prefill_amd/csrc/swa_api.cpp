@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <initializer_list>
 
 #include "../../include/swa.h"
 #include "swa_kernels.hpp"
@@ -31,7 +32,7 @@ float resolve_scale(float scale, int64_t d) {
 
 extern "C" {
 
-int swa_version(void) { return 200; }
+int swa_version(void) { return 300; }
 
 const char *swa_status_string(swa_status s) {
     switch (s) {
@@ -199,6 +200,54 @@ swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, con
                                                    workspace_bytes, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return SWA_ERR_UNSUPPORTED;
     return hip_status(e);
+}
+
+static bool aligned16(std::initializer_list<const void *> ptrs) {
+    uintptr_t bits = 0;
+    for (const void *x : ptrs) bits |= reinterpret_cast<uintptr_t>(x);
+    return (bits & 15) == 0;
+}
+
+static swa_status check_chunk(const swa_decode_params *p, const swa_cache *c, int64_t total_rows,
+                              int64_t max_seqlen) {
+    swa_status st = check_decode(p, c);
+    if (st != SWA_OK) return st;
+    if (total_rows < 0 || max_seqlen < 0) return SWA_ERR_INVALID_ARGUMENT;
+    if (total_rows > 0x7fffffff) return SWA_ERR_UNSUPPORTED;  // rows are int32 offsets
+    if (!swa::prefill_chunk_supported(decode_args(p, c->d), cache_args(c), total_rows, max_seqlen))
+        return SWA_ERR_UNSUPPORTED;
+    return SWA_OK;
+}
+
+size_t swa_prefill_chunk_workspace_bytes(const swa_decode_params *p, const swa_cache *c,
+                                         int64_t total_rows, int64_t max_seqlen) {
+    if (check_chunk(p, c, total_rows, max_seqlen) != SWA_OK) return 0;
+    return swa::prefill_chunk_workspace_bytes(decode_args(p, c->d), cache_args(c), total_rows,
+                                              max_seqlen);
+}
+
+swa_status swa_prefill_chunk(const swa_decode_params *p, const swa_cache *c, const void *q,
+                             const void *k_new, const void *v_new, const int32_t *cu_seqlens,
+                             const int32_t *pos0, int64_t total_rows, int64_t max_seqlen,
+                             void *o, void *workspace, size_t workspace_bytes, void *stream) {
+    swa_status st = check_chunk(p, c, total_rows, max_seqlen);
+    if (st != SWA_OK) return st;
+    if (c->num_seqs > 0 && (!cu_seqlens || !pos0)) return SWA_ERR_INVALID_ARGUMENT;
+    if (c->num_seqs > 0 && total_rows > 0 && (!q || !k_new || !v_new || !o))
+        return SWA_ERR_INVALID_ARGUMENT;
+    // 16-byte vector moves on every tensor
+    if (!aligned16({q, k_new, v_new, o, c->k_ring, c->v_ring, c->k_sink, c->v_sink,
+                    p->rope_table}))
+        return SWA_ERR_UNSUPPORTED;
+    const swa::DecodeArgs a = decode_args(p, c->d);
+    const swa::CacheArgs ca = cache_args(c);
+    const size_t need = swa::prefill_chunk_workspace_bytes(a, ca, total_rows, max_seqlen);
+    if (need > 0 && (!workspace || workspace_bytes < need ||
+                     (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
+        return SWA_ERR_INVALID_ARGUMENT;
+    return hip_status(swa::launch_prefill_chunk(a, ca, q, k_new, v_new, cu_seqlens, pos0,
+                                                total_rows, max_seqlen, o, workspace,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

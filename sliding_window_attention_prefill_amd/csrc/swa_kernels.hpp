@@ -59,6 +59,18 @@ size_t decode_workspace_bytes(const DecodeArgs &a, const CacheArgs &c);
 hipError_t launch_decode(const DecodeArgs &a, const CacheArgs &c, const void *q,
                          const int32_t *q_pos, void *o, void *ws, size_t ws_bytes,
                          hipStream_t st);
+// Chunked prefill over the ring cache (packed rows, cu/pos0 per sequence): a gather
+// pre-pass builds float16 tile images from sinks, ring and chunk, the matrix-core kernel
+// attends, then the chunk is appended. bf16 caches with d in {64, 128} only; ws must hold
+// prefill_chunk_workspace_bytes bytes, 16-byte aligned.
+bool prefill_chunk_supported(const DecodeArgs &a, const CacheArgs &c, int64_t T, int64_t max_q);
+size_t prefill_chunk_workspace_bytes(const DecodeArgs &a, const CacheArgs &c, int64_t T,
+                                     int64_t max_q);
+hipError_t launch_prefill_chunk(const DecodeArgs &a, const CacheArgs &c, const void *q,
+                                const void *k_new, const void *v_new, const int32_t *cu,
+                                const int32_t *pos0, int64_t T, int64_t max_q, void *o,
+                                void *ws, hipStream_t st);
+
 // Append one token per sequence at q_pos, then decode (one launch where possible).
 hipError_t launch_decode_append(const DecodeArgs &a, const CacheArgs &c, const void *q,
                                 const void *k_new, const void *v_new, const int32_t *q_pos,

@@ -162,3 +162,51 @@ def test_decode_workspace_bytes_split_kv(lib):
     assert wsb(1, 8, 4096, 0, 128, 32) == 4 * 1 * 8 * 8 * 4 * (128 + 2)
     # at most 64 ranges
     assert wsb(1, 1, 1 << 20, 0, 64, 2) == 4 * 1 * 1 * 64 * 2 * (64 + 2)
+
+
+def _dparams(H_q=4, mode=1, rope_table=None, rope_rows=0):
+    return swa.DecodeParams(H_q, mode, 0, 0.0, 0, None, rope_table, rope_rows)
+
+
+def test_prefill_chunk_workspace_bytes(lib):
+    """K and V tile images per (sequence, kv head): the sink tiles, then the window tiles a
+    chunk of max_seqlen rows can reach, (max_seqlen + w + 62) // 64 + 1 of them, or fewer
+    when the rotation table bounds the positions."""
+    def wsb(S=2, H_kv=2, w=8, s=2, d=64, T=10, max_q=5, **kw):
+        c = _cache(num_seqs=S, H_kv=H_kv, w=w, s=s, d=d)
+        p = _dparams(**kw)
+        return lib.swa_prefill_chunk_workspace_bytes(ctypes.byref(p), ctypes.byref(c), T, max_q)
+    tiles = lambda s, w, q: (s + 63) // 64 + (q + w + 62) // 64 + 1
+    assert wsb() == 2 * 2 * 2 * tiles(2, 8, 5) * 64 * 64 * 2
+    assert wsb(w=4096, s=0, d=128, max_q=2048, S=3, H_kv=8, H_q=32) == \
+        2 * 3 * 8 * tiles(0, 4096, 2048) * 64 * 128 * 2
+    # a table of 1000 positions: at most 16 window tiles
+    assert wsb(w=100000, s=4, max_q=512, rope_table=0x2000, rope_rows=1000) == \
+        2 * 2 * 2 * (1 + 16) * 64 * 64 * 2
+    assert wsb(T=0) == 0 and wsb(max_q=0) == 0 and wsb(S=0) == 0
+    assert wsb(d=96) == 0                      # unsupported head size
+    c = _cache(dtype=0)                        # float32 cache: unsupported
+    assert lib.swa_prefill_chunk_workspace_bytes(ctypes.byref(_dparams()), ctypes.byref(c),
+                                                 10, 5) == 0
+
+
+def test_prefill_chunk_rejects_bad_arguments(lib):
+    c = _cache()
+    p = _dparams()
+
+    def call(c=c, p=p, q=DUMMY, cu=DUMMY, pos=DUMMY, T=10, max_q=5, ws=None, ws_bytes=0):
+        return lib.swa_prefill_chunk(ctypes.byref(p), ctypes.byref(c), q, DUMMY, DUMMY, cu, pos,
+                                     T, max_q, DUMMY, ws, ws_bytes, None)
+    assert call(T=-1) == 1
+    assert call(max_q=-1) == 1
+    assert call(cu=None) == 1
+    assert call(pos=None) == 1
+    assert call(q=None) == 1
+    assert call(p=_dparams(H_q=3)) == 1                       # H_q % H_kv != 0
+    assert call(c=_cache(dtype=0)) == 2                       # float32 cache
+    assert call(c=_cache(d=96)) == 2                          # head size 96
+    assert call(q=ctypes.c_void_p(0x1008)) == 2               # 16-byte alignment
+    assert call() == 1                                        # no workspace
+    need = lib.swa_prefill_chunk_workspace_bytes(ctypes.byref(p), ctypes.byref(c), 10, 5)
+    assert call(ws=DUMMY, ws_bytes=need - 16) == 1            # short workspace
+    assert call(ws=ctypes.c_void_p(0x1004), ws_bytes=need) == 1  # misaligned workspace

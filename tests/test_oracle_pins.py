@@ -447,3 +447,17 @@ def test_chunk_without_history_is_rejected():
     with pytest.raises(ValueError, match="does not hold"):
         ring.chunk(np.ones((2, 1, 2)), np.ones((2, 1, 2)), np.ones((2, 1, 2)), [0, 2], [5],
                    H_q=1, mode=oracle.SOFTMAX)
+
+
+def test_chunk_rows_subset_equals_full():
+    """Computing a subset of packed rows gives those rows of the full result."""
+    S, Hq, Hkv, d, w, s, theta = 2, 2, 1, 8, 5, 1, 1e4
+    T = 9
+    q, k, v = _rand((T, Hq, d), 50), _rand((T, Hkv, d), 51), _rand((T, Hkv, d), 52)
+    cu, pos0 = np.array([0, 4, 9]), np.array([0, 0])
+    full = oracle.Ring(S, Hkv, w, s, d).chunk(q, k, v, cu, pos0, H_q=Hq, mode=oracle.SOFTMAX,
+                                             rope_theta=theta)
+    rows = [8, 0, 5, 3]
+    part = oracle.Ring(S, Hkv, w, s, d).chunk(q, k, v, cu, pos0, H_q=Hq, mode=oracle.SOFTMAX,
+                                             rope_theta=theta, rows=rows)
+    np.testing.assert_array_equal(part, full[rows])
