@@ -14,6 +14,9 @@ The JSON line also carries:
                 resident in the last-level cache (as specified) and, as decode_cold, with 18
                 cache copies in rotation so that the rings come from HBM; decode_long adds
                 two long-window decode workloads whose caches live in HBM;
+  chunk_prefill chunked prefill over the ring cache (8 prompts x 2048 rows per step at the
+                Mistral-7B layer shape, histories past the 4,096-token window), in-window
+                TFLOP/s of whole swa_prefill_chunk calls;
   cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -187,6 +190,57 @@ def bench_decode(cfg, out_dtype, copies=1):
     }
 
 
+def bench_chunk(cfg, out_dtype):
+    """Chunked prefill over the ring cache: step t prefills rows [hist + t * chunk, hist +
+    (t + 1) * chunk) of every sequence (gather, attention, append in one swa_prefill_chunk
+    call), so each step reads the history the previous step appended. HIP events around
+    each call on its stream; one untimed call on a separate copy of the cache first."""
+    import torch
+    import sliding_window_attention_prefill_amd as swa
+    import swa_workloads as wl
+
+    st = wl.chunk_inputs(cfg, device="cuda")
+    S, C, T = cfg.num_seqs, cfg.chunk, cfg.num_seqs * cfg.chunk
+    clone = lambda t: None if t is None else t.clone()
+    make = lambda: swa.SwaCache(clone(st.k_ring), clone(st.v_ring), clone(st.k_sink),
+                                clone(st.v_sink))
+    table = swa.swa_rope_table(cfg.hist_hi + (cfg.steps + 1) * C + 1, cfg.d, cfg.rope_theta)
+    cu = (torch.arange(S + 1, dtype=torch.int32, device="cuda") * C).contiguous()
+    pos = [(st.hist + t * C).to(torch.int32).to("cuda") for t in range(cfg.steps)]
+    out = torch.empty((T, cfg.H_q, cfg.d), dtype=out_dtype, device="cuda")
+    warm = make()
+    need = swa.swa_prefill_chunk_workspace_bytes(warm, cfg.H_q, T, C, mode=cfg.mode,
+                                                 rope_table=table)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def call(cache, p):
+        swa.swa_prefill_chunk(st.q, st.k, st.v, cu, p, cache, max_seqlen=C, mode=cfg.mode,
+                              rope_table=table, out=out, workspace=ws, stream=stream)
+
+    call(warm, pos[0])
+    cache = make()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(cfg.steps)]
+    for t in range(cfg.steps):
+        ev[t][0].record(stream)
+        call(cache, pos[t])
+        ev[t][1].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / cfg.steps
+    # every row's key set is the whole window (histories start past w + s)
+    flops = 4.0 * cfg.H_q * cfg.d * T * (cfg.w + cfg.s)
+    tf = flops / (ms / 1e3) / 1e12
+    return {
+        "workload": cfg.name, "sequences": S, "rows_per_sequence": C, "steps": cfg.steps,
+        "ms_per_step": round(ms, 4), "rows_per_s": round(T / (ms / 1e3), 1),
+        "in_window_flops_per_step": flops, "TFLOP_s": round(tf, 2),
+        "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+        "note": "one call per step: gather pre-pass, matrix-core attention, append",
+    }
+
+
 def cpu_baseline(cfg, sample_batches: int):
     """The float64 oracle on the first `sample_batches` sequences of the batch (all heads,
     all rows), timed on the host; reported in the metric's unit."""
@@ -216,6 +270,7 @@ def main():
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes three times (the "
@@ -265,6 +320,8 @@ def main():
         result["decode_cold"] = bench_decode(wl.C4, torch.float32, copies=18)
         result["decode_long"] = [bench_decode(c, torch.float32)
                                  for c in (wl.DECODE_W4096, wl.DECODE_W32K)]
+    if not args.no_chunk:
+        result["chunk_prefill"] = bench_chunk(wl.CHUNK_W4096, torch.float32)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_batches)
     print(json.dumps(result), flush=True)

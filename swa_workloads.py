@@ -114,6 +114,37 @@ DECODE_W32K = DecodeConfig("global_window_decode_bf16_S8_Hq32_Hkv8_d128_w32768",
                            rope_theta=1e6, slopes=None, len_lo=40000, len_hi=60000, steps=32,
                            seed=7)
 
+
+@dataclass(frozen=True)
+class ChunkConfig:
+    """Chunked prefill over the ring cache: every step gives each of num_seqs sequences its
+    next `chunk` prompt rows; the cache already holds a history of hist_lo..hist_hi tokens
+    (synthetic rotated keys and values, as for decode)."""
+    name: str
+    dtype: str
+    num_seqs: int
+    H_q: int
+    H_kv: int
+    d: int
+    w: int
+    s: int
+    mode: int
+    rope_theta: float
+    slopes: Optional[tuple]
+    hist_lo: int
+    hist_hi: int
+    chunk: int
+    steps: int
+    seed: int = 0
+
+
+# Serving-style chunked prefill at the C3 layer shape: 8 prompts, 2048 rows each per step,
+# histories past the 4,096-token window (measurement only).
+CHUNK_W4096 = ChunkConfig("mistral7b_chunked_prefill_bf16_S8_chunk2048_Hq32_Hkv8_d128_w4096",
+                          "bf16", num_seqs=8, H_q=32, H_kv=8, d=128, w=4096, s=0, mode=SOFTMAX,
+                          rope_theta=1e6, slopes=None, hist_lo=4096, hist_hi=32768, chunk=2048,
+                          steps=8, seed=8)
+
 PREFILL_CONFIGS = {c.name: c for c in (C1, C2, C3, C5)}
 
 
@@ -211,3 +242,34 @@ def sample_rows(n: int, count: int, seed: int, must=(0,)) -> list:
                 break
             picked.add(int(e))
     return sorted(picked)
+
+
+@dataclass
+class ChunkState:
+    """hist [S] int32: tokens already in each sequence's cache; k_ring/v_ring [S, H_kv, w, d]
+    and k_sink/v_sink [S, H_kv, s, d]: synthetic already-rotated cache contents; q [S*chunk,
+    H_q, d], k/v [S*chunk, H_kv, d]: one packed chunk (keys not rotated), reused by every
+    step at that step's positions."""
+    hist: torch.Tensor
+    k_ring: torch.Tensor
+    v_ring: torch.Tensor
+    k_sink: Optional[torch.Tensor]
+    v_sink: Optional[torch.Tensor]
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+
+
+def chunk_inputs(cfg: ChunkConfig, device="cpu") -> ChunkState:
+    g = _gen(cfg.seed, device)
+    dt = torch_dtype(cfg.dtype)
+    S, T = cfg.num_seqs, cfg.num_seqs * cfg.chunk
+    hist = torch.randint(cfg.hist_lo, cfg.hist_hi + 1, (S,), generator=g, device=device,
+                         dtype=torch.int64).to(torch.int32)
+    rn = lambda *shape: torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dt)
+    k_ring, v_ring = rn(S, cfg.H_kv, cfg.w, cfg.d), rn(S, cfg.H_kv, cfg.w, cfg.d)
+    k_sink = rn(S, cfg.H_kv, cfg.s, cfg.d) if cfg.s > 0 else None
+    v_sink = rn(S, cfg.H_kv, cfg.s, cfg.d) if cfg.s > 0 else None
+    q = rn(T, cfg.H_q, cfg.d)
+    k, v = rn(T, cfg.H_kv, cfg.d), rn(T, cfg.H_kv, cfg.d)
+    return ChunkState(hist, k_ring, v_ring, k_sink, v_sink, q, k, v)
