@@ -5,7 +5,7 @@ CPU-baseline leg. The product path never imports it, and it imports nothing of t
 product (no kernels, headers, tables or helpers are shared).
 
 Two independent implementations of the same definition, both in float64:
-  * `prefill`, `Ring.decode`, `Ring.append`, `Ring.chunk`: a plain C windowed loop
+  * `prefill`, `backward`, `Ring.decode`, `Ring.append`, `Ring.chunk`: a plain C windowed loop
     (swa_oracle.c), one query row at a time, OpenMP across rows;
   * `dense.prefill_dense`: numpy, a full [N, N] score matrix masked with the boolean band
     mask built as in the Sliding Window Attention glossary's example.
@@ -62,6 +62,9 @@ def bind(path: str):
                                      dbl, dp, dp, dp, ip, ip, i64, dp, dp, ip, dp, dp, ip, i64,
                                      dp]
     lib.swa_oracle_chunk.restype = ctypes.c_int
+    lib.swa_oracle_backward.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int, dbl,
+                                        dp, dbl, dp, dp, dp, dp, dp, dp, dp]
+    lib.swa_oracle_backward.restype = ctypes.c_int
     lib.swa_oracle_ring_fill_positions.argtypes = [i64, i64, ip]
     lib.swa_oracle_ring_fill_positions.restype = None
     lib.swa_oracle_threads.argtypes = []
@@ -131,6 +134,24 @@ def prefill(q, k, v, *, w: int, s: int = 0, mode: int = SIGMOID, scale: float = 
     if rc != 0:
         raise ValueError("oracle prefill rejected its arguments")
     return out
+
+
+def backward(q, k, v, dout, *, w: int, s: int = 0, mode: int = SIGMOID, scale: float = 0.0,
+             slopes=None, rope_theta: float = 0.0):
+    """float64 gradients (dq, dk, dv) of prefill for the output gradient dout [B,N,H_q,d]
+    (swa_oracle_backward)."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, N, Hkv, d) and v.shape == k.shape and g.shape == q.shape
+    sl = None if slopes is None else _f64(slopes)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    rc = _load().swa_oracle_backward(B, Hq, Hkv, N, d, w, s, mode, float(scale), _ptr(sl),
+                                     float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments")
+    return dq, dk, dv
 
 
 class Ring:

@@ -404,3 +404,130 @@ int swa_oracle_chunk(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, i
     }
     return status;
 }
+
+/*
+ * Backward pass of prefill (the gradients SWAT training needs; SWAT page, "Putting It
+ * Together": the forward is differentiated as written). Given dout = dL/do, for every
+ * (b, h, i) and j in K(i), with x_ij, p_ij as in the forward and q~ = R(i) q, k~ = R(j) k:
+ *   dP_ij = dout_i . v_j
+ *   dX_ij = dP_ij * p_ij * (1 - p_ij)                 sigmoid (the logistic derivative)
+ *         = p_ij * (dP_ij - sum_{j'} p_ij' dP_ij')     softmax (the row Jacobian)
+ *   dv_j += p_ij dout_i,  dq~_i += scale dX_ij k~_j,  dk~_j += scale dX_ij q~_i
+ * and dq_i = R(i)^T dq~_i, dk_j = R(j)^T dk~_j (the rotation is orthogonal; its transpose
+ * rotates by the opposite angle). Key and value gradients sum over the query heads of their
+ * group. The slopes are fixed (no gradient). Layouts as in swa_oracle_prefill; dq like q,
+ * dk/dv like k. Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int swa_oracle_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
+                        int64_t s, int mode, double scale, const double *slopes, double theta,
+                        const double *q, const double *k, const double *v, const double *dout,
+                        double *dq, double *dk, double *dv) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || N < 0 || d <= 0 || w < 1 || s < 0)
+        return -1;
+    if (theta > 0.0 && d % 2 != 0) return -1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    int64_t half = d / 2, group = Hq / Hkv;
+    double *cs = NULL, *sn = NULL;
+    if (theta > 0.0 && N > 0) {
+        cs = (double *)malloc(sizeof(double) * (size_t)(N * half));
+        sn = (double *)malloc(sizeof(double) * (size_t)(N * half));
+        if (!cs || !sn) { free(cs); free(sn); return -1; }
+        rope_table(N, d, theta, cs, sn);
+    }
+    memset(dq, 0, sizeof(double) * (size_t)(B * N * Hq * d));
+    memset(dk, 0, sizeof(double) * (size_t)(B * N * Hkv * d));
+    memset(dv, 0, sizeof(double) * (size_t)(B * N * Hkv * d));
+    int fail = 0;
+
+    /* one (batch, kv head) slice per task: its key and value gradients have one writer */
+#pragma omp parallel
+    {
+        double *qt = (double *)malloc(sizeof(double) * (size_t)d);
+        double *x = (double *)malloc(sizeof(double) * (size_t)(w + s + 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(w + s + 1));
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(w + s + 1));
+        double *kr = (double *)malloc(sizeof(double) * (size_t)((N > 0 ? N : 1) * d));
+        double *dkr = (double *)malloc(sizeof(double) * (size_t)((N > 0 ? N : 1) * d));
+        double *dqr = (double *)malloc(sizeof(double) * (size_t)d);
+        if (!qt || !x || !dp || !key || !kr || !dkr || !dqr) {
+#pragma omp atomic write
+            fail = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t bh = 0; bh < B * Hkv; ++bh) {
+                int64_t b = bh / Hkv, hk = bh % Hkv;
+                /* rotated keys of this slice, and their gradients in the rotated frame */
+                for (int64_t j = 0; j < N; ++j) {
+                    const double *kj = k + ((b * N + j) * Hkv + hk) * d;
+                    if (cs) rotate(kj, kr + j * d, d, cs + j * half, sn + j * half);
+                    else memcpy(kr + j * d, kj, sizeof(double) * (size_t)d);
+                }
+                memset(dkr, 0, sizeof(double) * (size_t)(N * d));
+                for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
+                    for (int64_t i = 0; i < N; ++i) {
+                        const double *qi = q + ((b * N + i) * Hq + h) * d;
+                        const double *gi = dout + ((b * N + i) * Hq + h) * d;
+                        if (cs) rotate(qi, qt, d, cs + i * half, sn + i * half);
+                        else memcpy(qt, qi, sizeof(double) * (size_t)d);
+                        int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;
+                        int64_t n = 0;
+                        for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
+                        for (int64_t j = lo; j <= i; ++j) key[n++] = j;
+                        for (int64_t e = 0; e < n; ++e) {
+                            int64_t j = key[e];
+                            double bias = slopes ? slopes[h] * (double)(i - j) : 0.0;
+                            x[e] = scale * dot(qt, kr + j * d, d) + bias;
+                            dp[e] = dot(gi, v + ((b * N + j) * Hkv + hk) * d, d);
+                        }
+                        weights(x, n, mode);   /* x now holds p */
+                        double rowsum = 0.0;
+                        if (mode == ORACLE_SOFTMAX)
+                            for (int64_t e = 0; e < n; ++e) rowsum += x[e] * dp[e];
+                        for (int64_t c = 0; c < d; ++c) dqr[c] = 0.0;
+                        for (int64_t e = 0; e < n; ++e) {
+                            int64_t j = key[e];
+                            double p = x[e];
+                            double dx = mode == ORACLE_SIGMOID ? dp[e] * p * (1.0 - p)
+                                                               : p * (dp[e] - rowsum);
+                            double *dvj = dv + ((b * N + j) * Hkv + hk) * d;
+                            for (int64_t c = 0; c < d; ++c) {
+                                dvj[c] += p * gi[c];
+                                dqr[c] += scale * dx * kr[j * d + c];
+                                dkr[j * d + c] += scale * dx * qt[c];
+                            }
+                        }
+                        double *dqi = dq + ((b * N + i) * Hq + h) * d;
+                        if (cs) {
+                            /* R^T: rotation by the opposite angle */
+                            for (int64_t t = 0; t < half; ++t) {
+                                double a = dqr[2 * t], bb = dqr[2 * t + 1];
+                                double c = cs[i * half + t], sv = sn[i * half + t];
+                                dqi[2 * t] = a * c + bb * sv;
+                                dqi[2 * t + 1] = -a * sv + bb * c;
+                            }
+                        } else {
+                            memcpy(dqi, dqr, sizeof(double) * (size_t)d);
+                        }
+                    }
+                }
+                for (int64_t j = 0; j < N; ++j) {
+                    double *dkj = dk + ((b * N + j) * Hkv + hk) * d;
+                    const double *g = dkr + j * d;
+                    if (cs) {
+                        for (int64_t t = 0; t < half; ++t) {
+                            double a = g[2 * t], bb = g[2 * t + 1];
+                            double c = cs[j * half + t], sv = sn[j * half + t];
+                            dkj[2 * t] = a * c + bb * sv;
+                            dkj[2 * t + 1] = -a * sv + bb * c;
+                        }
+                    } else {
+                        memcpy(dkj, g, sizeof(double) * (size_t)d);
+                    }
+                }
+            }
+        }
+        free(qt); free(x); free(dp); free(key); free(kr); free(dkr); free(dqr);
+    }
+    free(cs); free(sn);
+    return fail ? -1 : 0;
+}

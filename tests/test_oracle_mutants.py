@@ -1,7 +1,7 @@
 """Planted mistakes: each test compiles a copy of the C oracle with one plausible slip and
 checks that the pin suite rejects it. This shows the pins constrain every part of the
 definition (selection, sinks, bias sign, rotation, frequency, weights, scale, head map,
-ring slot, chunk offsets), not only the parts a random-input comparison would notice. CPU only."""
+ring slot, chunk offsets, gradients), not only the parts a random-input comparison would notice. CPU only."""
 import os
 import subprocess
 
@@ -36,6 +36,11 @@ MUTANTS = [
     ("chunk_key_rotation", "rotate_direct(kn, kt, d, j, theta);",
      "rotate_direct(kn, kt, d, p0, theta);"),
     ("chunk_boundary", "if (j >= p0) {", "if (j > p0) {"),
+    ("bwd_sigmoid_derivative", "dp[e] * p * (1.0 - p)", "dp[e] * p"),
+    ("bwd_softmax_row_term", "p * (dp[e] - rowsum)", "p * (dp[e] + rowsum)"),
+    ("bwd_inverse_rotation", "dqi[2 * t] = a * c + bb * sv;", "dqi[2 * t] = a * c - bb * sv;"),
+    ("bwd_scale", "dqr[c] += scale * dx * kr[j * d + c];", "dqr[c] += dx * kr[j * d + c];"),
+    ("bwd_value_gradient", "dvj[c] += p * gi[c];", "dvj[c] += dx * gi[c];"),
 ]
 
 PIN_TESTS = [
@@ -55,6 +60,9 @@ PIN_TESTS = [
     (pins.test_append_writes_position_mod_w, dict(w=3)),
     (pins.test_decode_equals_prefill_row_by_row, dict(mode=oracle.SIGMOID, w=5, s=2)),
     (pins.test_chunked_prefill_equals_whole_prefill, dict(mode=oracle.SOFTMAX, w=6, s=2)),
+    (pins.test_backward_matches_finite_differences,
+     dict(mode=oracle.SOFTMAX, w=4, s=2, theta=1e4, alibi=True)),
+    (pins.test_backward_window_of_one_closed_form, {}),
 ]
 
 

@@ -461,3 +461,82 @@ def test_chunk_rows_subset_equals_full():
     part = oracle.Ring(S, Hkv, w, s, d).chunk(q, k, v, cu, pos0, H_q=Hq, mode=oracle.SOFTMAX,
                                              rope_theta=theta, rows=rows)
     np.testing.assert_array_equal(part, full[rows])
+
+
+# ----------------------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("mode", [oracle.SIGMOID, oracle.SOFTMAX])
+@pytest.mark.parametrize("w,s,theta,alibi", [(3, 0, 0.0, False), (4, 2, 1e4, True),
+                                             (20, 0, 1e4, True), (1, 1, 1e2, False)])
+def test_backward_matches_finite_differences(mode, w, s, theta, alibi):
+    """The gradients of L = sum(dout * o) equal central differences of the (pinned) forward
+    oracle, element by element, for q, k and v, with grouped heads, sinks, bias and rotation."""
+    B, N, Hq, Hkv, d = 1, 9, 2, 1, 4
+    q, k, v = _rand((B, N, Hq, d), 60), _rand((B, N, Hkv, d), 61), _rand((B, N, Hkv, d), 62)
+    g = _rand((B, N, Hq, d), 63)
+    slopes = [-0.4, 0.3] if alibi else None
+    kw = dict(w=w, s=s, mode=mode, slopes=slopes, rope_theta=theta)
+    dq, dk, dv = oracle.backward(q, k, v, g, **kw)
+    loss = lambda q_, k_, v_: float(np.sum(g * oracle.prefill(q_, k_, v_, **kw)))
+    eps = 1e-5
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if n == name else y for n, y in (("q", q), ("k", k), ("v", v))]
+            args_m = [xm if n == name else y for n, y in (("q", q), ("k", k), ("v", v))]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("mode", [oracle.SIGMOID, oracle.SOFTMAX])
+def test_backward_equals_torch_autograd(mode):
+    """Library case: torch autograd (float64, CPU) through a dense masked form of the layer
+    (rotation, scaled scores plus bias, -inf outside the key set, sigmoid or softmax) gives
+    the same gradients."""
+    B, N, Hq, Hkv, d, w, s, theta = 2, 33, 4, 2, 8, 7, 2, 1e4
+    q, k, v = _rand((B, N, Hq, d), 70), _rand((B, N, Hkv, d), 71), _rand((B, N, Hkv, d), 72)
+    g = _rand((B, N, Hq, d), 73)
+    slopes = [-0.5, -0.25, 0.5, 0.25]
+    dq, dk, dv = oracle.backward(q, k, v, g, w=w, s=s, mode=mode, slopes=slopes,
+                                 rope_theta=theta)
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    pos = torch.arange(N, dtype=torch.float64)
+    freq = theta ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = pos[:, None] * freq[None, :]
+    c, sn = torch.cos(ang)[None, :, None, :], torch.sin(ang)[None, :, None, :]
+
+    def rot(x):
+        a, b = x[..., 0::2], x[..., 1::2]
+        return torch.stack((a * c - b * sn, a * sn + b * c), dim=-1).flatten(-2)
+    qr, kr = rot(tq), rot(tk)
+    kr = kr.repeat_interleave(Hq // Hkv, dim=2)
+    vr = tv.repeat_interleave(Hq // Hkv, dim=2)
+    x = torch.einsum("bihd,bjhd->bhij", qr, kr) / np.sqrt(d)
+    i, j = torch.arange(N)[:, None], torch.arange(N)[None, :]
+    x = x + torch.tensor(slopes, dtype=torch.float64)[None, :, None, None] * (i - j)
+    keep = (j <= i) & ((i - j < w) | (j < s))
+    if mode == oracle.SOFTMAX:
+        p = torch.softmax(x.masked_fill(~keep, float("-inf")), dim=-1)
+    else:
+        p = torch.sigmoid(x) * keep
+    o = torch.einsum("bhij,bjhd->bihd", p, vr)
+    (o * torch.tensor(g)).sum().backward()
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_window_of_one_closed_form():
+    """w = 1, sigmoid, no rotation or bias: o_i = sigmoid(scale q_i.k_i) v_i, so
+    dv_i = sigmoid(scale q_i.k_i) dout_i and dq_i = scale sigma(1 - sigma) (dout_i.v_i) k_i."""
+    B, N, H, d = 1, 6, 1, 4
+    q, k, v, g = (_rand((B, N, H, d), 80 + t) for t in range(4))
+    dq, dk, dv = oracle.backward(q, k, v, g, w=1, mode=oracle.SIGMOID)
+    sc = 1 / np.sqrt(d)
+    sig = 1 / (1 + np.exp(-sc * np.sum(q * k, axis=-1, keepdims=True)))
+    np.testing.assert_allclose(dv, sig * g, rtol=1e-12)
+    dp = np.sum(g * v, axis=-1, keepdims=True)
+    np.testing.assert_allclose(dq, sc * sig * (1 - sig) * dp * k, rtol=1e-12)
+    np.testing.assert_allclose(dk, sc * sig * (1 - sig) * dp * q, rtol=1e-12)
