@@ -94,6 +94,46 @@ swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k
 size_t swa_prefill_workspace_bytes(const swa_prefill_params *p);
 
 /*
+ * Training pair: the forward for training and its backward (SWAT: Sliding Window Attention
+ * Training, "Putting It Together": the layer is trained end to end, so its inputs need
+ * gradients). Both run on the matrix cores only: bf16 q, k, v, d in {64, 128} and 16-byte
+ * aligned tensors, else SWA_ERR_UNSUPPORTED; operands as in swa_prefill (float16 products,
+ * float32 accumulation), so dout must stay within the float16 range too.
+ *
+ * swa_prefill_train: swa_prefill, plus for softmax the natural-log normaliser of every row,
+ *   lse[b][h][i] = log sum_{j in K(i)} exp(x_ij), device float [B, H_q, N] (NULL allowed
+ *   for sigmoid, which has no normaliser). Workspace as for swa_prefill.
+ */
+swa_status swa_prefill_train(const swa_prefill_params *p, const void *q, const void *k,
+                             const void *v, void *o, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * swa_prefill_backward: gradients of a loss L given dout = dL/do [B, N, H_q, d]:
+ *   dP_ij = dout_i . v_j
+ *   dX_ij = dP_ij p_ij (1 - p_ij)            sigmoid (the logistic derivative)
+ *         = p_ij (dP_ij - dout_i . o_i)      softmax (the row Jacobian)
+ *   dv_j = sum_i p_ij dout_i,  dq_i = scale R(i)^T sum_j dX_ij R(j) k_j,
+ *   dk_j = scale R(j)^T sum_i dX_ij R(i) q_i
+ * over j in K(i); key and value gradients sum over the query heads of their group; the
+ * ALiBi slopes get no gradient. dq [B, N, H_q, d], dk, dv [B, N, H_kv, d] are written
+ * entirely (no accumulation into them). o, dout, dq, dk, dv have p->out_dtype; o and lse
+ * (from swa_prefill_train with the same parameters and inputs) are read for softmax only
+ * and may be NULL for sigmoid. workspace: swa_prefill_backward_workspace_bytes(p) bytes,
+ * 16-byte aligned: float16 images of k, v, q and dout (B * N_tiles * 64 * d * 2 bytes for
+ * each of H_kv, H_kv, H_q and H_q heads, N_tiles = ceil(N / 64)), for softmax 8 bytes of
+ * row statistics per (b, h, row), and with sinks a float32 partial gradient of the sink keys.
+ */
+swa_status swa_prefill_backward(const swa_prefill_params *p, const void *q, const void *k,
+                                const void *v, const void *o, const float *lse,
+                                const void *dout, void *dq, void *dk, void *dv,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace swa_prefill_backward needs (0 when none, or when the parameters are
+ * invalid or unsupported). */
+size_t swa_prefill_backward_workspace_bytes(const swa_prefill_params *p);
+
+/*
  * RoPE angle table (SWAT: Sliding Window Attention Training, "RoPE: Stabilizing Sigmoid
  * Attention Training"; the RoFormer rotation it cites):
  *   table[pos][t] = (cos(pos * theta^(-2t/d)), sin(pos * theta^(-2t/d))), pos in

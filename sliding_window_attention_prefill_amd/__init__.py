@@ -57,7 +57,8 @@ class DecodeParams(ctypes.Structure):
 
 EXPORTS = ["swa_prefill", "swa_prefill_workspace_bytes", "swa_rope_table", "swa_rope_apply", "swa_kv_append", "swa_decode",
            "swa_decode_append", "swa_decode_workspace_bytes", "swa_prefill_chunk",
-           "swa_prefill_chunk_workspace_bytes", "swa_status_string",
+           "swa_prefill_chunk_workspace_bytes", "swa_prefill_train", "swa_prefill_backward",
+           "swa_prefill_backward_workspace_bytes", "swa_status_string",
            "swa_last_hip_error", "swa_version"]
 
 _lib = None
@@ -100,6 +101,15 @@ def load():
         lib.swa_prefill_chunk_workspace_bytes.argtypes = [P(DecodeParams), P(CacheDesc), c_i64,
                                                           c_i64]
         lib.swa_prefill_chunk_workspace_bytes.restype = ctypes.c_size_t
+        lib.swa_prefill_train.argtypes = [P(PrefillParams), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                                          c_ptr, ctypes.c_size_t, c_ptr]
+        lib.swa_prefill_train.restype = ctypes.c_int
+        lib.swa_prefill_backward.argtypes = [P(PrefillParams), c_ptr, c_ptr, c_ptr, c_ptr, c_ptr,
+                                             c_ptr, c_ptr, c_ptr, c_ptr, c_ptr, ctypes.c_size_t,
+                                             c_ptr]
+        lib.swa_prefill_backward.restype = ctypes.c_int
+        lib.swa_prefill_backward_workspace_bytes.argtypes = [P(PrefillParams)]
+        lib.swa_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
         lib.swa_status_string.argtypes = [ctypes.c_int]
         lib.swa_status_string.restype = ctypes.c_char_p
         lib.swa_last_hip_error.argtypes = []
@@ -212,6 +222,109 @@ def swa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: int, s:
     _check("swa_prefill", lib.swa_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                           _ptr(workspace), ws_bytes, _stream(q.device, stream)))
     return out
+
+
+def _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table):
+    """Shape checks shared by the prefill entry points; returns PrefillParams."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _dev(t, n)
+    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4:
+        raise ValueError("q must be [B,N,H_q,d] and k, v [B,N,H_kv,d]")
+    B, N, Hq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError("q, k, v shapes disagree")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if tuple(out.shape) != (B, N, Hq, d):
+        raise ValueError("out must be [B,N,H_q,d]")
+    if alibi_slopes is not None:
+        _dev(alibi_slopes, "alibi_slopes")
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq:
+            raise ValueError("alibi_slopes must be float32[H_q]")
+    rows = 0
+    if rope_table is not None:
+        _dev(rope_table, "rope_table")
+        if rope_table.dtype != torch.float32 or rope_table.dim() != 3 or \
+                rope_table.shape[1] != d // 2 or rope_table.shape[2] != 2:
+            raise ValueError("rope_table must be float32 [rows, d/2, 2]")
+        rows = rope_table.shape[0]
+    return PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), _dt(out), scale,
+                         _ptr(alibi_slopes), _ptr(rope_table), rows)
+
+
+def _workspace(need: int, workspace, device):
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    return workspace, ws_bytes
+
+
+def swa_prefill_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: int, s: int = 0,
+                      mode=SWA_SIGMOID, scale: float = 0.0,
+                      alibi_slopes: Optional[torch.Tensor] = None,
+                      rope_table: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Forward for training: returns (o, lse), lse float32 [B, H_q, N] the natural-log row
+    normalisers (softmax; None for sigmoid)."""
+    B, N, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, N, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
+    p = _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table)
+    if p.mode == SWA_SOFTMAX:
+        if lse is None:
+            lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        _dev(lse, "lse")
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N):
+            raise ValueError("lse must be float32 [B, H_q, N]")
+    else:
+        lse = None
+    lib = load()
+    workspace, ws_bytes = _workspace(int(lib.swa_prefill_workspace_bytes(ctypes.byref(p))),
+                                     workspace, q.device)
+    _check("swa_prefill_train",
+           lib.swa_prefill_train(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), ws_bytes, _stream(q.device, stream)))
+    return out, lse
+
+
+def swa_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         o: Optional[torch.Tensor], lse: Optional[torch.Tensor],
+                         dout: torch.Tensor, *, w: int, s: int = 0, mode=SWA_SIGMOID,
+                         scale: float = 0.0, alibi_slopes: Optional[torch.Tensor] = None,
+                         rope_table: Optional[torch.Tensor] = None,
+                         grads=None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) in dout's dtype for the output gradient dout [B,N,H_q,d];
+    o and lse (from swa_prefill_train) are needed for softmax only."""
+    p = _prefill_params(q, k, v, dout, w, s, mode, scale, alibi_slopes, rope_table)
+    if p.mode == SWA_SOFTMAX:
+        if o is None or lse is None:
+            raise ValueError("softmax needs the forward's o and lse")
+        _dev(o, "o")
+        _dev(lse, "lse")
+        if o.shape != dout.shape or o.dtype != dout.dtype:
+            raise ValueError("o must match dout")
+    if grads is None:
+        grads = (torch.empty(q.shape, dtype=dout.dtype, device=q.device),
+                 torch.empty(k.shape, dtype=dout.dtype, device=q.device),
+                 torch.empty(v.shape, dtype=dout.dtype, device=q.device))
+    dq, dk, dv = grads
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _dev(t, n)
+        if t.shape != ref.shape or t.dtype != dout.dtype:
+            raise ValueError("%s must have the shape of its input and dout's dtype" % n)
+    lib = load()
+    workspace, ws_bytes = _workspace(
+        int(lib.swa_prefill_backward_workspace_bytes(ctypes.byref(p))), workspace, q.device)
+    _check("swa_prefill_backward",
+           lib.swa_prefill_backward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                    _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(workspace), ws_bytes, _stream(q.device, stream)))
+    return dq, dk, dv
 
 
 def swa_prefill_workspace_bytes(q: torch.Tensor, k: torch.Tensor, *, w: int, s: int = 0,

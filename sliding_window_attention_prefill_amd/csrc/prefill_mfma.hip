@@ -39,21 +39,11 @@
 //   * The output goes through LDS so that every global store writes whole rows.
 //   * Workgroups are numbered so that each of the 8 XCDs walks a contiguous run of query
 //     tiles of the same (batch, kv head), keeping shared K/V tiles in that XCD's L2.
-#include "swa_device.hpp"
+#include "mfma_common.hpp"
 #include "swa_kernels.hpp"
 
 namespace swa {
 namespace {
-
-constexpr int BK = 64;  // keys per tile
-constexpr float LOG2E = 1.4426950408889634f;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x4_t __attribute__((__vector_size__(4 * sizeof(short))));
-typedef short s16x8_t __attribute__((__vector_size__(8 * sizeof(short))));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <int D>
 struct Tile {
@@ -138,6 +128,7 @@ struct MfmaParams {
     int out_bf16;
     int chunked;              // 1: rows and positions per sequence from cg; V from vimg
     ChunkGeom cg;
+    float *lse;               // softmax row log-normalisers [B, Hq, N] (natural log), or null
 };
 
 struct PackParams {
@@ -147,44 +138,6 @@ struct PackParams {
     int64_t N, Hkv;
     int n_ktiles;
 };
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return make_uint4(x[0], x[1], x[2], x[3]);
-}
-
-__device__ __forceinline__ float4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_t x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-    return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
-                       __uint_as_float(x[3]));
-}
-
-__device__ __forceinline__ float4 as_float4(uint4 x) {
-    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
-                       __uint_as_float(x.w));
-}
-
-// A dword of two bf16 inputs -> two float16 matrix operands, rotated by (c, s) or not.
-__device__ __forceinline__ uint32_t rotate_pair(uint32_t w, float c, float s) {
-    const float a = __uint_as_float(w << 16);
-    const float b = __uint_as_float(w & 0xffff0000u);
-    return pack_f16x2(fmaf(-b, s, a * c), fmaf(a, s, b * c));
-}
-__device__ __forceinline__ uint32_t to_f16_pair(uint32_t w) {
-    return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-}
-__device__ __forceinline__ uint4 rotate_chunk(uint4 x, float4 t0, float4 t1) {
-    return make_uint4(rotate_pair(x.x, t0.x, t0.y), rotate_pair(x.y, t0.z, t0.w),
-                      rotate_pair(x.z, t1.x, t1.y), rotate_pair(x.w, t1.z, t1.w));
-}
-__device__ __forceinline__ uint4 convert_chunk(uint4 x) {
-    return make_uint4(to_f16_pair(x.x), to_f16_pair(x.y), to_f16_pair(x.z), to_f16_pair(x.w));
-}
 
 // ---------------------------------------------------------------------------------------
 // Pre-pass: every 64-key tile, once, into its LDS image. One block per (batch, tile, group of
@@ -381,88 +334,18 @@ struct LaneOffsets {
     uint32_t dvraw[Tile<D>::DMA_W];  // source byte offset in the V input rows, per transfer
 };
 
-// Buffer -> LDS transfers of one tile: DMA_W rounds of 1 KB per wavefront; lane l of round i
-// lands at bytes 16 l of that round's kilobyte. off[i] is this lane's source offset.
 template <int D>
 __device__ __forceinline__ void dma_tile(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t r,
-                                         uint32_t base, const uint32_t *off,
-                                         int wave) {
-#pragma unroll
-    for (int i = 0; i < Tile<D>::DMA_W; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (lds_void_t *)(dst + (wave * Tile<D>::DMA_W + i) * 512), 16, base + off[i], 0, 0, 0);
+                                         uint32_t base, const uint32_t *off, int wave) {
+    dma_rounds<Tile<D>::DMA_W>(dst, r, base, off, wave);
 }
 
-// Key offset (from j0 + 4g) of accumulator element e of score block kb.
-__device__ __forceinline__ constexpr int key_of(int kb, int e) {
-    return kb * 32 + 8 * (e >> 2) + (e & 3);
-}
-
-// Exclude the keys of an edge tile that are outside the key set: their logits become -inf
-// (weight 0 in both modes). Element (kb, e) is key j = jb + key_of(kb, e) with
-// i - j = dq - key_of(kb, e). SINKS adds the keys j < s at or before the query.
-template <bool SINKS>
-__device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, int w, int s) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int dij = dq - key_of(kb, e);
-            bool ok = (unsigned)dij < (unsigned)w;   // 0 <= i - j < w
-            if (SINKS) ok = ok | ((dij >= 0) & (jb + key_of(kb, e) < s));
-            sacc[kb][e] = ok ? sacc[kb][e] : -INFINITY;
-        }
-}
-
-// Operands of one extra matrix instruction per 32-key block that puts the key part of the
-// ALiBi bias into the score accumulator: with r = slope log2(e) / cs split as
-// 2^a (hi + lo) in float16, A row m holds (2^a kappa, 2^a kappa) and every B column
-// (-hi, -lo) in k = 0, 1, so the product is -r kappa for the key kappa = 32 kb + m of the
-// tile (kappa 2^a is exact in float16, and hi + lo carries r to about 22 bits).
-struct BiasOperands {
-    f16x8_t a[2];
-    f16x8_t b;
-};
-
-__device__ __forceinline__ BiasOperands bias_operands(float r, int lane) {
-    int ex = 0;
-    (void)frexpf(r, &ex);                      // |r| = m 2^ex, m in [0.5, 1)
-    int a = ex - 1;
-    a = a < -24 ? -24 : (a > 9 ? 9 : a);       // kappa 2^a stays exact for kappa < 64
-    const float rs = ldexpf(r, -a);
-    const _Float16 hi = (_Float16)rs;
-    const _Float16 lo = (_Float16)(rs - (float)hi);
-    BiasOperands bo;
-    const f16x8_t z = {};
-    bo.a[0] = z; bo.a[1] = z; bo.b = z;
-    if (lane < 32) {
-        const _Float16 k0 = (_Float16)ldexpf((float)lane, a);
-        const _Float16 k1 = (_Float16)ldexpf((float)(lane + 32), a);
-        bo.a[0][0] = k0; bo.a[0][1] = k0;
-        bo.a[1][0] = k1; bo.a[1][1] = k1;
-        bo.b[0] = -hi; bo.b[1] = -lo;
-    }
-    return bo;
-}
-
-// S^T = K Q^T for the 64 keys of one tile (two 32-key blocks, whose chains alternate); with
-// ALiBi each block starts from the key part of the bias.
+// S^T = K Q^T for the 64 keys of one tile.
 template <int D, bool ALIBI>
 __device__ __forceinline__ void qk_tile(const uint16_t *__restrict__ kl, const LaneOffsets<D> &lo,
                                         const BiasOperands &bo, const f16x8_t (&qreg)[D / 16],
                                         f32x16_t (&sacc)[2]) {
-    constexpr int KS = D / 16;
-    const f32x16_t zero = {};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bo.b, zero, 0, 0, 0) : zero;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + lo.k[ks]);
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sacc[kb], 0, 0, 0);
-        }
+    qk_tile_off<D, ALIBI>(kl, lo.k, bo, qreg, sacc);
 }
 
 // Scores of one tile made ready for weighting (run in the step that formed them): edge
@@ -855,6 +738,8 @@ void prefill_mfma_kernel(MfmaParams p) {
     // whole rows
     const float l_tot = MODE == 1 ? l_run + __shfl_xor(l_run, 32, 64) : 1.0f;
     const float inv = MODE == 1 ? 1.0f / l_tot : 1.0f;
+    if (MODE == 1 && p.lse != nullptr && g == 0 && i < N)
+        p.lse[((int64_t)b * p.Hq + h) * p.N + i] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
     float *ol = reinterpret_cast<float *>(lds) + (wave & 3) * (32 * T::OSTR);
     constexpr int C4 = D / 4;  // 4-float chunks per row
 #pragma unroll
@@ -964,7 +849,7 @@ size_t prefill_mfma_workspace_bytes(const PrefillArgs &a) {
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
-                               const void *v, void *o, void *ws, hipStream_t st) {
+                               const void *v, void *o, void *ws, hipStream_t st, float *lse) {
     if (a.B * a.N == 0) return hipSuccess;
     const Plan pl = plan_of(a);
     const int64_t G = a.Hq / a.Hkv;
@@ -989,6 +874,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.kv_bytes = (uint32_t)(((a.N - 1) * a.Hkv + 1) * a.d * 2);
     mp.row_bytes = (uint32_t)(a.Hkv * a.d * 2);
     mp.out_bf16 = a.out_dt == 1;
+    mp.lse = lse;
 
     {
         PackParams pp = {};

@@ -32,7 +32,7 @@ float resolve_scale(float scale, int64_t d) {
 
 extern "C" {
 
-int swa_version(void) { return 300; }
+int swa_version(void) { return 400; }
 
 const char *swa_status_string(swa_status s) {
     switch (s) {
@@ -97,6 +97,63 @@ swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k
     }
     if ((a.B * a.N * a.Hq + 3) / 4 > 0x7fffffff) return SWA_ERR_UNSUPPORTED;
     return hip_status(swa::launch_prefill_simt(a, q, k, v, o, st));
+}
+
+// The training pair runs on the matrix cores only: bf16 inputs, d in {64, 128}, 16-byte
+// aligned tensors.
+static swa_status check_train(const swa_prefill_params *p, std::initializer_list<const void *> ptrs) {
+    const swa_status chk = check_prefill(p);
+    if (chk != SWA_OK) return chk;
+    const swa::PrefillArgs a = prefill_args(p);
+    if (!swa::prefill_mfma_supported(a)) return SWA_ERR_UNSUPPORTED;
+    uintptr_t bits = reinterpret_cast<uintptr_t>(p->rope_table);
+    for (const void *x : ptrs) bits |= reinterpret_cast<uintptr_t>(x);
+    if (bits & 15) return SWA_ERR_UNSUPPORTED;
+    return SWA_OK;
+}
+
+swa_status swa_prefill_train(const swa_prefill_params *p, const void *q, const void *k,
+                             const void *v, void *o, float *lse, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    const swa_status chk = check_train(p, {q, k, v, o});
+    if (chk != SWA_OK) return chk;
+    const int64_t elems = p->B * p->N;
+    if (elems > 0 && (!q || !k || !v || !o)) return SWA_ERR_INVALID_ARGUMENT;
+    if (elems > 0 && p->mode == SWA_SOFTMAX && !lse) return SWA_ERR_INVALID_ARGUMENT;
+    const swa::PrefillArgs a = prefill_args(p);
+    const size_t need = swa::prefill_mfma_workspace_bytes(a);
+    if (need > 0 && (!workspace || workspace_bytes < need ||
+                     (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
+        return SWA_ERR_INVALID_ARGUMENT;
+    return hip_status(swa::launch_prefill_mfma(a, q, k, v, o, workspace,
+                                               static_cast<hipStream_t>(stream),
+                                               p->mode == SWA_SOFTMAX ? lse : nullptr));
+}
+
+size_t swa_prefill_backward_workspace_bytes(const swa_prefill_params *p) {
+    if (check_prefill(p) != SWA_OK) return 0;
+    const swa::PrefillArgs a = prefill_args(p);
+    if (!swa::prefill_mfma_supported(a)) return 0;
+    return swa::prefill_bwd_workspace_bytes(a);
+}
+
+swa_status swa_prefill_backward(const swa_prefill_params *p, const void *q, const void *k,
+                                const void *v, const void *o, const float *lse,
+                                const void *dout, void *dq, void *dk, void *dv,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    const swa_status chk = check_train(p, {q, k, v, o, dout, dq, dk, dv});
+    if (chk != SWA_OK) return chk;
+    const int64_t elems = p->B * p->N;
+    if (elems > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
+        return SWA_ERR_INVALID_ARGUMENT;
+    if (elems > 0 && p->mode == SWA_SOFTMAX && (!o || !lse)) return SWA_ERR_INVALID_ARGUMENT;
+    const swa::PrefillArgs a = prefill_args(p);
+    const size_t need = swa::prefill_bwd_workspace_bytes(a);
+    if (need > 0 && (!workspace || workspace_bytes < need ||
+                     (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
+        return SWA_ERR_INVALID_ARGUMENT;
+    return hip_status(swa::launch_prefill_bwd(a, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 swa_status swa_rope_table(float *table, int64_t n_pos, int64_t d, double theta, void *stream) {

@@ -42,8 +42,18 @@ hipError_t launch_prefill_simt(const PrefillArgs &a, const void *q, const void *
 // prefill_mfma_workspace_bytes(a) bytes (packed K/V tile images), 16-byte aligned.
 bool prefill_mfma_supported(const PrefillArgs &a);
 size_t prefill_mfma_workspace_bytes(const PrefillArgs &a);
+// lse (softmax only, may be null): the log-normaliser of every row, [B, Hq, N] float32.
 hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
-                               const void *v, void *o, void *ws, hipStream_t st);
+                               const void *v, void *o, void *ws, hipStream_t st,
+                               float *lse = nullptr);
+
+// Backward of the matrix-core prefill (bf16 inputs, d in {64, 128}): gradients dq, dk, dv
+// (out dtype) from dout (out dtype), the forward output o and, for softmax, the forward's
+// lse. ws holds prefill_bwd_workspace_bytes(a) bytes, 16-byte aligned.
+size_t prefill_bwd_workspace_bytes(const PrefillArgs &a);
+hipError_t launch_prefill_bwd(const PrefillArgs &a, const void *q, const void *k,
+                              const void *v, const void *o, const float *lse, const void *dout,
+                              void *dq, void *dk, void *dv, void *ws, hipStream_t st);
 
 hipError_t launch_rope_table(float *table, int64_t n_pos, int64_t d, double theta,
                              hipStream_t st);

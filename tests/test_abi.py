@@ -210,3 +210,39 @@ def test_prefill_chunk_rejects_bad_arguments(lib):
     need = lib.swa_prefill_chunk_workspace_bytes(ctypes.byref(p), ctypes.byref(c), 10, 5)
     assert call(ws=DUMMY, ws_bytes=need - 16) == 1            # short workspace
     assert call(ws=ctypes.c_void_p(0x1004), ws_bytes=need) == 1  # misaligned workspace
+
+
+def test_training_pair_rejections(lib):
+    """The training pair runs on the matrix cores only, and softmax needs o and lse."""
+    p = _params(mode=1)
+    z = ctypes.c_void_p(0)
+    assert lib.swa_prefill_train(ctypes.byref(_params(in_dtype=0)), DUMMY, DUMMY, DUMMY, DUMMY,
+                                 DUMMY, None, 0, None) == 2        # float32 inputs
+    assert lib.swa_prefill_train(ctypes.byref(_params(d=96)), DUMMY, DUMMY, DUMMY, DUMMY,
+                                 DUMMY, None, 0, None) == 2        # head size 96
+    assert lib.swa_prefill_train(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, None, None, 0,
+                                 None) == 1                        # softmax without lse
+    assert lib.swa_prefill_backward(ctypes.byref(p), DUMMY, DUMMY, DUMMY, None, None, DUMMY,
+                                    DUMMY, DUMMY, DUMMY, None, 0, None) == 1   # no o / lse
+    assert lib.swa_prefill_backward(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                    z, DUMMY, DUMMY, None, 0, None) == 1       # no dq
+    need = lib.swa_prefill_backward_workspace_bytes(ctypes.byref(p))
+    assert lib.swa_prefill_backward(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                    DUMMY, DUMMY, DUMMY, DUMMY, need - 16, None) == 1
+
+
+def test_backward_workspace_bytes(lib):
+    """k, v, q and dout images (64-row tiles, float16), softmax row statistics, and the sink
+    keys' float32 partial gradients when some queries see a sink only through the sink rule."""
+    def wsb(**kw):
+        return lib.swa_prefill_backward_workspace_bytes(ctypes.byref(_params(**kw)))
+    B, Hq, Hkv, N, d = 1, 4, 2, 16, 64
+    img = lambda H: B * H * 1 * 64 * d * 2
+    assert wsb(mode=0) == 2 * img(Hkv) + 2 * img(Hq)
+    assert wsb(mode=1) == 2 * img(Hkv) + 2 * img(Hq) + B * Hq * 64 * 8
+    # N 1000, w 100, s 4: the sink rule reaches queries past 127 + 100 -> one sink block
+    big = dict(N=1000, w=100, s=4, mode=0)
+    tiles = (1000 + 63) // 64
+    assert wsb(**big) == 2 * B * Hkv * tiles * 64 * d * 2 + 2 * B * Hq * tiles * 64 * d * 2 + \
+        2 * B * Hkv * 128 * d * 4
+    assert wsb(in_dtype=0) == 0 and wsb(d=96) == 0 and wsb(B=0) == 0
