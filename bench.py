@@ -17,6 +17,8 @@ The JSON line also carries:
   chunk_prefill chunked prefill over the ring cache (8 prompts x 2048 rows per step at the
                 Mistral-7B layer shape, histories past the 4,096-token window), in-window
                 TFLOP/s of whole swa_prefill_chunk calls;
+  backward      the training backward (swa_prefill_backward) of this layer and of the
+                Mistral-7B-shaped one, in TFLOP/s of its five band contractions;
   cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -241,6 +243,50 @@ def bench_chunk(cfg, out_dtype):
     }
 
 
+def bench_backward(cfg, steps: int = 5):
+    """The backward of one prefill layer (swa_prefill_backward: pre-passes, dk/dv and dq
+    kernels) given the forward's o and lse, bf16 gradients; HIP events around each call on
+    its stream. Algorithmic FLOPs: the score recompute and the four gradient products,
+    5 x 2d per in-window (query, key) pair = 2.5 x the forward's."""
+    import torch
+    import sliding_window_attention_prefill_amd as swa
+    import swa_workloads as wl
+
+    q, k, v = wl.prefill_inputs(cfg, device="cuda")
+    sl = wl.slopes_tensor(cfg.slopes, device="cuda")
+    table = swa.swa_rope_table(cfg.N, cfg.d, cfg.rope_theta)
+    o, lse = swa.swa_prefill_train(q, k, v, w=cfg.w, s=cfg.s, mode=cfg.mode, alibi_slopes=sl,
+                                   rope_table=table, out_dtype=torch.bfloat16)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 100)
+    dout = torch.randn(o.shape, generator=g, device="cuda").to(torch.bfloat16)
+    grads = tuple(torch.empty(t.shape, dtype=torch.bfloat16, device="cuda") for t in (q, k, v))
+    need = swa.swa_prefill_backward_workspace_bytes(q, k, w=cfg.w, s=cfg.s, mode=cfg.mode)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def call():
+        swa.swa_prefill_backward(q, k, v, o, lse, dout, w=cfg.w, s=cfg.s, mode=cfg.mode,
+                                 alibi_slopes=sl, rope_table=table, grads=grads, workspace=ws,
+                                 stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    flops = 2.5 * prefill_flops(cfg)
+    tf = flops / (ms / 1e3) / 1e12
+    return {"workload": cfg.name, "ms_per_call": round(ms, 4), "algorithmic_flops": flops,
+            "TFLOP_s": round(tf, 2), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "note": "bf16 gradients; pre-passes, dk/dv and dq kernels"}
+
+
 def cpu_baseline(cfg, sample_batches: int):
     """The float64 oracle on the first `sample_batches` sequences of the batch (all heads,
     all rows), timed on the host; reported in the metric's unit."""
@@ -271,6 +317,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes three times (the "
@@ -322,6 +369,8 @@ def main():
                                  for c in (wl.DECODE_W4096, wl.DECODE_W32K)]
     if not args.no_chunk:
         result["chunk_prefill"] = bench_chunk(wl.CHUNK_W4096, torch.float32)
+    if not args.no_backward:
+        result["backward"] = [bench_backward(c) for c in (cfg, wl.C3)]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_batches)
     print(json.dumps(result), flush=True)

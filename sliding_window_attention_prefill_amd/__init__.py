@@ -338,6 +338,17 @@ def swa_prefill_workspace_bytes(q: torch.Tensor, k: torch.Tensor, *, w: int, s: 
     return int(load().swa_prefill_workspace_bytes(ctypes.byref(p)))
 
 
+def swa_prefill_backward_workspace_bytes(q: torch.Tensor, k: torch.Tensor, *, w: int, s: int = 0,
+                                         mode=SWA_SIGMOID,
+                                         grad_dtype: Optional[torch.dtype] = None) -> int:
+    """Workspace bytes swa_prefill_backward needs for q [B,N,H_q,d], k [B,N,H_kv,d]."""
+    B, N, Hq, d = q.shape
+    out_dt = SWA_F32 if (grad_dtype or q.dtype) == torch.float32 else SWA_BF16
+    p = PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), out_dt, 0.0,
+                      None, None, 0)
+    return int(load().swa_prefill_backward_workspace_bytes(ctypes.byref(p)))
+
+
 def swa_rope_apply(x: torch.Tensor, pos0: torch.Tensor, rope_table: torch.Tensor,
                    stream=None) -> torch.Tensor:
     """Rotate x [B,N,H,d] in place; row n of batch b at position pos0[b] + n."""
