@@ -52,6 +52,10 @@ def bind(path: str):
     lib.swa_oracle_prefill.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                        dbl, dp, dbl, dp, dp, dp, ip, i64, dp]
     lib.swa_oracle_prefill.restype = ctypes.c_int
+    lib.swa_oracle_prefill_dilated.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64,
+                                               ctypes.c_int, dbl, dp, dbl, dp, dp, dp, ip, i64,
+                                               dp]
+    lib.swa_oracle_prefill_dilated.restype = ctypes.c_int
     lib.swa_oracle_append.argtypes = [i64, i64, i64, i64, i64, dbl, dp, dp, ip, dp, dp,
                                       dp, dp, ip, i64]
     lib.swa_oracle_append.restype = ctypes.c_int
@@ -112,9 +116,10 @@ def threads() -> int:
 
 
 def prefill(q, k, v, *, w: int, s: int = 0, mode: int = SIGMOID, scale: float = 0.0,
-            slopes=None, rope_theta: float = 0.0, rows=None) -> np.ndarray:
+            slopes=None, rope_theta: float = 0.0, rows=None, dilation: int = 1) -> np.ndarray:
     """float64 attention output. q [B,N,H_q,d], k/v [B,N,H_kv,d]. rows: optional list of
-    query rows; then the result is [B, len(rows), H_q, d]."""
+    query rows; then the result is [B, len(rows), H_q, d]. dilation r > 1: window keys
+    i, i - r, ..., i - r (w - 1) (swa_oracle_prefill_dilated)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -128,9 +133,15 @@ def prefill(q, k, v, *, w: int, s: int = 0, mode: int = SIGMOID, scale: float = 
         r = _i64(rows)
         nr = r.shape[0]
     out = np.zeros((B, nr, Hq, d), dtype=np.float64)
-    rc = _load().swa_oracle_prefill(B, Hq, Hkv, N, d, w, s, mode, float(scale), _ptr(sl),
-                                    float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(r),
-                                    nr if r is not None else 0, _ptr(out))
+    if dilation == 1:
+        rc = _load().swa_oracle_prefill(B, Hq, Hkv, N, d, w, s, mode, float(scale), _ptr(sl),
+                                        float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(r),
+                                        nr if r is not None else 0, _ptr(out))
+    else:
+        rc = _load().swa_oracle_prefill_dilated(B, Hq, Hkv, N, d, w, s, int(dilation), mode,
+                                                float(scale), _ptr(sl), float(rope_theta),
+                                                _ptr(q), _ptr(k), _ptr(v), _ptr(r),
+                                                nr if r is not None else 0, _ptr(out))
     if rc != 0:
         raise ValueError("oracle prefill rejected its arguments")
     return out

@@ -109,11 +109,12 @@ static void weights(double *x, int64_t n, int mode) {
  * slopes: float64[H_q] signed ALiBi slopes, or NULL for no bias. theta <= 0: no rotation.
  * scale <= 0 means 1/sqrt(d). Returns 0, or -1 on bad arguments / allocation failure.
  */
-int swa_oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
-                       int64_t s, int mode, double scale, const double *slopes, double theta,
-                       const double *q, const double *k, const double *v,
-                       const int64_t *rows, int64_t n_rows, double *o) {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || N < 0 || d <= 0 || w < 1 || s < 0)
+static int prefill_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
+                        int64_t s, int64_t dil, int mode, double scale, const double *slopes,
+                        double theta, const double *q, const double *k, const double *v,
+                        const int64_t *rows, int64_t n_rows, double *o) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || N < 0 || d <= 0 || w < 1 || s < 0 ||
+        dil < 1)
         return -1;
     if (theta > 0.0 && d % 2 != 0) return -1;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
@@ -142,8 +143,10 @@ int swa_oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
     {
         double *qt = (double *)malloc(sizeof(double) * (size_t)d);
         double *kt = (double *)malloc(sizeof(double) * (size_t)d);
-        double *x = (double *)malloc(sizeof(double) * (size_t)(w + s + 1));
-        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(w + s + 1));
+        /* a key set has at most min(i + 1, w + s) entries; N + s + 1 also holds any list
+           that repeats the sinks, so a planted mistake fails a pin instead of a write */
+        double *x = (double *)malloc(sizeof(double) * (size_t)(N + s + 1));
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N + s + 1));
         if (!qt || !kt || !x || !key) {
 #pragma omp atomic write
             fail = 1;
@@ -162,8 +165,16 @@ int swa_oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                 /* K(i) as two disjoint ranges: sinks [0, min(s, lo)) and window [lo, i]. */
                 int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;
                 int64_t n = 0;
-                for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
-                for (int64_t j = lo; j <= i; ++j) key[n++] = j;
+                if (dil == 1) {
+                    for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
+                    for (int64_t j = lo; j <= i; ++j) key[n++] = j;
+                } else {
+                    /* dilated: window keys i, i - dil, ..., i - dil (w - 1); every sink j < s */
+                    lo = i - dil * (w - 1) > 0 ? i - dil * (w - 1) : 0;
+                    for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
+                    for (int64_t j = lo; j <= i; ++j)
+                        if ((i - j) % dil == 0 || j < s) key[n++] = j;
+                }
 
                 for (int64_t e = 0; e < n; ++e) {
                     int64_t j = key[e];
@@ -187,6 +198,30 @@ int swa_oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
     }
     free(cs); free(sn);
     return fail ? -1 : 0;
+}
+
+int swa_oracle_prefill(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
+                       int64_t s, int mode, double scale, const double *slopes, double theta,
+                       const double *q, const double *k, const double *v,
+                       const int64_t *rows, int64_t n_rows, double *o) {
+    return prefill_impl(B, Hq, Hkv, N, d, w, s, 1, mode, scale, slopes, theta, q, k, v, rows,
+                        n_rows, o);
+}
+
+/*
+ * Dilated prefill (the dilated-window member of the sparse-attention family the Sliding
+ * Window Attention glossary lists beside SWA): the window keeps every dil-th position,
+ *   K(i) = { j <= i : ((i - j) mod dil = 0 and (i - j) / dil < w)  or  j < s },
+ * so the window spans dil (w - 1) + 1 positions with w keys; the sinks are unchanged.
+ * dil = 1 is swa_oracle_prefill. Everything else as there.
+ */
+int swa_oracle_prefill_dilated(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                               int64_t w, int64_t s, int64_t dil, int mode, double scale,
+                               const double *slopes, double theta, const double *q,
+                               const double *k, const double *v, const int64_t *rows,
+                               int64_t n_rows, double *o) {
+    return prefill_impl(B, Hq, Hkv, N, d, w, s, dil, mode, scale, slopes, theta, q, k, v, rows,
+                        n_rows, o);
 }
 
 /*
@@ -443,9 +478,9 @@ int swa_oracle_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d
 #pragma omp parallel
     {
         double *qt = (double *)malloc(sizeof(double) * (size_t)d);
-        double *x = (double *)malloc(sizeof(double) * (size_t)(w + s + 1));
-        double *dp = (double *)malloc(sizeof(double) * (size_t)(w + s + 1));
-        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(w + s + 1));
+        double *x = (double *)malloc(sizeof(double) * (size_t)(N + s + 1));
+        double *dp = (double *)malloc(sizeof(double) * (size_t)(N + s + 1));
+        int64_t *key = (int64_t *)malloc(sizeof(int64_t) * (size_t)(N + s + 1));
         double *kr = (double *)malloc(sizeof(double) * (size_t)((N > 0 ? N : 1) * d));
         double *dkr = (double *)malloc(sizeof(double) * (size_t)((N > 0 ? N : 1) * d));
         double *dqr = (double *)malloc(sizeof(double) * (size_t)d);

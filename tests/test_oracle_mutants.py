@@ -41,6 +41,10 @@ MUTANTS = [
     ("bwd_inverse_rotation", "dqi[2 * t] = a * c + bb * sv;", "dqi[2 * t] = a * c - bb * sv;"),
     ("bwd_scale", "dqr[c] += scale * dx * kr[j * d + c];", "dqr[c] += dx * kr[j * d + c];"),
     ("bwd_value_gradient", "dvj[c] += p * gi[c];", "dvj[c] += dx * gi[c];"),
+    ("dilated_stride", "if ((i - j) % dil == 0 || j < s) key[n++] = j;",
+     "if ((i - j) % (dil + 1) == 0 || j < s) key[n++] = j;"),
+    ("dilated_span", "lo = i - dil * (w - 1) > 0 ? i - dil * (w - 1) : 0;",
+     "lo = i - dil * w > 0 ? i - dil * w : 0;"),
 ]
 
 PIN_TESTS = [
@@ -63,6 +67,8 @@ PIN_TESTS = [
     (pins.test_backward_matches_finite_differences,
      dict(mode=oracle.SOFTMAX, w=4, s=2, theta=1e4, alibi=True)),
     (pins.test_backward_window_of_one_closed_form, {}),
+    (pins.test_dilated_selection_readout, dict(N=33, w=7, s=9, r=4)),
+    (pins.test_dilated_selection_readout, dict(N=40, w=5, s=0, r=2)),
 ]
 
 

@@ -540,3 +540,56 @@ def test_backward_window_of_one_closed_form():
     dp = np.sum(g * v, axis=-1, keepdims=True)
     np.testing.assert_allclose(dq, sc * sig * (1 - sig) * dp * k, rtol=1e-12)
     np.testing.assert_allclose(dk, sc * sig * (1 - sig) * dp * q, rtol=1e-12)
+
+
+# ----------------------------------------------------------------------------- dilated windows
+
+@pytest.mark.parametrize("N,w,s,r", [(40, 5, 0, 2), (41, 4, 3, 3), (33, 7, 9, 4), (20, 1, 2, 2),
+                                     (30, 40, 0, 2)])
+def test_dilated_selection_readout(N, w, s, r):
+    """q = k = 0 and one-hot values: row i of the output selects, with weight 1/2 each, exactly
+    the keys of the dilated definition written as a brute-force predicate: w keys i, i - r,
+    ..., i - r (w - 1) that exist, plus every sink j < s at or before i."""
+    q = np.zeros((1, N, 1, N))
+    k = np.zeros((1, N, 1, N))
+    v = np.zeros((1, N, 1, N))
+    for j in range(N):
+        v[0, j, 0, j] = 1.0
+    sel = oracle.prefill(q, k, v, w=w, s=s, mode=oracle.SIGMOID, dilation=r)[0, :, 0, :]
+    for i in range(N):
+        keys = {i - r * m for m in range(w) if i - r * m >= 0} | {j for j in range(min(s, i + 1))}
+        want = np.zeros(N)
+        want[sorted(keys)] = 0.5
+        assert np.array_equal(sel[i], want), i
+
+
+@pytest.mark.parametrize("mode", [oracle.SIGMOID, oracle.SOFTMAX])
+@pytest.mark.parametrize("r", [2, 3])
+def test_dilated_is_plain_window_per_residue_class(mode, r):
+    """Without sinks, a dilated window is the plain window over each residue class of
+    positions: class c (positions c, c + r, ...) as its own sequence, with q and k rotated at
+    their true positions beforehand and the slopes scaled by r (the true distance is r times
+    the distance inside the class), gives the same rows."""
+    B, N, Hq, Hkv, d, w, theta = 1, 29, 2, 1, 8, 4, 1e4
+    q, k, v = _rand((B, N, Hq, d), 90), _rand((B, N, Hkv, d), 91), _rand((B, N, Hkv, d), 92)
+    slopes = [-0.3, 0.2]
+    full = oracle.prefill(q, k, v, w=w, mode=mode, slopes=slopes, rope_theta=theta, dilation=r)
+    qr, kr = dense.rope_dense(q, theta), dense.rope_dense(k, theta)
+    for c in range(r):
+        sub = oracle.prefill(qr[:, c::r], kr[:, c::r], v[:, c::r], w=w, mode=mode,
+                             slopes=[x * r for x in slopes])
+        np.testing.assert_allclose(full[:, c::r], sub, rtol=1e-12, atol=1e-13)
+
+
+def test_dilation_one_is_the_plain_window():
+    B, N, Hq, Hkv, d = 1, 25, 2, 2, 8
+    q, k, v = _rand((B, N, Hq, d), 93), _rand((B, N, Hkv, d), 94), _rand((B, N, Hkv, d), 95)
+    a = oracle.prefill(q, k, v, w=6, s=2, mode=oracle.SOFTMAX, rope_theta=1e4)
+    lib = oracle._load()
+    out = np.zeros_like(a)
+    qq, kk, vv = (np.ascontiguousarray(x) for x in (q, k, v))
+    rc = lib.swa_oracle_prefill_dilated(B, Hq, Hkv, N, d, 6, 2, 1, oracle.SOFTMAX, 0.0, None, 1e4,
+                                        oracle._ptr(qq), oracle._ptr(kk), oracle._ptr(vv), None, 0,
+                                        oracle._ptr(out))
+    assert rc == 0
+    np.testing.assert_array_equal(out, a)
