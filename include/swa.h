@@ -58,6 +58,12 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * scale <= 0 selects 1/sqrt(d). alibi_slopes: device float[H_q] of signed slopes, or NULL
  * for no bias (a zero slope also means no bias on that head). rope_table: device float
  * [rope_rows, d/2, 2] from swa_rope_table, or NULL for no rotation; rope_rows >= N.
+ * Dilated window (the dilated-window member of the sparse-attention family the Sliding
+ * Window Attention glossary lists beside SWA): with dilation r > 1 the window keeps every
+ * r-th position, K(i) = { j <= i : ((i - j) mod r = 0 and (i - j) / r < w) or j < s }, so w
+ * keys span r (w - 1) + 1 positions; the sinks are unchanged. The matrix-core path takes r a
+ * power of two (other r run on the general kernel); the training pair and the cache entry
+ * points take no dilation.
  * bf16 inputs with d in {64, 128} and 16-byte aligned tensors run on the matrix cores,
  * which form the score product from float16 operands (rotated q and k) and the value
  * product from float16 (softmax) or bf16 (sigmoid) operands, with float32 accumulation:
@@ -75,6 +81,7 @@ typedef struct swa_prefill_params {
     const float *alibi_slopes; /* device float[H_q] or NULL                            */
     const float *rope_table;   /* device float[rope_rows][d/2][2] (cos, sin) or NULL   */
     int64_t rope_rows;
+    int64_t dilation;          /* 0 or 1: contiguous window; r > 1: dilated (below)    */
 } swa_prefill_params;
 
 /*

@@ -40,7 +40,7 @@ class PrefillParams(ctypes.Structure):
     _fields_ = [("B", c_i64), ("H_q", c_i64), ("H_kv", c_i64), ("N", c_i64), ("d", c_i64),
                 ("w", c_i64), ("s", c_i64), ("mode", c_i32), ("in_dtype", c_i32),
                 ("out_dtype", c_i32), ("scale", c_f32), ("alibi_slopes", c_ptr),
-                ("rope_table", c_ptr), ("rope_rows", c_i64)]
+                ("rope_table", c_ptr), ("rope_rows", c_i64), ("dilation", c_i64)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -179,8 +179,9 @@ def swa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: int, s:
                 alibi_slopes: Optional[torch.Tensor] = None,
                 rope_table: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                 out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
-                stream=None) -> torch.Tensor:
+                stream=None, dilation: int = 1) -> torch.Tensor:
     """Sliding-window attention over whole sequences. q [B,N,H_q,d], k/v [B,N,H_kv,d].
+    dilation r > 1: the window keys are i, i - r, ..., i - r (w - 1) (plus the sinks).
 
     workspace: a device uint8 tensor of at least swa_prefill_workspace_bytes(...) bytes;
     allocated here when it is not given and the call needs one."""
@@ -210,7 +211,7 @@ def swa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: int, s:
             raise ValueError("rope_table must be float32 [rows, d/2, 2]")
         rows = rope_table.shape[0]
     p = PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), _dt(out), scale,
-                      _ptr(alibi_slopes), _ptr(rope_table), rows)
+                      _ptr(alibi_slopes), _ptr(rope_table), rows, dilation)
     lib = load()
     need = lib.swa_prefill_workspace_bytes(ctypes.byref(p))
     if workspace is None and need > 0:

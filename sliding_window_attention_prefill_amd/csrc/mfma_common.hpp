@@ -75,15 +75,18 @@ __device__ __forceinline__ constexpr int key_of(int kb, int e) {
 
 // Exclude the keys of an edge tile that are outside the key set: their logits become -inf
 // (weight 0 in both modes). Element (kb, e) is key j = jb + key_of(kb, e) with
-// i - j = dq - key_of(kb, e). SINKS adds the keys j < s at or before the query.
+// i - j = dq - key_of(kb, e). w is the window's extent in positions; with a dilation r (a
+// power of two, dmask = r - 1) only every r-th of them is a key. SINKS adds the keys j < s
+// at or before the query.
 template <bool SINKS>
-__device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, int w, int s) {
+__device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, int w, int s,
+                                          int dmask = 0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int dij = dq - key_of(kb, e);
-            bool ok = (unsigned)dij < (unsigned)w;   // 0 <= i - j < w
+            bool ok = ((unsigned)dij < (unsigned)w) & ((dij & dmask) == 0);   // 0 <= i - j < w
             if (SINKS) ok = ok | ((dij >= 0) & (jb + key_of(kb, e) < s));
             sacc[kb][e] = ok ? sacc[kb][e] : -INFINITY;
         }

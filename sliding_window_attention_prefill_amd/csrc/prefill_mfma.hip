@@ -121,7 +121,8 @@ struct MfmaParams {
     const float *rope;
     int64_t N, Hq, Hkv, G;
     int n_qtiles, n_hgroups, n_ktiles;
-    int w, s;                 // clamped to N
+    int w, s;                 // window extent in positions and sinks, clamped to N
+    int dmask;                // dilation - 1 (the window keeps every dilation-th position)
     float cs;                 // scale * log2(e)
     uint32_t kv_bytes;        // bytes of one (batch, kv head) K or V slice, rows [0, N)
     uint32_t row_bytes;       // bytes between consecutive positions of K/V
@@ -355,10 +356,10 @@ __device__ __forceinline__ void qk_tile(const uint16_t *__restrict__ kl, const L
 template <int D, int MODE, bool ALIBI>
 __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
                                             float &m_run, float &l_run, float cs, float bias_q,
-                                            int kind, int dq, int jb, int w, int s) {
+                                            int kind, int dq, int jb, int w, int s, int dmask) {
     constexpr int DB = D / 32;
-    if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s);
-    else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s);
+    if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, dmask);
+    else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s, dmask);
     if (MODE == 1) {
         // excluded keys stay -inf
 #pragma unroll
@@ -457,6 +458,7 @@ struct TileCtx {
     __amdgpu_buffer_rsrc_t rk, rv;
     uint32_t row_bytes;
     int tid, wave, qa, qb, i, g, w, s, N;
+    int dmask;                      // dilation - 1 (a power of two minus one; 0: contiguous)
     int n_tiles, ts_end, tw_begin;  // the walk: sink tiles [0, ts_end), then window tiles
     int ns_img, shift;              // tile t of the key positions is image tile img_of(t)
     uint32_t vtile_bytes;           // bytes between V tiles read as rows
@@ -474,7 +476,7 @@ struct TileCtx {
     // -1 = no pair in the key set (wave-uniform: this wavefront's queries [qa, qb])
     __device__ __forceinline__ int kind_of(int j0) const {
         if (qa >= N || j0 > qb || (qa - (j0 + BK - 1) >= w && j0 >= s)) return -1;
-        if ((j0 + BK - 1 <= qa) && (qb - j0 < w || j0 + BK - 1 < s)) return 0;
+        if ((j0 + BK - 1 <= qa) && ((qb - j0 < w && dmask == 0) || j0 + BK - 1 < s)) return 0;
         return j0 >= s ? 1 : 2;
     }
 };
@@ -520,7 +522,7 @@ __device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
     if (kind1 >= 0)
         prep_scores<D, MODE, ALIBI>(s_next, oacc, m_run, l_run, cx.cs,
                                     cx.slope_l2 * (float)(cx.i - j1), kind1,
-                                    cx.i - j1 - 4 * cx.g, j1 + 4 * cx.g, cx.w, cx.s);
+                                    cx.i - j1 - 4 * cx.g, j1 + 4 * cx.g, cx.w, cx.s, cx.dmask);
 }
 
 // Step t without pipelining: start the transfers of tile t + 1 (K and V) into the other
@@ -545,7 +547,7 @@ __device__ __forceinline__ void plain_step(uint16_t *__restrict__ k_fill,
         const float bq = cx.slope_l2 * (float)(cx.i - j0);
         qk_tile<D, ALIBI>(k_cur, lo, bo, qreg, sacc);
         prep_scores<D, MODE, ALIBI>(sacc, oacc, m_run, l_run, cx.cs, bq, kind,
-                                    cx.i - j0 - 4 * cx.g, j0 + 4 * cx.g, cx.w, cx.s);
+                                    cx.i - j0 - 4 * cx.g, j0 + 4 * cx.g, cx.w, cx.s, cx.dmask);
         weigh_pv<D, MODE, VF16>(v_cur, lo, sacc, oacc, m_run, l_run, cx.cs, bq);
     }
 }
@@ -636,7 +638,7 @@ void prefill_mfma_kernel(MfmaParams p) {
         cx.ns_img = ns_img; cx.shift = shift;
         cx.vtile_bytes = p.chunked ? (uint32_t)T::IMG_BYTES : (uint32_t)BK * p.row_bytes;
         cx.tid = tid; cx.wave = wave; cx.qa = qa; cx.qb = qa + 31 < N ? qa + 31 : N - 1;
-        cx.i = i; cx.g = g; cx.w = p.w; cx.s = p.s; cx.N = N;
+        cx.i = i; cx.g = g; cx.w = p.w; cx.s = p.s; cx.N = N; cx.dmask = p.dmask;
         cx.n_tiles = ts_end + (tw_end - tw_begin + 1);
         cx.ts_end = ts_end; cx.tw_begin = tw_begin;
         cx.cs = p.cs;
@@ -704,7 +706,7 @@ void prefill_mfma_kernel(MfmaParams p) {
                 qk_tile<D, ALIBI>(kbuf0, lo, bo, qreg, sa);
                 prep_scores<D, MODE, ALIBI>(sa, oacc, m_run, l_run, cx.cs,
                                             cx.slope_l2 * (float)(i - j0), kind0, i - j0 - 4 * g,
-                                            j0 + 4 * g, cx.w, cx.s);
+                                            j0 + 4 * g, cx.w, cx.s, cx.dmask);
             }
         }
         __syncthreads();
@@ -827,6 +829,7 @@ Plan plan_of(const PrefillArgs &a) {
 
 bool prefill_mfma_supported(const PrefillArgs &a) {
     if (a.in_dt != 1 || (a.d != 64 && a.d != 128)) return false;
+    if ((a.dil & (a.dil - 1)) != 0 || a.dil > (int64_t(1) << 24)) return false;
     if (a.B * a.N == 0) return true;
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
@@ -868,7 +871,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.n_qtiles = (int)((a.N + QP - 1) / QP);
     mp.n_hgroups = (int)(G / GP);
     mp.n_ktiles = (int)pl.n_ktiles;
-    mp.w = (int)(a.w < a.N ? a.w : a.N);
+    // positions the window spans (w - 1 < N keeps the product small)
+    const int64_t extent = a.w - 1 >= a.N ? a.N : a.dil * (a.w - 1) + 1;
+    mp.w = (int)(extent < a.N ? extent : a.N);
+    mp.dmask = (int)(a.dil - 1);
     mp.s = (int)(a.s < a.N ? a.s : a.N);
     mp.cs = a.scale * LOG2E;
     mp.kv_bytes = (uint32_t)(((a.N - 1) * a.Hkv + 1) * a.d * 2);

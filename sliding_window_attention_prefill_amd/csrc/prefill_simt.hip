@@ -17,7 +17,7 @@ namespace swa {
 namespace {
 
 struct SimtParams {
-    int64_t B, Hq, Hkv, N, d, w, s;
+    int64_t B, Hq, Hkv, N, d, w, s, dil;
     int mode;
     float scale;
     const float *slopes;
@@ -67,13 +67,16 @@ __global__ __launch_bounds__(256) void prefill_simt_kernel(SimtParams p, const v
     }
     if (p.rope) rotate_lanes(qv, lane, d, p.rope, i);
 
-    const int64_t lo = i - p.w + 1 > 0 ? i - p.w + 1 : 0;
+    // the window spans positions [lo, i]; with a dilation only every dil-th of them is a key
+    const int64_t span = p.w - 1 >= i ? i : p.dil * (p.w - 1);
+    const int64_t lo = i - span > 0 ? i - span : 0;
     const int64_t n_sink = p.s < lo ? p.s : lo;
     const int64_t n_keys = n_sink + (i - lo + 1);
     float m = -INFINITY, l = 0.0f;
 
     for (int64_t e = 0; e < n_keys; ++e) {
         const int64_t j = e < n_sink ? e : lo + (e - n_sink);
+        if (e >= n_sink && (i - j) % p.dil != 0 && j >= p.s) continue;   // wave-uniform
         const int64_t kbase = ((b * p.N + j) * p.Hkv + hk) * d;
         float kv[kMaxPerLane];
 #pragma unroll
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256) void prefill_simt_kernel(SimtParams p, const v
 template <int IN, int OUT>
 hipError_t launch_t(const PrefillArgs &a, const void *q, const void *k, const void *v, void *o,
                     hipStream_t st) {
-    SimtParams p{a.B, a.Hq, a.Hkv, a.N, a.d, a.w, a.s, a.mode, a.scale, a.slopes, a.rope};
+    SimtParams p{a.B, a.Hq, a.Hkv, a.N, a.d, a.w, a.s, a.dil, a.mode, a.scale, a.slopes, a.rope};
     const int64_t rows = a.B * a.N * a.Hq;
     const int64_t blocks = (rows + 3) / 4;
     hipLaunchKernelGGL((prefill_simt_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(256), 0, st,

@@ -32,7 +32,7 @@ float resolve_scale(float scale, int64_t d) {
 
 extern "C" {
 
-int swa_version(void) { return 400; }
+int swa_version(void) { return 500; }
 
 const char *swa_status_string(swa_status s) {
     switch (s) {
@@ -56,6 +56,7 @@ static swa_status check_prefill(const swa_prefill_params *p) {
         return SWA_ERR_INVALID_ARGUMENT;
     if (!std::isfinite(p->scale)) return SWA_ERR_INVALID_ARGUMENT;
     if (p->rope_table && p->rope_rows < p->N) return SWA_ERR_INVALID_ARGUMENT;
+    if (p->dilation < 0) return SWA_ERR_INVALID_ARGUMENT;
     if (p->d > 256) return SWA_ERR_UNSUPPORTED;
     // positions travel as float-exact integers and 32-bit grid dimensions
     if (p->N > (int64_t(1) << 24)) return SWA_ERR_UNSUPPORTED;
@@ -65,7 +66,8 @@ static swa_status check_prefill(const swa_prefill_params *p) {
 static swa::PrefillArgs prefill_args(const swa_prefill_params *p) {
     return swa::PrefillArgs{p->B, p->H_q, p->H_kv, p->N, p->d, p->w, p->s, p->mode,
                             p->in_dtype, p->out_dtype, resolve_scale(p->scale, p->d),
-                            p->alibi_slopes, p->rope_table, p->rope_table ? p->rope_rows : 0};
+                            p->alibi_slopes, p->rope_table, p->rope_table ? p->rope_rows : 0,
+                            p->dilation > 1 ? p->dilation : 1};
 }
 
 size_t swa_prefill_workspace_bytes(const swa_prefill_params *p) {
@@ -105,7 +107,7 @@ static swa_status check_train(const swa_prefill_params *p, std::initializer_list
     const swa_status chk = check_prefill(p);
     if (chk != SWA_OK) return chk;
     const swa::PrefillArgs a = prefill_args(p);
-    if (!swa::prefill_mfma_supported(a)) return SWA_ERR_UNSUPPORTED;
+    if (!swa::prefill_mfma_supported(a) || a.dil != 1) return SWA_ERR_UNSUPPORTED;
     uintptr_t bits = reinterpret_cast<uintptr_t>(p->rope_table);
     for (const void *x : ptrs) bits |= reinterpret_cast<uintptr_t>(x);
     if (bits & 15) return SWA_ERR_UNSUPPORTED;
@@ -133,7 +135,7 @@ swa_status swa_prefill_train(const swa_prefill_params *p, const void *q, const v
 size_t swa_prefill_backward_workspace_bytes(const swa_prefill_params *p) {
     if (check_prefill(p) != SWA_OK) return 0;
     const swa::PrefillArgs a = prefill_args(p);
-    if (!swa::prefill_mfma_supported(a)) return 0;
+    if (!swa::prefill_mfma_supported(a) || a.dil != 1) return 0;
     return swa::prefill_bwd_workspace_bytes(a);
 }
 

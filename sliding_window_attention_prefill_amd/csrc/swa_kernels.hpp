@@ -16,6 +16,7 @@ struct PrefillArgs {
     const float *slopes;
     const float *rope;  // [rope_rows, d/2, 2] or null
     int64_t rope_rows;
+    int64_t dil;        // window dilation (1: contiguous)
 };
 
 struct CacheArgs {

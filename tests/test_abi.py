@@ -246,3 +246,15 @@ def test_backward_workspace_bytes(lib):
     assert wsb(**big) == 2 * B * Hkv * tiles * 64 * d * 2 + 2 * B * Hq * tiles * 64 * d * 2 + \
         2 * B * Hkv * 128 * d * 4
     assert wsb(in_dtype=0) == 0 and wsb(d=96) == 0 and wsb(B=0) == 0
+
+
+def test_dilation_arguments(lib):
+    """A negative dilation is rejected; the training pair takes no dilation."""
+    assert lib.swa_prefill(ctypes.byref(_params(dilation=-1)), DUMMY, DUMMY, DUMMY, DUMMY, None,
+                           0, None) == 1
+    assert lib.swa_prefill_train(ctypes.byref(_params(dilation=2)), DUMMY, DUMMY, DUMMY, DUMMY,
+                                 DUMMY, None, 0, None) == 2
+    assert lib.swa_prefill_backward_workspace_bytes(ctypes.byref(_params(dilation=2))) == 0
+    # the workspace of the forward does not depend on the dilation
+    assert lib.swa_prefill_workspace_bytes(ctypes.byref(_params(dilation=4))) == \
+        lib.swa_prefill_workspace_bytes(ctypes.byref(_params()))
