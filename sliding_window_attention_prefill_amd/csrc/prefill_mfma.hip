@@ -353,13 +353,14 @@ __device__ __forceinline__ void qk_tile(const uint16_t *__restrict__ kl, const L
 // masking, and for softmax the base-2 logits x log2(e) = cs * acc + bias_q
 // (bias_q = slope log2(e) (i - j0), zero without ALiBi) with the running maximum and the
 // lazy rescale of the accumulator.
-template <int D, int MODE, bool ALIBI>
+template <int D, int MODE, bool ALIBI, bool DIL>
 __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
                                             float &m_run, float &l_run, float cs, float bias_q,
                                             int kind, int dq, int jb, int w, int s, int dmask) {
     constexpr int DB = D / 32;
-    if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, dmask);
-    else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s, dmask);
+    // the stride test exists only in the dilated instantiations
+    if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, DIL ? dmask : 0);
+    else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s, DIL ? dmask : 0);
     if (MODE == 1) {
         // excluded keys stay -inf
 #pragma unroll
@@ -501,7 +502,7 @@ __device__ __forceinline__ void load_v(uint16_t *__restrict__ dst, const TileCtx
 // tile t, and prepares tile t + 1's scores.
 // The four buffers are distinct restrict pointers, so no LDS read here waits for the
 // transfers this step starts.
-template <int D, int MODE, bool ALIBI, bool VF16>
+template <int D, int MODE, bool ALIBI, bool VF16, bool DIL>
 __device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
                                           uint16_t *__restrict__ v_fill,
                                           const uint16_t *__restrict__ k_next,
@@ -520,14 +521,14 @@ __device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
     if (kind1 >= 0) qk_tile<D, ALIBI>(k_next, lo, bo, qreg, s_next);
     if (kind0 >= 0) weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run, cx.cs, bq0);
     if (kind1 >= 0)
-        prep_scores<D, MODE, ALIBI>(s_next, oacc, m_run, l_run, cx.cs,
+        prep_scores<D, MODE, ALIBI, DIL>(s_next, oacc, m_run, l_run, cx.cs,
                                     cx.slope_l2 * (float)(cx.i - j1), kind1,
                                     cx.i - j1 - 4 * cx.g, j1 + 4 * cx.g, cx.w, cx.s, cx.dmask);
 }
 
 // Step t without pipelining: start the transfers of tile t + 1 (K and V) into the other
 // buffer pair, then form, prepare and weigh tile t. Fewer live registers than pipe_step.
-template <int D, int MODE, bool ALIBI, bool VF16>
+template <int D, int MODE, bool ALIBI, bool VF16, bool DIL>
 __device__ __forceinline__ void plain_step(uint16_t *__restrict__ k_fill,
                                            uint16_t *__restrict__ v_fill,
                                            const uint16_t *__restrict__ k_cur,
@@ -546,7 +547,7 @@ __device__ __forceinline__ void plain_step(uint16_t *__restrict__ k_fill,
         f32x16_t sacc[2];
         const float bq = cx.slope_l2 * (float)(cx.i - j0);
         qk_tile<D, ALIBI>(k_cur, lo, bo, qreg, sacc);
-        prep_scores<D, MODE, ALIBI>(sacc, oacc, m_run, l_run, cx.cs, bq, kind,
+        prep_scores<D, MODE, ALIBI, DIL>(sacc, oacc, m_run, l_run, cx.cs, bq, kind,
                                     cx.i - j0 - 4 * cx.g, j0 + 4 * cx.g, cx.w, cx.s, cx.dmask);
         weigh_pv<D, MODE, VF16>(v_cur, lo, sacc, oacc, m_run, l_run, cx.cs, bq);
     }
@@ -571,7 +572,7 @@ __device__ void nan_rows(const MfmaParams &p, const ChunkSeq &cs, int r_first, i
 
 // Register budget: 4 wavefronts per SIMD at d = 64 (3 with four heads per workgroup, which
 // keeps more per-head state), 2 at d = 128.
-template <int D, int GP, int MODE, bool ALIBI, bool VF16>
+template <int D, int GP, int MODE, bool ALIBI, bool VF16, bool DIL>
 __global__ __launch_bounds__(64 * Tile<D>::NW)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? (GP < 4 ? 4 : 3) : 2)))
 void prefill_mfma_kernel(MfmaParams p) {
@@ -704,7 +705,7 @@ void prefill_mfma_kernel(MfmaParams p) {
             const int j0 = cx.j0_of(0), kind0 = cx.kind_of(j0);
             if (kind0 >= 0) {
                 qk_tile<D, ALIBI>(kbuf0, lo, bo, qreg, sa);
-                prep_scores<D, MODE, ALIBI>(sa, oacc, m_run, l_run, cx.cs,
+                prep_scores<D, MODE, ALIBI, DIL>(sa, oacc, m_run, l_run, cx.cs,
                                             cx.slope_l2 * (float)(i - j0), kind0, i - j0 - 4 * g,
                                             j0 + 4 * g, cx.w, cx.s, cx.dmask);
             }
@@ -713,11 +714,11 @@ void prefill_mfma_kernel(MfmaParams p) {
 
         // ---- tile t lives in K/V buffer t % 2; two steps per trip keep the score registers
         for (int t = 0; t < cx.n_tiles; t += 2) {
-            pipe_step<D, MODE, ALIBI, VF16>(kbuf0, vbuf1, kbuf1, vbuf0, cx, lo, bo, qreg, sa, sb,
+            pipe_step<D, MODE, ALIBI, VF16, DIL>(kbuf0, vbuf1, kbuf1, vbuf0, cx, lo, bo, qreg, sa, sb,
                                             oacc, m_run, l_run, t);
             __syncthreads();
             if (t + 1 >= cx.n_tiles) break;
-            pipe_step<D, MODE, ALIBI, VF16>(kbuf1, vbuf0, kbuf0, vbuf1, cx, lo, bo, qreg, sb, sa,
+            pipe_step<D, MODE, ALIBI, VF16, DIL>(kbuf1, vbuf0, kbuf0, vbuf1, cx, lo, bo, qreg, sb, sa,
                                             oacc, m_run, l_run, t + 1);
             __syncthreads();
         }
@@ -726,11 +727,11 @@ void prefill_mfma_kernel(MfmaParams p) {
         load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
         __syncthreads();
         for (int t = 0; t < cx.n_tiles; t += 2) {
-            plain_step<D, MODE, ALIBI, VF16>(kbuf1, vbuf1, kbuf0, vbuf0, cx, lo, bo, qreg, oacc,
+            plain_step<D, MODE, ALIBI, VF16, DIL>(kbuf1, vbuf1, kbuf0, vbuf0, cx, lo, bo, qreg, oacc,
                                              m_run, l_run, t);
             __syncthreads();
             if (t + 1 >= cx.n_tiles) break;
-            plain_step<D, MODE, ALIBI, VF16>(kbuf0, vbuf0, kbuf1, vbuf1, cx, lo, bo, qreg, oacc,
+            plain_step<D, MODE, ALIBI, VF16, DIL>(kbuf0, vbuf0, kbuf1, vbuf1, cx, lo, bo, qreg, oacc,
                                              m_run, l_run, t + 1);
             __syncthreads();
         }
@@ -781,12 +782,14 @@ void prefill_mfma_kernel(MfmaParams p) {
 
 template <int D, int GP, int MODE, bool VF16>
 hipError_t launch_main(const MfmaParams &mp, int nblocks, bool alibi, hipStream_t st) {
-    if (alibi)
-        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, true, VF16>), dim3((unsigned)nblocks),
-                           dim3(64 * Tile<D>::NW), 0, st, mp);
-    else
-        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, false, VF16>), dim3((unsigned)nblocks),
-                           dim3(64 * Tile<D>::NW), 0, st, mp);
+    const dim3 grid((unsigned)nblocks), block(64 * Tile<D>::NW);
+    if (mp.dmask != 0) {
+        if (alibi) hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, true, VF16, true>), grid, block, 0, st, mp);
+        else hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, false, VF16, true>), grid, block, 0, st, mp);
+    } else {
+        if (alibi) hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, true, VF16, false>), grid, block, 0, st, mp);
+        else hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, MODE, false, VF16, false>), grid, block, 0, st, mp);
+    }
     return hipGetLastError();
 }
 
