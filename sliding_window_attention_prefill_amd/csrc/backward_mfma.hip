@@ -32,13 +32,16 @@
 namespace swa {
 namespace {
 
-// Chunk c of tile row r is stored at chunk c ^ bswz(r). Row reads touch 16 rows at one chunk
-// and transposing reads 4 rows x 2 chunks per 16 lanes; this swizzle keeps both free of LDS
-// bank conflicts (rows of 256 bytes at d = 128, two rows per 256 bytes at d = 64).
+// Chunk c of tile row r is stored at chunk c ^ bswz(r). A row read serves 16 rows at one
+// chunk per group of 16 lanes; a transposing read serves 4 consecutive rows x 4 adjacent
+// chunks per group of 32 lanes. This swizzle keeps both free of LDS bank conflicts: it is a
+// permutation of 16 consecutive rows (of 8 rows per row parity at d = 64, where two rows
+// share a 256-byte bank line), and it sends the 4 rows of a transposing read to 4 different
+// aligned groups of 4 chunks.
 template <int D>
 __host__ __device__ __forceinline__ constexpr int bswz(int r) {
-    return D == 128 ? ((r & 8) | ((r & 3) << 1) | ((r >> 2) & 1))
-                    : ((r & 2) | ((r >> 2) & 1) | ((r >> 1) & 4));
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                    : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 template <int D>
@@ -675,6 +678,266 @@ void bwd_dkv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// dk, dv with each 32-key block's work split over two wavefronts (eight per workgroup, two
+// per SIMD): wavefront w < 4 forms the scores and weights P of its keys, publishes P (float16)
+// in LDS and accumulates dV^T += dO^T P; wavefront w + 4 forms dP = dO V^T, takes P from LDS,
+// forms dX and accumulates dK~^T += Q~^T dX. Each role holds one fragment (K or V) and one
+// accumulator, half the registers of the single-wavefront form, so two wavefronts share a SIMD.
+template <int D, int MODE, bool ALIBI, bool SINK>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkv2_kernel(BwdParams p) {
+    using T = BT<D>;
+    constexpr int KS = D / 16, DB = D / 32;
+    constexpr int NWG = 8;
+    constexpr int DMA_R = T::IMG_BYTES / (NWG * 1024);   // 1 KB transfers per wavefront
+    constexpr int STAGE = 2 * T::IMG + 256;              // Q tile, dO tile, 64 row statistics
+    constexpr int PX = 4 * 2 * 64 * 16;                  // P: 4 key blocks x 2 row blocks x 64 lanes x 16
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE + PX];
+    uint16_t *const px = lds + 2 * STAGE;
+
+    int b, hkv, kblk, split = 0;
+    {
+        int rest = xcd_logical();
+        if (SINK) {
+            split = rest % p.n_splits;
+            rest /= p.n_splits;
+            kblk = rest % p.sink_blocks;
+            rest /= p.sink_blocks;
+        } else {
+            kblk = rest % p.n_kblocks;
+            rest /= p.n_kblocks;
+        }
+        hkv = rest % (int)p.Hkv;
+        b = rest / (int)p.Hkv;
+    }
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int g = lane >> 5;
+    const bool role_p = wave < 4;                 // P and dV; else dP, dX and dK
+    const int kw = wave & 3;                      // this wavefront's 32-key block
+    const int N = (int)p.N;
+    const int j0 = kblk * T::KP;
+    const int jw = j0 + 32 * kw;
+    const int j = jw + (lane & 31);
+    const int win_end = j0 + T::KP - 1 + p.w < N ? j0 + T::KP - 1 + p.w : N;
+    int qlo, qhi;
+    if (SINK) {
+        qlo = win_end + split * p.split_tiles * BK;
+        qhi = qlo + p.split_tiles * BK < N ? qlo + p.split_tiles * BK : N;
+        if (qlo >= N) return;
+    } else {
+        qlo = j0;
+        qhi = win_end;
+    }
+    const int t_lo = qlo / BK, t_hi = (qhi - 1) / BK;
+    const int n_steps = (t_hi - t_lo + 1) * (int)p.G;
+    const bool active = !SINK || jw < p.s;
+
+    const uint32_t qslice_bytes = (uint32_t)p.n_tiles * T::IMG_BYTES;
+    uint32_t dimg[DMA_R];
+#pragma unroll
+    for (int r = 0; r < DMA_R; ++r) dimg[r] = (uint32_t)((wave * DMA_R + r) * 64 + lane) * 16;
+    int qoff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qoff[ks] = slot_of<D>(lane & 31, 2 * ks + g);
+    int toff[2][DB];
+    tr_offsets<D>(lane, toff);
+
+    // this lane's key (P role) or value (dX role) fragment
+    f16x8_t kv[KS];
+    {
+        const uint16_t *img = role_p ? p.kimg : p.vimg;
+        const int64_t slice = ((int64_t)b * p.Hkv + hkv) * p.n_tiles * T::IMG;
+        const int jt = j / BK, rj = j % BK;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            uint4 x = make_uint4(0, 0, 0, 0);
+            if (j < N) x = ldg16(img + slice + (int64_t)jt * T::IMG + slot_of<D>(rj, 2 * ks + g));
+            kv[ks] = __builtin_bit_cast(f16x8_t, x);
+        }
+    }
+    f32x16_t acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
+
+    auto load = [&](int n, int buf) {
+        const int qt = t_lo + n / (int)p.G;
+        const int64_t hq = (int64_t)hkv * p.G + n % (int)p.G;
+        const int64_t slice = ((int64_t)b * p.Hq + hq) * p.n_tiles * T::IMG;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qimg + slice, qslice_bytes);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.gimg + slice, qslice_bytes);
+        uint16_t *st = lds + buf * STAGE;
+        dma_rounds<DMA_R>(st, rq, (uint32_t)qt * T::IMG_BYTES, dimg, wave);
+        dma_rounds<DMA_R>(st + T::IMG, rg, (uint32_t)qt * T::IMG_BYTES, dimg, wave);
+        if (MODE == 1 && wave == 0 && lane < 32) {
+            const float *src = p.stats + (((int64_t)b * p.Hq + hq) * p.n_tiles * BK + (int64_t)qt * BK) * 2;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, 512);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(st + 2 * T::IMG), 16,
+                                                     (uint32_t)lane * 16, 0, 0, 0);
+        }
+    };
+
+    load(0, 0);
+    __syncthreads();
+    for (int n = 0; n < n_steps; ++n) {
+        const int cur = n & 1;
+        if (n + 1 < n_steps) load(n + 1, cur ^ 1);
+        const int qt = t_lo + n / (int)p.G;
+        const int64_t hq = (int64_t)hkv * p.G + n % (int)p.G;
+        const int i0 = qt * BK;
+        const int ilo = i0 > qlo ? i0 : qlo, ihi = (i0 + BK < qhi ? i0 + BK : qhi) - 1;
+        const bool any = active && ilo <= ihi && ihi >= jw &&
+                         ((ilo - (jw + 31) < p.w) || jw < p.s);
+        const bool all = ilo == i0 && ihi == i0 + BK - 1 && i0 >= jw + 31 &&
+                         ((i0 + BK - 1 - jw < p.w) || jw + 31 < p.s) && jw + 31 < N;
+        const uint16_t *ql = lds + cur * STAGE;
+        const uint16_t *gl = ql + T::IMG;
+        const float *stl = reinterpret_cast<const float *>(ql + 2 * T::IMG);
+        // this lane's P of row block qb: values 0..7 at pxw + qb * 1024, 8..15 at + 512
+        uint16_t *pxw = px + (kw * 2) * 64 * 16 + lane * 8;
+        f32x16_t sd[2];                                       // P (P role) or dP (dX role)
+        if (any) {
+            const float slope_l2 = ALIBI ? p.slopes[hq] * LOG2E : 0.0f;
+            const BiasOperands bo = bias_operands(ALIBI ? -slope_l2 / p.cs : 0.0f, lane);
+            const float lb = slope_l2 * (float)(i0 - j);   // key part of the bias
+            const uint16_t *al = role_p ? ql : gl;          // A rows: Q for S, dO for dP
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const f32x16_t zero = {};
+                f32x16_t a = (ALIBI && role_p) ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[qb], bo.b, zero, 0, 0, 0) : zero;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const f16x8_t ar = *reinterpret_cast<const f16x8_t *>(al + qb * 32 * D + qoff[ks]);
+                    a = __builtin_amdgcn_mfma_f32_32x32x16_f16(ar, kv[ks], a, 0, 0, 0);
+                }
+                sd[qb] = a;
+            }
+            if (role_p) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r0 = 32 * qb + 8 * u + 4 * g;
+                        float4 st0 = make_float4(0.f, 0.f, 0.f, 0.f), st1 = st0;
+                        if (MODE == 1) {
+                            st0 = *reinterpret_cast<const float4 *>(stl + 2 * r0);
+                            st1 = *reinterpret_cast<const float4 *>(stl + 2 * r0 + 4);
+                        }
+                        const float l2v[4] = {st0.x, st0.z, st1.x, st1.z};
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            const int e = 4 * u + e4;
+                            const int iq = i0 + r0 + e4;
+                            float x = sd[qb][e];
+                            if (!all) {
+                                const int dij = iq - j;
+                                const bool ok = iq >= qlo && iq < qhi && iq < N && j < N && dij >= 0 &&
+                                                (dij < p.w || j < p.s);
+                                x = ok ? x : -INFINITY;
+                            }
+                            sd[qb][e] = MODE == 0
+                                ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(x, -p.cs, -lb)))
+                                : __builtin_amdgcn_exp2f(fmaf(x, p.cs, lb) - l2v[e4]);
+                        }
+                    }
+                    uint4 w0, w1;
+                    w0.x = pack_f16x2(sd[qb][0], sd[qb][1]);   w0.y = pack_f16x2(sd[qb][2], sd[qb][3]);
+                    w0.z = pack_f16x2(sd[qb][4], sd[qb][5]);   w0.w = pack_f16x2(sd[qb][6], sd[qb][7]);
+                    w1.x = pack_f16x2(sd[qb][8], sd[qb][9]);   w1.y = pack_f16x2(sd[qb][10], sd[qb][11]);
+                    w1.z = pack_f16x2(sd[qb][12], sd[qb][13]); w1.w = pack_f16x2(sd[qb][14], sd[qb][15]);
+                    *reinterpret_cast<uint4 *>(pxw + qb * 64 * 16) = w0;
+                    *reinterpret_cast<uint4 *>(pxw + qb * 64 * 16 + 64 * 8) = w1;
+                }
+            }
+        }
+        __syncthreads();   // P of every key block published
+        if (any) {
+            if (role_p) {
+                acc_tr<D>(gl, 0, toff, sd[0], acc);   // dV^T += dO^T P
+                acc_tr<D>(gl, 1, toff, sd[1], acc);
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    const uint4 w0 = *reinterpret_cast<const uint4 *>(pxw + qb * 64 * 16);
+                    const uint4 w1 = *reinterpret_cast<const uint4 *>(pxw + qb * 64 * 16 + 64 * 8);
+                    const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r0 = 32 * qb + 8 * u + 4 * g;
+                        float4 st0 = make_float4(0.f, 0.f, 0.f, 0.f), st1 = st0;
+                        if (MODE == 1) {
+                            st0 = *reinterpret_cast<const float4 *>(stl + 2 * r0);
+                            st1 = *reinterpret_cast<const float4 *>(stl + 2 * r0 + 4);
+                        }
+                        const float dlv[4] = {st0.y, st0.w, st1.y, st1.w};
+#pragma unroll
+                        for (int e4 = 0; e4 < 4; ++e4) {
+                            const int e = 4 * u + e4;
+                            const f16x2_t h2 = __builtin_bit_cast(f16x2_t, wv[e >> 1]);
+                            const float pe = (float)h2[e & 1];
+                            sd[qb][e] = MODE == 0 ? sd[qb][e] * pe * (1.0f - pe)
+                                                  : pe * (sd[qb][e] - dlv[e4]);
+                        }
+                    }
+                    acc_tr<D>(ql, qb, toff, sd[qb], acc);   // dK~^T += Q~^T dX
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue: the P role owns dv, the dX role dk
+    const int64_t sk = (int64_t)p.sink_blocks * T::KP;
+    float *sink = role_p ? p.sink_v : p.sink_k;
+    if (SINK) {
+        if (!active) return;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
+                atomicAdd(sink + (((int64_t)b * p.Hkv + hkv) * sk + j) * D + d, acc[db][e]);
+            }
+        return;
+    }
+    if (j >= N) return;
+    if (sink != nullptr && kblk < p.sink_blocks) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
+                acc[db][e] += sink[(((int64_t)b * p.Hkv + hkv) * sk + j) * D + d];
+            }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d0 = 32 * db + 8 * r + 4 * g;
+            float x0 = acc[db][4 * r], x1 = acc[db][4 * r + 1];
+            float x2 = acc[db][4 * r + 2], x3 = acc[db][4 * r + 3];
+            if (!role_p) {
+                x0 *= p.scale; x1 *= p.scale; x2 *= p.scale; x3 *= p.scale;
+                if (p.rope != nullptr) {
+                    const float4 c = as_float4(ldg16(p.rope + ((int64_t)j * (D / 2) + d0 / 2) * 2));
+                    const float2 u0 = unrotate(x0, x1, make_float2(c.x, c.y));
+                    const float2 u1 = unrotate(x2, x3, make_float2(c.z, c.w));
+                    x0 = u0.x; x1 = u0.y; x2 = u1.x; x3 = u1.y;
+                }
+            }
+            void *dst = role_p ? p.dv : p.dk;
+            const int64_t off = (((int64_t)b * p.N + j) * p.Hkv + hkv) * D + d0;
+            if (p.out_bf16)
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst) + off) =
+                    make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
+            else
+                *reinterpret_cast<float4 *>(static_cast<float *>(dst) + off) = make_float4(x0, x1, x2, x3);
+        }
+}
+
+// ---------------------------------------------------------------------------------------
 // Host side.
 struct BwdPlan {
     int64_t n_tiles;
@@ -706,11 +969,20 @@ int gp_of(int64_t G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 template <int D, int MODE, bool ALIBI>
 hipError_t launch_kernels(const BwdParams &bp, int n_dq, int n_dkv, int n_sink, int GP,
                           hipStream_t st) {
-    if (n_sink > 0)
-        hipLaunchKernelGGL((bwd_dkv_kernel<D, MODE, ALIBI, true>), dim3((unsigned)n_sink),
+    if (D == 128) {
+        // two wavefronts per 32-key block (see bwd_dkv2_kernel)
+        if (n_sink > 0)
+            hipLaunchKernelGGL((bwd_dkv2_kernel<D, MODE, ALIBI, true>), dim3((unsigned)n_sink),
+                               dim3(512), 0, st, bp);
+        hipLaunchKernelGGL((bwd_dkv2_kernel<D, MODE, ALIBI, false>), dim3((unsigned)n_dkv),
+                           dim3(512), 0, st, bp);
+    } else {
+        if (n_sink > 0)
+            hipLaunchKernelGGL((bwd_dkv_kernel<D, MODE, ALIBI, true>), dim3((unsigned)n_sink),
+                               dim3(256), 0, st, bp);
+        hipLaunchKernelGGL((bwd_dkv_kernel<D, MODE, ALIBI, false>), dim3((unsigned)n_dkv),
                            dim3(256), 0, st, bp);
-    hipLaunchKernelGGL((bwd_dkv_kernel<D, MODE, ALIBI, false>), dim3((unsigned)n_dkv), dim3(256),
-                       0, st, bp);
+    }
     if (GP == 4)
         hipLaunchKernelGGL((bwd_dq_kernel<D, 4, MODE, ALIBI>), dim3((unsigned)n_dq), dim3(256), 0, st, bp);
     else if (GP == 2)
