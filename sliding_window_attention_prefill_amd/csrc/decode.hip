@@ -241,12 +241,16 @@ struct DecLds {
     static constexpr int KG = 256 / C8;       // key groups of the value pass
     static constexpr int VK = DEC_KC / KG;    // keys per thread in the value pass
     static constexpr int QE = D / 4;          // elements per thread in the score pass
+    // a head's query is kept as four quarters of QE values, each padded by 4 floats, so the
+    // four quarters that one wavefront reads at once sit in different banks
+    static constexpr int QQ = QE + 4;         // floats per stored quarter
+    static constexpr int QG = 4 * QQ;         // floats per stored head
 };
 
 template <int D>
 size_t decode_fast_lds(int G) {
     using L = DecLds<D>;
-    return sizeof(float) * ((size_t)G * D + (size_t)G * DEC_KC + 2 * D + 3 * 8 +
+    return sizeof(float) * ((size_t)G * L::QG + (size_t)G * DEC_KC + 2 * D + 3 * 8 +
                             (size_t)L::KG * G * D);
 }
 
@@ -267,8 +271,8 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
                                                           const uint16_t *__restrict__ v_new) {
     using L = DecLds<D>;
     extern __shared__ float lds[];
-    float *qs = lds;                    // [G][D] rotated queries * scale * log2(e)
-    float *sc = qs + G * D;             // [G][KC] scores, then weights
+    float *qs = lds;                    // [G][4][QQ] rotated queries * scale * log2(e)
+    float *sc = qs + G * L::QG;         // [G][KC] scores, then weights
     float *kn = sc + G * DEC_KC;        // [D] appended key (as stored)
     float *vn = kn + D;                 // [D] appended value
     float *ml = vn + D;                 // [3][8] max, sum, correction per head
@@ -330,8 +334,9 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
             x1 = fmaf(x0, cs.y, x1 * cs.x);
             x0 = r0;
         }
-        qs[g * D + 2 * t] = x0 * a.cs;
-        qs[g * D + 2 * t + 1] = x1 * a.cs;
+        const int col = 2 * t;   // a quarter holds QE consecutive columns
+        qs[g * L::QG + (col / L::QE) * L::QQ + col % L::QE] = x0 * a.cs;
+        qs[g * L::QG + (col / L::QE) * L::QQ + col % L::QE + 1] = x1 * a.cs;
     }
     if (tid < 8) {
         ml[tid] = -INFINITY;
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
             for (int g = 0; g < G; ++g) {
                 float acc_d = 0.0f;
 #pragma unroll
-                for (int c = 0; c < L::QE; ++c) acc_d = fmaf(qs[g * D + qq * L::QE + c], kf[c], acc_d);
+                for (int c = 0; c < L::QE; ++c) acc_d = fmaf(qs[g * L::QG + qq * L::QQ + c], kf[c], acc_d);
                 part[g] = acc_d;
             }
 #pragma unroll
