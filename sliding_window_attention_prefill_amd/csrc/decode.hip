@@ -346,6 +346,13 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
     const int lo = lo_w;
     const int n_sink = a.s < lo ? a.s : lo;
     const int n_keys = k_end;
+    // ring slot of window position lo + m (0 <= m < w): lo mod w + m, less w past the end
+    // (rows past the key list, which are never read, get slot 0)
+    const int slot_lo = lo % a.w;
+    auto ring_slot = [&](int P) {
+        const int sl = slot_lo + (P - lo);
+        return sl < a.w ? sl : (sl - a.w < a.w ? sl - a.w : 0);
+    };
 
     // value-pass ownership: 8 columns, keys kg, kg + KG, ...
     const int c8 = tid % L::C8, kg = tid / L::C8;
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
             kpos[r] = P;
             const bool from_mem = e < nk && !(APPEND && P == p);
             const uint16_t *row = ee < n_sink ? a.k_sink + sink_base + (int64_t)P * D
-                                              : a.k_ring + ring_base + (int64_t)(P % a.w) * D;
+                                              : a.k_ring + ring_base + (int64_t)ring_slot(P) * D;
 #pragma unroll
             for (int u = 0; u < L::QE / 8; ++u)
                 kx[r][u] = from_mem ? ld16(row + qq * L::QE + 8 * u) : make_uint4(0, 0, 0, 0);
@@ -388,7 +395,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const ui
             vpos[r] = P;
             const bool from_mem = e < nk && !(APPEND && P == p);
             const uint16_t *row = ee < n_sink ? a.v_sink + sink_base + (int64_t)P * D
-                                              : a.v_ring + ring_base + (int64_t)(P % a.w) * D;
+                                              : a.v_ring + ring_base + (int64_t)ring_slot(P) * D;
             vx[r] = from_mem ? ld16(row + 8 * c8) : make_uint4(0, 0, 0, 0);
         }
     };
@@ -703,7 +710,10 @@ __global__ __launch_bounds__(NT) void decode_window_kernel(DecodeFast a, const u
             int P;
             bool inset;
             if (e < a.w) {
-                P = p - ((p - e) % a.w + a.w) % a.w;
+                // ring slot e holds p - ((p - e) mod w); with slot_new = p mod w and e < w
+                // that distance is slot_new - e, or slot_new - e + w when negative
+                const int dist = slot_new >= e ? slot_new - e : slot_new - e + a.w;
+                P = p - dist;
                 inset = e < NK && P >= 0;
             } else {
                 P = e - a.w;
