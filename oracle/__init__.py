@@ -69,6 +69,10 @@ def bind(path: str):
     lib.swa_oracle_backward.argtypes = [i64, i64, i64, i64, i64, i64, i64, ctypes.c_int, dbl,
                                         dp, dbl, dp, dp, dp, dp, dp, dp, dp]
     lib.swa_oracle_backward.restype = ctypes.c_int
+    lib.swa_oracle_backward_dilated.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64,
+                                                ctypes.c_int, dbl, dp, dbl, dp, dp, dp, dp, dp,
+                                                dp, dp]
+    lib.swa_oracle_backward_dilated.restype = ctypes.c_int
     lib.swa_oracle_ring_fill_positions.argtypes = [i64, i64, ip]
     lib.swa_oracle_ring_fill_positions.restype = None
     lib.swa_oracle_threads.argtypes = []
@@ -148,18 +152,25 @@ def prefill(q, k, v, *, w: int, s: int = 0, mode: int = SIGMOID, scale: float = 
 
 
 def backward(q, k, v, dout, *, w: int, s: int = 0, mode: int = SIGMOID, scale: float = 0.0,
-             slopes=None, rope_theta: float = 0.0):
+             slopes=None, rope_theta: float = 0.0, dilation: int = 1):
     """float64 gradients (dq, dk, dv) of prefill for the output gradient dout [B,N,H_q,d]
-    (swa_oracle_backward)."""
+    (swa_oracle_backward; with dilation r > 1 the dilated window's,
+    swa_oracle_backward_dilated)."""
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     assert k.shape == (B, N, Hkv, d) and v.shape == k.shape and g.shape == q.shape
     sl = None if slopes is None else _f64(slopes)
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
-    rc = _load().swa_oracle_backward(B, Hq, Hkv, N, d, w, s, mode, float(scale), _ptr(sl),
-                                     float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                     _ptr(dq), _ptr(dk), _ptr(dv))
+    if dilation == 1:
+        rc = _load().swa_oracle_backward(B, Hq, Hkv, N, d, w, s, mode, float(scale), _ptr(sl),
+                                         float(rope_theta), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                         _ptr(dq), _ptr(dk), _ptr(dv))
+    else:
+        rc = _load().swa_oracle_backward_dilated(B, Hq, Hkv, N, d, w, s, int(dilation), mode,
+                                                 float(scale), _ptr(sl), float(rope_theta),
+                                                 _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dq),
+                                                 _ptr(dk), _ptr(dv))
     if rc != 0:
         raise ValueError("oracle backward rejected its arguments")
     return dq, dk, dv

@@ -109,6 +109,22 @@ static void weights(double *x, int64_t n, int mode) {
  * slopes: float64[H_q] signed ALiBi slopes, or NULL for no bias. theta <= 0: no rotation.
  * scale <= 0 means 1/sqrt(d). Returns 0, or -1 on bad arguments / allocation failure.
  */
+/*
+ * K(i) written out as an ascending list of key positions: the sinks below the window
+ * [0, min(s, lo)), then the window. With dil = 1 the window is [lo, i], lo = max(0, i-w+1)
+ * (the band mask of the Sliding Window Attention glossary, sinks per the SWA(w, s) rule of
+ * Sliding-window beats linear attention); with dil > 1 it keeps i, i - dil, ...,
+ * i - dil (w - 1) and every sink position inside it. Returns the count.
+ */
+static int64_t key_set(int64_t i, int64_t w, int64_t s, int64_t dil, int64_t *key) {
+    int64_t n = 0;
+    int64_t lo = i - dil * (w - 1) > 0 ? i - dil * (w - 1) : 0;
+    for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
+    for (int64_t j = lo; j <= i; ++j)
+        if ((i - j) % dil == 0 || j < s) key[n++] = j;
+    return n;
+}
+
 static int prefill_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
                         int64_t s, int64_t dil, int mode, double scale, const double *slopes,
                         double theta, const double *q, const double *k, const double *v,
@@ -162,19 +178,7 @@ static int prefill_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d
                 if (cs) rotate(qi, qt, d, cs + i * half, sn + i * half);
                 else memcpy(qt, qi, sizeof(double) * (size_t)d);
 
-                /* K(i) as two disjoint ranges: sinks [0, min(s, lo)) and window [lo, i]. */
-                int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;
-                int64_t n = 0;
-                if (dil == 1) {
-                    for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
-                    for (int64_t j = lo; j <= i; ++j) key[n++] = j;
-                } else {
-                    /* dilated: window keys i, i - dil, ..., i - dil (w - 1); every sink j < s */
-                    lo = i - dil * (w - 1) > 0 ? i - dil * (w - 1) : 0;
-                    for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
-                    for (int64_t j = lo; j <= i; ++j)
-                        if ((i - j) % dil == 0 || j < s) key[n++] = j;
-                }
+                int64_t n = key_set(i, w, s, dil, key);
 
                 for (int64_t e = 0; e < n; ++e) {
                     int64_t j = key[e];
@@ -453,11 +457,12 @@ int swa_oracle_chunk(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, i
  * group. The slopes are fixed (no gradient). Layouts as in swa_oracle_prefill; dq like q,
  * dk/dv like k. Returns 0, or -1 on bad arguments / allocation failure.
  */
-int swa_oracle_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
-                        int64_t s, int mode, double scale, const double *slopes, double theta,
-                        const double *q, const double *k, const double *v, const double *dout,
-                        double *dq, double *dk, double *dv) {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || N < 0 || d <= 0 || w < 1 || s < 0)
+static int backward_impl(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
+                         int64_t s, int64_t dil, int mode, double scale, const double *slopes,
+                         double theta, const double *q, const double *k, const double *v,
+                         const double *dout, double *dq, double *dk, double *dv) {
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || N < 0 || d <= 0 || w < 1 || s < 0 ||
+        dil < 1)
         return -1;
     if (theta > 0.0 && d % 2 != 0) return -1;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
@@ -504,10 +509,7 @@ int swa_oracle_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d
                         const double *gi = dout + ((b * N + i) * Hq + h) * d;
                         if (cs) rotate(qi, qt, d, cs + i * half, sn + i * half);
                         else memcpy(qt, qi, sizeof(double) * (size_t)d);
-                        int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;
-                        int64_t n = 0;
-                        for (int64_t j = 0; j < s && j < lo; ++j) key[n++] = j;
-                        for (int64_t j = lo; j <= i; ++j) key[n++] = j;
+                        int64_t n = key_set(i, w, s, dil, key);
                         for (int64_t e = 0; e < n; ++e) {
                             int64_t j = key[e];
                             double bias = slopes ? slopes[h] * (double)(i - j) : 0.0;
@@ -565,4 +567,23 @@ int swa_oracle_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d
     }
     free(cs); free(sn);
     return fail ? -1 : 0;
+}
+
+int swa_oracle_backward(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d, int64_t w,
+                        int64_t s, int mode, double scale, const double *slopes, double theta,
+                        const double *q, const double *k, const double *v, const double *dout,
+                        double *dq, double *dk, double *dv) {
+    return backward_impl(B, Hq, Hkv, N, d, w, s, 1, mode, scale, slopes, theta, q, k, v, dout,
+                         dq, dk, dv);
+}
+
+/* Backward of the dilated prefill: the same gradients over the dilated K(i) of
+ * swa_oracle_prefill_dilated. dil = 1 is swa_oracle_backward. */
+int swa_oracle_backward_dilated(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                                int64_t w, int64_t s, int64_t dil, int mode, double scale,
+                                const double *slopes, double theta, const double *q,
+                                const double *k, const double *v, const double *dout,
+                                double *dq, double *dk, double *dv) {
+    return backward_impl(B, Hq, Hkv, N, d, w, s, dil, mode, scale, slopes, theta, q, k, v, dout,
+                         dq, dk, dv);
 }

@@ -14,7 +14,9 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "swa_oracle.c")
 
 # (name, text in swa_oracle.c, replacement)
 MUTANTS = [
-    ("window_off_by_one", "int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;",
+    ("window_off_by_one", "int64_t lo = i - dil * (w - 1) > 0 ? i - dil * (w - 1) : 0;",
+     "int64_t lo = i - dil * w > 0 ? i - dil * w : 0;"),
+    ("chunk_window_off_by_one", "int64_t lo = i - w + 1 > 0 ? i - w + 1 : 0;",
      "int64_t lo = i - w > 0 ? i - w : 0;"),
     ("bias_sign", "slopes[h] * (double)(i - j)", "slopes[h] * (double)(j - i)"),
     ("rotation_sign", "y[2 * t] = a * c[t] - b * s[t];", "y[2 * t] = a * c[t] + b * s[t];"),
@@ -43,8 +45,10 @@ MUTANTS = [
     ("bwd_value_gradient", "dvj[c] += p * gi[c];", "dvj[c] += dx * gi[c];"),
     ("dilated_stride", "if ((i - j) % dil == 0 || j < s) key[n++] = j;",
      "if ((i - j) % (dil + 1) == 0 || j < s) key[n++] = j;"),
-    ("dilated_span", "lo = i - dil * (w - 1) > 0 ? i - dil * (w - 1) : 0;",
-     "lo = i - dil * w > 0 ? i - dil * w : 0;"),
+    ("dilated_sink_rule", "if ((i - j) % dil == 0 || j < s) key[n++] = j;",
+     "if ((i - j) % dil == 0) key[n++] = j;"),
+    ("dilated_bwd_key_set", "int64_t n = key_set(i, w, s, dil, key);\n                        for",
+     "int64_t n = key_set(i, w, s, 1, key);\n                        for"),
 ]
 
 PIN_TESTS = [
@@ -69,6 +73,7 @@ PIN_TESTS = [
     (pins.test_backward_window_of_one_closed_form, {}),
     (pins.test_dilated_selection_readout, dict(N=33, w=7, s=9, r=4)),
     (pins.test_dilated_selection_readout, dict(N=40, w=5, s=0, r=2)),
+    (pins.test_dilated_backward_is_plain_backward_per_residue_class, dict(mode=oracle.SOFTMAX)),
 ]
 
 

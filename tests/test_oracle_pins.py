@@ -581,6 +581,48 @@ def test_dilated_is_plain_window_per_residue_class(mode, r):
         np.testing.assert_allclose(full[:, c::r], sub, rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("mode", [oracle.SIGMOID, oracle.SOFTMAX])
+@pytest.mark.parametrize("w,s,r,theta,alibi", [(3, 0, 2, 1e4, True), (2, 2, 3, 0.0, False),
+                                               (4, 1, 2, 1e2, True)])
+def test_dilated_backward_matches_finite_differences(mode, w, s, r, theta, alibi):
+    """The dilated backward's gradients of L = sum(dout * o) equal central differences of the
+    (pinned) dilated forward oracle, element by element."""
+    B, N, Hq, Hkv, d = 1, 11, 2, 1, 4
+    q, k, v = _rand((B, N, Hq, d), 64), _rand((B, N, Hkv, d), 65), _rand((B, N, Hkv, d), 66)
+    g = _rand((B, N, Hq, d), 67)
+    slopes = [0.35, -0.2] if alibi else None
+    kw = dict(w=w, s=s, mode=mode, slopes=slopes, rope_theta=theta, dilation=r)
+    dq, dk, dv = oracle.backward(q, k, v, g, **kw)
+    loss = lambda q_, k_, v_: float(np.sum(g * oracle.prefill(q_, k_, v_, **kw)))
+    eps = 1e-5
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [xp if n == name else y for n, y in (("q", q), ("k", k), ("v", v))]
+            args_m = [xm if n == name else y for n, y in (("q", q), ("k", k), ("v", v))]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("mode", [oracle.SIGMOID, oracle.SOFTMAX])
+def test_dilated_backward_is_plain_backward_per_residue_class(mode):
+    """Without sinks or rotation the residue classes of a dilated window are independent plain
+    windows (slopes scaled by r): their gradients are the plain backward's, class by class."""
+    B, N, Hq, Hkv, d, w, r = 1, 26, 2, 1, 6, 4, 3
+    q, k, v = _rand((B, N, Hq, d), 96), _rand((B, N, Hkv, d), 97), _rand((B, N, Hkv, d), 98)
+    g = _rand((B, N, Hq, d), 99)
+    slopes = [-0.3, 0.2]
+    full = oracle.backward(q, k, v, g, w=w, mode=mode, slopes=slopes, dilation=r)
+    for c in range(r):
+        sub = oracle.backward(q[:, c::r], k[:, c::r], v[:, c::r], g[:, c::r], w=w, mode=mode,
+                              slopes=[x * r for x in slopes])
+        for a, b in zip(full, sub):
+            np.testing.assert_allclose(a[:, c::r], b, rtol=1e-12, atol=1e-13)
+
+
 def test_dilation_one_is_the_plain_window():
     B, N, Hq, Hkv, d = 1, 25, 2, 2, 8
     q, k, v = _rand((B, N, Hq, d), 93), _rand((B, N, Hkv, d), 94), _rand((B, N, Hkv, d), 95)
