@@ -62,8 +62,8 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * Window Attention glossary lists beside SWA): with dilation r > 1 the window keeps every
  * r-th position, K(i) = { j <= i : ((i - j) mod r = 0 and (i - j) / r < w) or j < s }, so w
  * keys span r (w - 1) + 1 positions; the sinks are unchanged. The matrix-core path takes r a
- * power of two (other r run on the general kernel); the training pair and the cache entry
- * points take no dilation.
+ * power of two (other r run on the general kernel); the cache entry points take no
+ * dilation.
  * bf16 inputs with d in {64, 128} and 16-byte aligned tensors run on the matrix cores,
  * which form the score product from float16 operands (rotated q and k) and the value
  * product from float16 (softmax) or bf16 (sigmoid) operands, with float32 accumulation:
@@ -103,9 +103,13 @@ size_t swa_prefill_workspace_bytes(const swa_prefill_params *p);
 /*
  * Training pair: the forward for training and its backward (SWAT: Sliding Window Attention
  * Training, "Putting It Together": the layer is trained end to end, so its inputs need
- * gradients). Both run on the matrix cores only: bf16 q, k, v, d in {64, 128} and 16-byte
- * aligned tensors, else SWA_ERR_UNSUPPORTED; operands as in swa_prefill (float16 products,
- * float32 accumulation), so dout must stay within the float16 range too.
+ * gradients). They take every shape swa_prefill takes. bf16 q, k, v with d in {64, 128}, a
+ * contiguous window (dilation 0 or 1) and 16-byte aligned tensors (q, k, v, o, dout, dq, dk,
+ * dv, rope_table) run on the matrix cores, with operands as in swa_prefill (float16
+ * products, float32 accumulation), so dout must stay within the float16 range too; every
+ * other shape, dilated windows included, runs on general float32 vector kernels. Each call
+ * picks its path by these rules alone, so a forward and a backward may take different
+ * paths: lse and o mean the same on both.
  *
  * swa_prefill_train: swa_prefill, plus for softmax the natural-log normaliser of every row,
  *   lse[b][h][i] = log sum_{j in K(i)} exp(x_ij), device float [B, H_q, N] (NULL allowed
@@ -119,7 +123,9 @@ swa_status swa_prefill_train(const swa_prefill_params *p, const void *q, const v
  * swa_prefill_backward: gradients of a loss L given dout = dL/do [B, N, H_q, d]:
  *   dP_ij = dout_i . v_j
  *   dX_ij = dP_ij p_ij (1 - p_ij)            sigmoid (the logistic derivative)
- *         = p_ij (dP_ij - dout_i . o_i)      softmax (the row Jacobian)
+ *         = p_ij (dP_ij - dout_i . o_i)      softmax (the row Jacobian; the general path
+ *                                            sums dout_i . o_i as sum_j p_ij dP_ij, which
+ *                                            keeps a bf16 o's rounding out)
  *   dv_j = sum_i p_ij dout_i,  dq_i = scale R(i)^T sum_j dX_ij R(j) k_j,
  *   dk_j = scale R(j)^T sum_i dX_ij R(i) q_i
  * over j in K(i); key and value gradients sum over the query heads of their group; the
@@ -127,17 +133,20 @@ swa_status swa_prefill_train(const swa_prefill_params *p, const void *q, const v
  * entirely (no accumulation into them). o, dout, dq, dk, dv have p->out_dtype; o and lse
  * (from swa_prefill_train with the same parameters and inputs) are read for softmax only
  * and may be NULL for sigmoid. workspace: swa_prefill_backward_workspace_bytes(p) bytes,
- * 16-byte aligned: float16 images of k, v, q and dout (B * N_tiles * 64 * d * 2 bytes for
- * each of H_kv, H_kv, H_q and H_q heads, N_tiles = ceil(N / 64)), for softmax 8 bytes of
- * row statistics per (b, h, row), and with sinks a float32 partial gradient of the sink keys.
+ * 16-byte aligned. The matrix-core path keeps float16 images of k, v, q and dout there
+ * (B * N_tiles * 64 * d * 2 bytes for each of H_kv, H_kv, H_q and H_q heads, N_tiles =
+ * ceil(N / 64)), for softmax 8 bytes of row statistics per (b, h, row), and with sinks a
+ * float32 partial gradient of the sink keys; the general path, for softmax, one float per
+ * (b, h, row) (none for sigmoid). With dilation > 1 the window is the dilated K(i) of
+ * swa_prefill.
  */
 swa_status swa_prefill_backward(const swa_prefill_params *p, const void *q, const void *k,
                                 const void *v, const void *o, const float *lse,
                                 const void *dout, void *dq, void *dk, void *dv,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
-/* Bytes of workspace swa_prefill_backward needs (0 when none, or when the parameters are
- * invalid or unsupported). */
+/* Bytes of workspace swa_prefill_backward needs on whichever path it takes (0 when none,
+ * or when the parameters are invalid). */
 size_t swa_prefill_backward_workspace_bytes(const swa_prefill_params *p);
 
 /*

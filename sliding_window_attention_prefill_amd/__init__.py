@@ -185,47 +185,21 @@ def swa_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: int, s:
 
     workspace: a device uint8 tensor of at least swa_prefill_workspace_bytes(...) bytes;
     allocated here when it is not given and the call needs one."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n)
-    if q.dim() != 4 or k.shape != v.shape or k.dim() != 4:
+    if q.dim() != 4:
         raise ValueError("q must be [B,N,H_q,d] and k, v [B,N,H_kv,d]")
-    B, N, Hq, d = q.shape
-    if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
-        raise ValueError("q, k, v shapes disagree")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("q, k, v must share a dtype")
     if out is None:
+        B, N, Hq, d = q.shape
         out = torch.empty((B, N, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    _dev(out, "out")
-    if tuple(out.shape) != (B, N, Hq, d):
-        raise ValueError("out must be [B,N,H_q,d]")
-    if alibi_slopes is not None:
-        _dev(alibi_slopes, "alibi_slopes")
-        if alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != Hq:
-            raise ValueError("alibi_slopes must be float32[H_q]")
-    rows = 0
-    if rope_table is not None:
-        _dev(rope_table, "rope_table")
-        if rope_table.dtype != torch.float32 or rope_table.dim() != 3 or \
-                rope_table.shape[1] != d // 2 or rope_table.shape[2] != 2:
-            raise ValueError("rope_table must be float32 [rows, d/2, 2]")
-        rows = rope_table.shape[0]
-    p = PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), _dt(out), scale,
-                      _ptr(alibi_slopes), _ptr(rope_table), rows, dilation)
+    p = _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table, dilation)
     lib = load()
-    need = lib.swa_prefill_workspace_bytes(ctypes.byref(p))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0
-    if workspace is not None:
-        _dev(workspace, "workspace")
-        ws_bytes = workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(int(lib.swa_prefill_workspace_bytes(ctypes.byref(p))),
+                                     workspace, q.device)
     _check("swa_prefill", lib.swa_prefill(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                                           _ptr(workspace), ws_bytes, _stream(q.device, stream)))
     return out
 
 
-def _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table):
+def _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table, dilation=1):
     """Shape checks shared by the prefill entry points; returns PrefillParams."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
         _dev(t, n)
@@ -250,7 +224,7 @@ def _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table):
             raise ValueError("rope_table must be float32 [rows, d/2, 2]")
         rows = rope_table.shape[0]
     return PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), _dt(out), scale,
-                         _ptr(alibi_slopes), _ptr(rope_table), rows)
+                         _ptr(alibi_slopes), _ptr(rope_table), rows, dilation)
 
 
 def _workspace(need: int, workspace, device):
@@ -269,13 +243,13 @@ def swa_prefill_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, w: i
                       rope_table: Optional[torch.Tensor] = None,
                       out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                       lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                      stream=None):
+                      stream=None, dilation: int = 1):
     """Forward for training: returns (o, lse), lse float32 [B, H_q, N] the natural-log row
     normalisers (softmax; None for sigmoid)."""
     B, N, Hq, d = q.shape
     if out is None:
         out = torch.empty((B, N, Hq, d), dtype=out_dtype or q.dtype, device=q.device)
-    p = _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table)
+    p = _prefill_params(q, k, v, out, w, s, mode, scale, alibi_slopes, rope_table, dilation)
     if p.mode == SWA_SOFTMAX:
         if lse is None:
             lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
@@ -298,10 +272,11 @@ def swa_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                          dout: torch.Tensor, *, w: int, s: int = 0, mode=SWA_SIGMOID,
                          scale: float = 0.0, alibi_slopes: Optional[torch.Tensor] = None,
                          rope_table: Optional[torch.Tensor] = None,
-                         grads=None, workspace: Optional[torch.Tensor] = None, stream=None):
+                         grads=None, workspace: Optional[torch.Tensor] = None, stream=None,
+                         dilation: int = 1):
     """Gradients (dq, dk, dv) in dout's dtype for the output gradient dout [B,N,H_q,d];
     o and lse (from swa_prefill_train) are needed for softmax only."""
-    p = _prefill_params(q, k, v, dout, w, s, mode, scale, alibi_slopes, rope_table)
+    p = _prefill_params(q, k, v, dout, w, s, mode, scale, alibi_slopes, rope_table, dilation)
     if p.mode == SWA_SOFTMAX:
         if o is None or lse is None:
             raise ValueError("softmax needs the forward's o and lse")
@@ -329,24 +304,26 @@ def swa_prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 
 def swa_prefill_workspace_bytes(q: torch.Tensor, k: torch.Tensor, *, w: int, s: int = 0,
-                                mode=SWA_SIGMOID, out_dtype: Optional[torch.dtype] = None) -> int:
+                                mode=SWA_SIGMOID, out_dtype: Optional[torch.dtype] = None,
+                                dilation: int = 1) -> int:
     """Workspace bytes swa_prefill needs for q [B,N,H_q,d], k [B,N,H_kv,d] and these options
     (ALiBi and RoPE do not change it)."""
     B, N, Hq, d = q.shape
     out_dt = SWA_F32 if (out_dtype or q.dtype) == torch.float32 else SWA_BF16
     p = PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), out_dt, 0.0,
-                      None, None, 0)
+                      None, None, 0, dilation)
     return int(load().swa_prefill_workspace_bytes(ctypes.byref(p)))
 
 
 def swa_prefill_backward_workspace_bytes(q: torch.Tensor, k: torch.Tensor, *, w: int, s: int = 0,
                                          mode=SWA_SIGMOID,
-                                         grad_dtype: Optional[torch.dtype] = None) -> int:
+                                         grad_dtype: Optional[torch.dtype] = None,
+                                         dilation: int = 1) -> int:
     """Workspace bytes swa_prefill_backward needs for q [B,N,H_q,d], k [B,N,H_kv,d]."""
     B, N, Hq, d = q.shape
     out_dt = SWA_F32 if (grad_dtype or q.dtype) == torch.float32 else SWA_BF16
     p = PrefillParams(B, Hq, k.shape[2], N, d, w, s, _mode(mode), _dt(q), out_dt, 0.0,
-                      None, None, 0)
+                      None, None, 0, dilation)
     return int(load().swa_prefill_backward_workspace_bytes(ctypes.byref(p)))
 
 

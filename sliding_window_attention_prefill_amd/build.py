@@ -18,8 +18,8 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libswa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["swa_api.cpp", "prefill_simt.hip", "prefill_mfma.hip", "backward_mfma.hip", "rope.hip",
-           "decode.hip"]
+SOURCES = ["swa_api.cpp", "prefill_simt.hip", "prefill_mfma.hip", "backward_mfma.hip",
+           "backward_simt.hip", "rope.hip", "decode.hip"]
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

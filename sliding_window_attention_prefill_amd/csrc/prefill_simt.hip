@@ -22,25 +22,8 @@ struct SimtParams {
     float scale;
     const float *slopes;
     const float *rope;
+    float *lse;  // softmax row log-normalisers [B, Hq, N], or null
 };
-
-constexpr int kMaxPerLane = 4;  // d <= 256 over 64 lanes
-
-// Rotate the lane-distributed head vector x (element c = lane + 64 t) at position pos.
-// Pair (2u, 2u+1) lives in adjacent lanes; the partner value comes from lane ^ 1.
-__device__ __forceinline__ void rotate_lanes(float (&x)[kMaxPerLane], int lane, int d,
-                                             const float *rope, int64_t pos) {
-    const int half = d >> 1;
-#pragma unroll
-    for (int t = 0; t < kMaxPerLane; ++t) {
-        const float partner = __shfl_xor(x[t], 1, 64);
-        const int c = lane + 64 * t;
-        if (c < d) {
-            const float2 cs = reinterpret_cast<const float2 *>(rope)[pos * half + (c >> 1)];
-            x[t] = (c & 1) ? fmaf(partner, cs.y, x[t] * cs.x) : fmaf(-partner, cs.y, x[t] * cs.x);
-        }
-    }
-}
 
 template <int IN, int OUT>
 __global__ __launch_bounds__(256) void prefill_simt_kernel(SimtParams p, const void *__restrict__ q,
@@ -107,6 +90,7 @@ __global__ __launch_bounds__(256) void prefill_simt_kernel(SimtParams p, const v
             acc[t] = fmaf(wgt, vv, acc[t] * corr);
         }
     }
+    if (p.mode == 1 && p.lse && lane == 0) p.lse[(b * p.Hq + h) * p.N + i] = m + logf(l);
     const float inv = p.mode == 1 ? 1.0f / l : 1.0f;
 #pragma unroll
     for (int t = 0; t < kMaxPerLane; ++t) {
@@ -117,8 +101,9 @@ __global__ __launch_bounds__(256) void prefill_simt_kernel(SimtParams p, const v
 
 template <int IN, int OUT>
 hipError_t launch_t(const PrefillArgs &a, const void *q, const void *k, const void *v, void *o,
-                    hipStream_t st) {
-    SimtParams p{a.B, a.Hq, a.Hkv, a.N, a.d, a.w, a.s, a.dil, a.mode, a.scale, a.slopes, a.rope};
+                    float *lse, hipStream_t st) {
+    SimtParams p{a.B, a.Hq, a.Hkv, a.N, a.d, a.w, a.s, a.dil, a.mode, a.scale, a.slopes, a.rope,
+                 lse};
     const int64_t rows = a.B * a.N * a.Hq;
     const int64_t blocks = (rows + 3) / 4;
     hipLaunchKernelGGL((prefill_simt_kernel<IN, OUT>), dim3((unsigned)blocks), dim3(256), 0, st,
@@ -129,12 +114,12 @@ hipError_t launch_t(const PrefillArgs &a, const void *q, const void *k, const vo
 }  // namespace
 
 hipError_t launch_prefill_simt(const PrefillArgs &a, const void *q, const void *k,
-                               const void *v, void *o, hipStream_t st) {
+                               const void *v, void *o, hipStream_t st, float *lse) {
     if (a.B * a.N * a.Hq == 0) return hipSuccess;
-    if (a.in_dt == 0 && a.out_dt == 0) return launch_t<0, 0>(a, q, k, v, o, st);
-    if (a.in_dt == 0 && a.out_dt == 1) return launch_t<0, 1>(a, q, k, v, o, st);
-    if (a.in_dt == 1 && a.out_dt == 0) return launch_t<1, 0>(a, q, k, v, o, st);
-    return launch_t<1, 1>(a, q, k, v, o, st);
+    if (a.in_dt == 0 && a.out_dt == 0) return launch_t<0, 0>(a, q, k, v, o, lse, st);
+    if (a.in_dt == 0 && a.out_dt == 1) return launch_t<0, 1>(a, q, k, v, o, lse, st);
+    if (a.in_dt == 1 && a.out_dt == 0) return launch_t<1, 0>(a, q, k, v, o, lse, st);
+    return launch_t<1, 1>(a, q, k, v, o, lse, st);
 }
 
 }  // namespace swa

@@ -5,6 +5,7 @@
 // HIP error kept per thread for swa_last_hip_error().
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <initializer_list>
 
@@ -67,7 +68,10 @@ static swa::PrefillArgs prefill_args(const swa_prefill_params *p) {
     return swa::PrefillArgs{p->B, p->H_q, p->H_kv, p->N, p->d, p->w, p->s, p->mode,
                             p->in_dtype, p->out_dtype, resolve_scale(p->scale, p->d),
                             p->alibi_slopes, p->rope_table, p->rope_table ? p->rope_rows : 0,
-                            p->dilation > 1 ? p->dilation : 1};
+                            // a dilation of at least N keeps only i - j = 0 in the window;
+                            // 2^24 >= N stands for every larger one
+                            p->dilation > 1 ? std::min<int64_t>(p->dilation, int64_t(1) << 24)
+                                            : 1};
 }
 
 size_t swa_prefill_workspace_bytes(const swa_prefill_params *p) {
@@ -101,61 +105,76 @@ swa_status swa_prefill(const swa_prefill_params *p, const void *q, const void *k
     return hip_status(swa::launch_prefill_simt(a, q, k, v, o, st));
 }
 
-// The training pair runs on the matrix cores only: bf16 inputs, d in {64, 128}, 16-byte
-// aligned tensors.
-static swa_status check_train(const swa_prefill_params *p, std::initializer_list<const void *> ptrs) {
-    const swa_status chk = check_prefill(p);
-    if (chk != SWA_OK) return chk;
-    const swa::PrefillArgs a = prefill_args(p);
-    if (!swa::prefill_mfma_supported(a) || a.dil != 1) return SWA_ERR_UNSUPPORTED;
+// The training pair runs on the matrix cores for bf16 inputs, d in {64, 128}, a contiguous
+// window and 16-byte aligned tensors, and on the general vector kernels otherwise.
+static bool train_on_mfma(const swa::PrefillArgs &a, const swa_prefill_params *p,
+                          std::initializer_list<const void *> ptrs) {
+    if (!swa::prefill_mfma_supported(a) || a.dil != 1) return false;
     uintptr_t bits = reinterpret_cast<uintptr_t>(p->rope_table);
     for (const void *x : ptrs) bits |= reinterpret_cast<uintptr_t>(x);
-    if (bits & 15) return SWA_ERR_UNSUPPORTED;
-    return SWA_OK;
+    return (bits & 15) == 0;
 }
 
 swa_status swa_prefill_train(const swa_prefill_params *p, const void *q, const void *k,
                              const void *v, void *o, float *lse, void *workspace,
                              size_t workspace_bytes, void *stream) {
-    const swa_status chk = check_train(p, {q, k, v, o});
+    const swa_status chk = check_prefill(p);
     if (chk != SWA_OK) return chk;
     const int64_t elems = p->B * p->N;
     if (elems > 0 && (!q || !k || !v || !o)) return SWA_ERR_INVALID_ARGUMENT;
     if (elems > 0 && p->mode == SWA_SOFTMAX && !lse) return SWA_ERR_INVALID_ARGUMENT;
     const swa::PrefillArgs a = prefill_args(p);
-    const size_t need = swa::prefill_mfma_workspace_bytes(a);
-    if (need > 0 && (!workspace || workspace_bytes < need ||
-                     (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
-        return SWA_ERR_INVALID_ARGUMENT;
-    return hip_status(swa::launch_prefill_mfma(a, q, k, v, o, workspace,
-                                               static_cast<hipStream_t>(stream),
-                                               p->mode == SWA_SOFTMAX ? lse : nullptr));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *row_lse = p->mode == SWA_SOFTMAX ? lse : nullptr;
+    if (train_on_mfma(a, p, {q, k, v, o})) {
+        const size_t need = swa::prefill_mfma_workspace_bytes(a);
+        if (need > 0 && (!workspace || workspace_bytes < need ||
+                         (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
+            return SWA_ERR_INVALID_ARGUMENT;
+        return hip_status(swa::launch_prefill_mfma(a, q, k, v, o, workspace, st, row_lse));
+    }
+    if ((a.B * a.N * a.Hq + 3) / 4 > 0x7fffffff) return SWA_ERR_UNSUPPORTED;
+    return hip_status(swa::launch_prefill_simt(a, q, k, v, o, st, row_lse));
 }
 
+// Workspace for whichever path a call takes: the matrix-core need (when that path can be
+// taken) covers the general path's (4 bytes per softmax row against at least 8).
 size_t swa_prefill_backward_workspace_bytes(const swa_prefill_params *p) {
     if (check_prefill(p) != SWA_OK) return 0;
     const swa::PrefillArgs a = prefill_args(p);
-    if (!swa::prefill_mfma_supported(a) || a.dil != 1) return 0;
-    return swa::prefill_bwd_workspace_bytes(a);
+    const size_t gen = swa::prefill_bwd_simt_workspace_bytes(a);
+    if (!swa::prefill_mfma_supported(a) || a.dil != 1) return gen;
+    const size_t mf = swa::prefill_bwd_workspace_bytes(a);
+    return mf > gen ? mf : gen;
 }
 
 swa_status swa_prefill_backward(const swa_prefill_params *p, const void *q, const void *k,
                                 const void *v, const void *o, const float *lse,
                                 const void *dout, void *dq, void *dk, void *dv,
                                 void *workspace, size_t workspace_bytes, void *stream) {
-    const swa_status chk = check_train(p, {q, k, v, o, dout, dq, dk, dv});
+    const swa_status chk = check_prefill(p);
     if (chk != SWA_OK) return chk;
     const int64_t elems = p->B * p->N;
     if (elems > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
         return SWA_ERR_INVALID_ARGUMENT;
     if (elems > 0 && p->mode == SWA_SOFTMAX && (!o || !lse)) return SWA_ERR_INVALID_ARGUMENT;
     const swa::PrefillArgs a = prefill_args(p);
-    const size_t need = swa::prefill_bwd_workspace_bytes(a);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (train_on_mfma(a, p, {q, k, v, o, dout, dq, dk, dv})) {
+        const size_t need = swa::prefill_bwd_workspace_bytes(a);
+        if (need > 0 && (!workspace || workspace_bytes < need ||
+                         (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
+            return SWA_ERR_INVALID_ARGUMENT;
+        return hip_status(
+            swa::launch_prefill_bwd(a, q, k, v, o, lse, dout, dq, dk, dv, workspace, st));
+    }
+    if ((a.B * a.N * a.Hq + 3) / 4 > 0x7fffffff) return SWA_ERR_UNSUPPORTED;
+    const size_t need = swa::prefill_bwd_simt_workspace_bytes(a);
     if (need > 0 && (!workspace || workspace_bytes < need ||
                      (reinterpret_cast<uintptr_t>(workspace) & 15) != 0))
         return SWA_ERR_INVALID_ARGUMENT;
-    return hip_status(swa::launch_prefill_bwd(a, q, k, v, o, lse, dout, dq, dk, dv, workspace,
-                                              static_cast<hipStream_t>(stream)));
+    return hip_status(
+        swa::launch_prefill_bwd_simt(a, q, k, v, lse, dout, dq, dk, dv, workspace, st));
 }
 
 swa_status swa_rope_table(float *table, int64_t n_pos, int64_t d, double theta, void *stream) {

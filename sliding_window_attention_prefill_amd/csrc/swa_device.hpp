@@ -135,6 +135,28 @@ __device__ __forceinline__ float row16_max(float x) {
     return x;
 }
 
+// The general vector kernels spread one head vector over a wavefront: element c sits in
+// lane c % 64, register c / 64.
+constexpr int kMaxPerLane = 4;  // d <= 256 over 64 lanes
+
+// Rotate a lane-distributed head vector by the RoPE angles of position pos (sgn = 1) or by
+// their negatives (sgn = -1, the transpose R(pos)^T). Pair (2u, 2u+1) lives in adjacent
+// lanes; the partner value comes from lane ^ 1. rope: [rows, d/2, 2] (cos, sin).
+__device__ __forceinline__ void rotate_lanes(float (&x)[kMaxPerLane], int lane, int d,
+                                             const float *rope, int64_t pos, float sgn = 1.0f) {
+    const int half = d >> 1;
+#pragma unroll
+    for (int t = 0; t < kMaxPerLane; ++t) {
+        const float partner = __shfl_xor(x[t], 1, 64);
+        const int c = lane + 64 * t;
+        if (c < d) {
+            const float2 cs = reinterpret_cast<const float2 *>(rope)[pos * half + (c >> 1)];
+            const float sn = sgn * cs.y;
+            x[t] = (c & 1) ? fmaf(partner, sn, x[t] * cs.x) : fmaf(-partner, sn, x[t] * cs.x);
+        }
+    }
+}
+
 // Quiet NaN used to flag outputs of queries whose position could not be served.
 __device__ __forceinline__ float qnan() { return __uint_as_float(0x7fc00000u); }
 

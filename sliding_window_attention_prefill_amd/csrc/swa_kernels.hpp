@@ -34,9 +34,18 @@ struct DecodeArgs {
     int64_t rope_rows;
 };
 
-// General vector kernel: any even d <= 256, float32 or bfloat16 in/out.
+// General vector kernel: any even d <= 256, float32 or bfloat16 in/out. lse (softmax only,
+// may be null): the log-normaliser of every row, [B, Hq, N] float32.
 hipError_t launch_prefill_simt(const PrefillArgs &a, const void *q, const void *k,
-                               const void *v, void *o, hipStream_t st);
+                               const void *v, void *o, hipStream_t st, float *lse = nullptr);
+
+// Backward of the general kernel (any shape it takes): dq, dk, dv in the out dtype from
+// dout (out dtype) and, for softmax, lse. ws: prefill_bwd_simt_workspace_bytes(a) bytes,
+// 4-byte aligned (softmax: one float per row for sum_j p_ij dP_ij).
+size_t prefill_bwd_simt_workspace_bytes(const PrefillArgs &a);
+hipError_t launch_prefill_bwd_simt(const PrefillArgs &a, const void *q, const void *k,
+                                   const void *v, const float *lse, const void *dout, void *dq,
+                                   void *dk, void *dv, void *ws, hipStream_t st);
 
 // Matrix-core kernel: bfloat16 inputs, d in {64, 128}; prefill_mfma_supported tells
 // whether a shape is covered (the caller otherwise uses the general kernel). ws must hold

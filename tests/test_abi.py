@@ -213,22 +213,39 @@ def test_prefill_chunk_rejects_bad_arguments(lib):
 
 
 def test_training_pair_rejections(lib):
-    """The training pair runs on the matrix cores only, and softmax needs o and lse."""
+    """Softmax needs o and lse, every tensor must be given, and the matrix-core backward
+    checks its workspace (shapes it does not take run on the general kernels, which need
+    none)."""
     p = _params(mode=1)
     z = ctypes.c_void_p(0)
-    assert lib.swa_prefill_train(ctypes.byref(_params(in_dtype=0)), DUMMY, DUMMY, DUMMY, DUMMY,
-                                 DUMMY, None, 0, None) == 2        # float32 inputs
-    assert lib.swa_prefill_train(ctypes.byref(_params(d=96)), DUMMY, DUMMY, DUMMY, DUMMY,
-                                 DUMMY, None, 0, None) == 2        # head size 96
+    assert lib.swa_prefill_train(ctypes.byref(_params(d=258)), DUMMY, DUMMY, DUMMY, DUMMY,
+                                 DUMMY, None, 0, None) == 2        # head size above 256
+    assert lib.swa_prefill_train(ctypes.byref(_params(in_dtype=0, mode=1)), DUMMY, DUMMY, DUMMY,
+                                 DUMMY, None, None, 0, None) == 1  # float32, softmax, no lse
     assert lib.swa_prefill_train(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, None, None, 0,
                                  None) == 1                        # softmax without lse
+    assert lib.swa_prefill_train(ctypes.byref(p), DUMMY, z, DUMMY, DUMMY, DUMMY, None, 0,
+                                 None) == 1                        # no k
     assert lib.swa_prefill_backward(ctypes.byref(p), DUMMY, DUMMY, DUMMY, None, None, DUMMY,
                                     DUMMY, DUMMY, DUMMY, None, 0, None) == 1   # no o / lse
+    assert lib.swa_prefill_backward(ctypes.byref(_params(d=96, mode=1)), DUMMY, DUMMY, DUMMY,
+                                    DUMMY, None, DUMMY, DUMMY, DUMMY, DUMMY, None, 0,
+                                    None) == 1                     # general path, no lse
     assert lib.swa_prefill_backward(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
                                     z, DUMMY, DUMMY, None, 0, None) == 1       # no dq
+    assert lib.swa_prefill_backward(ctypes.byref(_params(H_q=3)), DUMMY, DUMMY, DUMMY, DUMMY,
+                                    DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, 0,
+                                    None) == 1                     # H_q % H_kv != 0
     need = lib.swa_prefill_backward_workspace_bytes(ctypes.byref(p))
     assert lib.swa_prefill_backward(ctypes.byref(p), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
                                     DUMMY, DUMMY, DUMMY, DUMMY, need - 16, None) == 1
+    g = _params(in_dtype=0, mode=1)
+    need = lib.swa_prefill_backward_workspace_bytes(ctypes.byref(g))
+    assert need > 0
+    assert lib.swa_prefill_backward(ctypes.byref(g), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                    DUMMY, DUMMY, DUMMY, None, 0, None) == 1   # general, no ws
+    assert lib.swa_prefill_backward(ctypes.byref(g), DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY,
+                                    DUMMY, DUMMY, DUMMY, DUMMY, need - 4, None) == 1
 
 
 def test_backward_workspace_bytes(lib):
@@ -246,14 +263,18 @@ def test_backward_workspace_bytes(lib):
     assert wsb(**big) == 2 * B * Hkv * tiles * 64 * d * 2 + 2 * B * Hq * tiles * 64 * d * 2 + \
         2 * B * Hkv * 128 * d * 4
     assert wsb(in_dtype=0) == 0 and wsb(d=96) == 0 and wsb(B=0) == 0
+    # the general path (float32, other head sizes, dilation): one float per softmax row
+    assert wsb(in_dtype=0, mode=1) == B * Hq * N * 4 == wsb(d=96, mode=1)
+    assert wsb(dilation=3, mode=1) == B * Hq * N * 4
 
 
 def test_dilation_arguments(lib):
-    """A negative dilation is rejected; the training pair takes no dilation."""
+    """A negative dilation is rejected; a dilated window trains on the general kernels,
+    whose backward needs no workspace."""
     assert lib.swa_prefill(ctypes.byref(_params(dilation=-1)), DUMMY, DUMMY, DUMMY, DUMMY, None,
                            0, None) == 1
-    assert lib.swa_prefill_train(ctypes.byref(_params(dilation=2)), DUMMY, DUMMY, DUMMY, DUMMY,
-                                 DUMMY, None, 0, None) == 2
+    assert lib.swa_prefill_train(ctypes.byref(_params(dilation=-1)), DUMMY, DUMMY, DUMMY, DUMMY,
+                                 DUMMY, None, 0, None) == 1
     assert lib.swa_prefill_backward_workspace_bytes(ctypes.byref(_params(dilation=2))) == 0
     # the workspace of the forward does not depend on the dilation
     assert lib.swa_prefill_workspace_bytes(ctypes.byref(_params(dilation=4))) == \
