@@ -110,10 +110,13 @@ def test_train_forward_equals_prefill(mode):
     assert (lse is None) == (mode == wl.SIGMOID)
 
 
-def test_backward_bf16_gradients():
-    B, Hq, Hkv, N, d, w, s, mode, theta = 1, 4, 2, 400, 64, 70, 2, wl.SOFTMAX, 1e4
-    q, k, v, dout = _inputs(B, Hq, Hkv, N, d, seed=11)
-    slopes = (-0.2, -0.1, 0.1, 0.2)
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,w,s", [(1, 4, 2, 400, 64, 70, 2), (1, 2, 1, 140, 64, 30, 1),
+                                              (1, 4, 2, 300, 128, 24, 0)])
+def test_backward_bf16_gradients(B, Hq, Hkv, N, d, w, s):
+    """bf16 output and gradients: o reaches the softmax row term rounded to bf16."""
+    mode, theta = wl.SOFTMAX, 1e4
+    q, k, v, dout = _inputs(B, Hq, Hkv, N, d, seed=11 + N)
+    slopes = tuple(np.linspace(-0.2, 0.2, Hq).tolist())
     o, lse, dq, dk, dv, g = _run(q, k, v, dout, w, s, mode, slopes, theta, out_dtype=torch.bfloat16)
     assert dq.dtype == torch.bfloat16
     ref = oracle.backward(q, k, v, g.cpu(), w=w, s=s, mode=mode, slopes=slopes, rope_theta=theta)
