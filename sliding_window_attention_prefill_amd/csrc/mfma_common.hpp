@@ -55,6 +55,18 @@ __device__ __forceinline__ uint4 rotate_chunk(uint4 x, float4 t0, float4 t1) {
 __device__ __forceinline__ uint4 convert_chunk(uint4 x) {
     return make_uint4(to_f16_pair(x.x), to_f16_pair(x.y), to_f16_pair(x.z), to_f16_pair(x.w));
 }
+// The same with every value multiplied by f before the single rounding to float16.
+__device__ __forceinline__ uint4 rotate_chunk_scaled(uint4 x, float4 t0, float4 t1, float f) {
+    return make_uint4(rotate_pair(x.x, t0.x * f, t0.y * f), rotate_pair(x.y, t0.z * f, t0.w * f),
+                      rotate_pair(x.z, t1.x * f, t1.y * f), rotate_pair(x.w, t1.z * f, t1.w * f));
+}
+__device__ __forceinline__ uint32_t to_f16_pair_scaled(uint32_t w, float f) {
+    return pack_f16x2(__uint_as_float(w << 16) * f, __uint_as_float(w & 0xffff0000u) * f);
+}
+__device__ __forceinline__ uint4 convert_chunk_scaled(uint4 x, float f) {
+    return make_uint4(to_f16_pair_scaled(x.x, f), to_f16_pair_scaled(x.y, f),
+                      to_f16_pair_scaled(x.z, f), to_f16_pair_scaled(x.w, f));
+}
 
 // Buffer -> LDS transfers: ROUNDS rounds of 1 KB per wavefront; lane l of round i lands at
 // bytes 16 l of that round's kilobyte (wavefront wave fills kilobytes wave * ROUNDS + i).
@@ -73,14 +85,14 @@ __device__ __forceinline__ constexpr int key_of(int kb, int e) {
     return kb * 32 + 8 * (e >> 2) + (e & 3);
 }
 
-// Exclude the keys of an edge tile that are outside the key set: their logits become -inf
-// (weight 0 in both modes). Element (kb, e) is key j = jb + key_of(kb, e) with
+// Exclude the keys of an edge tile that are outside the key set: their scores become fill
+// (-inf for a logit, +inf for the sigmoid's negated logit: weight 0 either way). Element (kb, e) is key j = jb + key_of(kb, e) with
 // i - j = dq - key_of(kb, e). w is the window's extent in positions; with a dilation r (a
 // power of two, dmask = r - 1) only every r-th of them is a key. SINKS adds the keys j < s
 // at or before the query.
 template <bool SINKS>
 __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, int w, int s,
-                                          int dmask = 0) {
+                                          int dmask = 0, float fill = -INFINITY) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -88,7 +100,7 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
             const int dij = dq - key_of(kb, e);
             bool ok = ((unsigned)dij < (unsigned)w) & ((dij & dmask) == 0);   // 0 <= i - j < w
             if (SINKS) ok = ok | ((dij >= 0) & (jb + key_of(kb, e) < s));
-            sacc[kb][e] = ok ? sacc[kb][e] : -INFINITY;
+            sacc[kb][e] = ok ? sacc[kb][e] : fill;
         }
 }
 
@@ -97,12 +109,19 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
 // 2^a (hi + lo) in float16, A row m holds (2^a kappa, 2^a kappa) and every B column
 // (-hi, -lo) in k = 0, 1, so the product is -r kappa for the key kappa = 32 kb + m of the
 // tile (kappa 2^a is exact in float16, and hi + lo carries r to about 22 bits).
+//
+// With qterm the same instruction also carries a per-query term r u (u = i - j0, refreshed
+// per tile by query_term): k = 2, 3 hold 2^c in A and the two-term float16 split of
+// r u 2^-c in B (query_term's dword), c = min(a + 12, 15). Then |r u 2^-c| < 2^13 for
+// u < 2^24 (no float16 overflow) and >= 2^-12 for u >= 1 (normal float16); a term past
+// the float16 range (only for |r| >= 16) is clamped, where the sigmoid has saturated.
 struct BiasOperands {
     f16x8_t a[2];
     f16x8_t b;
+    float qmul;  // r 2^-c (qterm only)
 };
 
-__device__ __forceinline__ BiasOperands bias_operands(float r, int lane) {
+__device__ __forceinline__ BiasOperands bias_operands(float r, int lane, bool qterm = false) {
     int ex = 0;
     (void)frexpf(r, &ex);                      // |r| = m 2^ex, m in [0.5, 1)
     int a = ex - 1;
@@ -110,31 +129,50 @@ __device__ __forceinline__ BiasOperands bias_operands(float r, int lane) {
     const float rs = ldexpf(r, -a);
     const _Float16 hi = (_Float16)rs;
     const _Float16 lo = (_Float16)(rs - (float)hi);
+    const int c = a + 12 < 15 ? a + 12 : 15;
     BiasOperands bo;
     const f16x8_t z = {};
     bo.a[0] = z; bo.a[1] = z; bo.b = z;
+    bo.qmul = qterm ? ldexpf(r, -c) : 0.0f;
     if (lane < 32) {
         const _Float16 k0 = (_Float16)ldexpf((float)lane, a);
         const _Float16 k1 = (_Float16)ldexpf((float)(lane + 32), a);
         bo.a[0][0] = k0; bo.a[0][1] = k0;
         bo.a[1][0] = k1; bo.a[1][1] = k1;
         bo.b[0] = -hi; bo.b[1] = -lo;
+        if (qterm) {
+            const _Float16 pc = (_Float16)ldexpf(1.0f, c);
+            bo.a[0][2] = pc; bo.a[0][3] = pc;
+            bo.a[1][2] = pc; bo.a[1][3] = pc;
+        }
     }
     return bo;
 }
 
+// The bias B operand for a tile whose query offset is u = i - j0: the two-term float16
+// split of qmul u in k = 2, 3 (lanes of k >= 8 carry it too; their A entries are zero).
+__device__ __forceinline__ f16x8_t query_term(const BiasOperands &bo, int u) {
+    float v = bo.qmul * (float)u;
+    v = fminf(fmaxf(v, -65000.0f), 65000.0f);
+    const float vh = (float)(_Float16)v;
+    f16x8_t b = bo.b;
+    b[2] = (_Float16)vh;
+    b[3] = (_Float16)(v - vh);
+    return b;
+}
+
 // S^T = K Q^T for the 64 keys of one LDS tile (two 32-key blocks, whose chains alternate);
 // koff[ks] is this lane's element offset of its row's chunk for k-step ks. With ALiBi each
-// block starts from the key part of the bias.
+// block starts from the bias instruction (A from bo, B = bb).
 template <int D, bool ALIBI>
 __device__ __forceinline__ void qk_tile_off(const uint16_t *__restrict__ kl, const int (&koff)[D / 16],
-                                            const BiasOperands &bo, const f16x8_t (&qreg)[D / 16],
-                                            f32x16_t (&sacc)[2]) {
+                                            const BiasOperands &bo, const f16x8_t &bb,
+                                            const f16x8_t (&qreg)[D / 16], f32x16_t (&sacc)[2]) {
     constexpr int KS = D / 16;
     const f32x16_t zero = {};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bo.b, zero, 0, 0, 0) : zero;
+        sacc[kb] = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bb, zero, 0, 0, 0) : zero;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -142,6 +180,13 @@ __device__ __forceinline__ void qk_tile_off(const uint16_t *__restrict__ kl, con
             const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + koff[ks]);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sacc[kb], 0, 0, 0);
         }
+}
+
+template <int D, bool ALIBI>
+__device__ __forceinline__ void qk_tile_off(const uint16_t *__restrict__ kl, const int (&koff)[D / 16],
+                                            const BiasOperands &bo, const f16x8_t (&qreg)[D / 16],
+                                            f32x16_t (&sacc)[2]) {
+    qk_tile_off<D, ALIBI>(kl, koff, bo, bo.b, qreg, sacc);
 }
 
 }  // namespace

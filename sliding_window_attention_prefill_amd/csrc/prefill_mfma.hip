@@ -341,26 +341,30 @@ __device__ __forceinline__ void dma_tile(uint16_t *__restrict__ dst, __amdgpu_bu
     dma_rounds<Tile<D>::DMA_W>(dst, r, base, off, wave);
 }
 
-// S^T = K Q^T for the 64 keys of one tile.
-template <int D, bool ALIBI>
+// S^T = K Q^T for the 64 keys of one tile at j0 (i: this lane's query). For sigmoid the
+// product is the negated base-2 logit t = -x log2(e) itself: q enters scaled by -cs and
+// the bias instruction adds -slope log2(e) (i - j), its query part refreshed per tile.
+template <int D, int MODE, bool ALIBI>
 __device__ __forceinline__ void qk_tile(const uint16_t *__restrict__ kl, const LaneOffsets<D> &lo,
                                         const BiasOperands &bo, const f16x8_t (&qreg)[D / 16],
-                                        f32x16_t (&sacc)[2]) {
-    qk_tile_off<D, ALIBI>(kl, lo.k, bo, qreg, sacc);
+                                        f32x16_t (&sacc)[2], int i, int j0) {
+    if (MODE == 0 && ALIBI) qk_tile_off<D, ALIBI>(kl, lo.k, bo, query_term(bo, i - j0), qreg, sacc);
+    else qk_tile_off<D, ALIBI>(kl, lo.k, bo, qreg, sacc);
 }
 
 // Scores of one tile made ready for weighting (run in the step that formed them): edge
-// masking, and for softmax the base-2 logits x log2(e) = cs * acc + bias_q
-// (bias_q = slope log2(e) (i - j0), zero without ALiBi) with the running maximum and the
-// lazy rescale of the accumulator.
+// masking (sigmoid scores are negated logits, so an excluded key gets +inf), and for
+// softmax the base-2 logits x log2(e) = cs * acc + bias_q (bias_q = slope log2(e) (i - j0),
+// zero without ALiBi) with the running maximum and the lazy rescale of the accumulator.
 template <int D, int MODE, bool ALIBI, bool DIL>
 __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
                                             float &m_run, float &l_run, float cs, float bias_q,
                                             int kind, int dq, int jb, int w, int s, int dmask) {
     constexpr int DB = D / 32;
     // the stride test exists only in the dilated instantiations
-    if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, DIL ? dmask : 0);
-    else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s, DIL ? dmask : 0);
+    constexpr float fill = MODE == 0 ? INFINITY : -INFINITY;
+    if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, DIL ? dmask : 0, fill);
+    else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s, DIL ? dmask : 0, fill);
     if (MODE == 1) {
         // excluded keys stay -inf
 #pragma unroll
@@ -397,17 +401,16 @@ __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc
 template <int D, int MODE, bool VF16>
 __device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const LaneOffsets<D> &lo,
                                          f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
-                                         float m_run, float &l_run, float cs, float bias_q) {
+                                         float m_run, float &l_run) {
     constexpr int DB = D / 32;
     if (MODE == 0) {
-        // sigma(x) = 1 / (1 + 2^t) with t = -x log2(e); an excluded key has t = +inf -> 0
+        // sigma(x) = 1 / (1 + 2^t); the scores already are t = -x log2(e) (an excluded key
+        // has t = +inf -> 0)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float t = fmaf(sacc[kb][e], -cs, -bias_q);
-                sacc[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
-            }
+            for (int e = 0; e < 16; ++e)
+                sacc[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sacc[kb][e]));
     } else {
         float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -517,9 +520,8 @@ __device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
     if (has1) load_v<D, VF16>(v_fill, cx, lo, j1);
     const int kind0 = cx.kind_of(j0);
     const int kind1 = has1 ? cx.kind_of(j1) : -1;
-    const float bq0 = cx.slope_l2 * (float)(cx.i - j0);
-    if (kind1 >= 0) qk_tile<D, ALIBI>(k_next, lo, bo, qreg, s_next);
-    if (kind0 >= 0) weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run, cx.cs, bq0);
+    if (kind1 >= 0) qk_tile<D, MODE, ALIBI>(k_next, lo, bo, qreg, s_next, cx.i, j1);
+    if (kind0 >= 0) weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run);
     if (kind1 >= 0)
         prep_scores<D, MODE, ALIBI, DIL>(s_next, oacc, m_run, l_run, cx.cs,
                                     cx.slope_l2 * (float)(cx.i - j1), kind1,
@@ -546,10 +548,10 @@ __device__ __forceinline__ void plain_step(uint16_t *__restrict__ k_fill,
     if (kind >= 0) {
         f32x16_t sacc[2];
         const float bq = cx.slope_l2 * (float)(cx.i - j0);
-        qk_tile<D, ALIBI>(k_cur, lo, bo, qreg, sacc);
+        qk_tile<D, MODE, ALIBI>(k_cur, lo, bo, qreg, sacc, cx.i, j0);
         prep_scores<D, MODE, ALIBI, DIL>(sacc, oacc, m_run, l_run, cx.cs, bq, kind,
                                     cx.i - j0 - 4 * cx.g, j0 + 4 * cx.g, cx.w, cx.s, cx.dmask);
-        weigh_pv<D, MODE, VF16>(v_cur, lo, sacc, oacc, m_run, l_run, cx.cs, bq);
+        weigh_pv<D, MODE, VF16>(v_cur, lo, sacc, oacc, m_run, l_run);
     }
 }
 
@@ -645,7 +647,10 @@ void prefill_mfma_kernel(MfmaParams p) {
         cx.cs = p.cs;
         cx.slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;  // bias in base-2 units
     }
-    const BiasOperands bo = bias_operands(ALIBI ? cx.slope_l2 / p.cs : 0.0f, lane);
+    // softmax: key part -(slope log2(e) / cs) kappa of the unscaled product; sigmoid: the
+    // whole bias of the negated logit, key part slope log2(e) kappa plus the query part
+    const BiasOperands bo = MODE == 0 ? bias_operands(ALIBI ? -cx.slope_l2 : 0.0f, lane, ALIBI)
+                                      : bias_operands(ALIBI ? cx.slope_l2 / p.cs : 0.0f, lane);
 
     LaneOffsets<D> lo;
 #pragma unroll
@@ -667,10 +672,12 @@ void prefill_mfma_kernel(MfmaParams p) {
         lo.dvraw[r] = (uint32_t)row * (p.chunked ? (uint32_t)(2 * D) : p.row_bytes) + c * 16;
     }
 
-    // ---- this lane's query fragment (B operand of S^T = K Q^T): rotated, float16
+    // ---- this lane's query fragment (B operand of S^T = K Q^T): rotated, float16; for
+    // sigmoid scaled by -cs first, so that the product is the negated base-2 logit
     f16x8_t qreg[KS];
     {
         const uint16_t *qrow = p.q + ((qrow0 + (i - qpos0)) * p.Hq + h) * D;
+        const float qs = -p.cs;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 x = make_uint4(0, 0, 0, 0);
@@ -678,9 +685,9 @@ void prefill_mfma_kernel(MfmaParams p) {
                 x = *reinterpret_cast<const uint4 *>(qrow + ks * 16 + g * 8);
                 if (rope) {
                     const float4 *t = reinterpret_cast<const float4 *>(p.rope + ((int64_t)i * (D / 2) + ks * 8 + g * 4) * 2);
-                    x = rotate_chunk(x, t[0], t[1]);
+                    x = MODE == 0 ? rotate_chunk_scaled(x, t[0], t[1], qs) : rotate_chunk(x, t[0], t[1]);
                 } else {
-                    x = convert_chunk(x);
+                    x = MODE == 0 ? convert_chunk_scaled(x, qs) : convert_chunk(x);
                 }
             }
             qreg[ks] = __builtin_bit_cast(f16x8_t, x);
@@ -704,7 +711,7 @@ void prefill_mfma_kernel(MfmaParams p) {
         {
             const int j0 = cx.j0_of(0), kind0 = cx.kind_of(j0);
             if (kind0 >= 0) {
-                qk_tile<D, ALIBI>(kbuf0, lo, bo, qreg, sa);
+                qk_tile<D, MODE, ALIBI>(kbuf0, lo, bo, qreg, sa, i, j0);
                 prep_scores<D, MODE, ALIBI, DIL>(sa, oacc, m_run, l_run, cx.cs,
                                             cx.slope_l2 * (float)(i - j0), kind0, i - j0 - 4 * g,
                                             j0 + 4 * g, cx.w, cx.s, cx.dmask);
