@@ -104,6 +104,21 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
         }
 }
 
+// The two one-sided cuts of an edge tile, one compare each: keys after the query (causal
+// edge, i - j < 0) and keys that left the window (i - j >= w; dqw = dq - w).
+__device__ __forceinline__ void mask_causal(f32x16_t (&sacc)[2], int dq, float fill) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb][e] = key_of(kb, e) <= dq ? sacc[kb][e] : fill;
+}
+__device__ __forceinline__ void mask_far(f32x16_t (&sacc)[2], int dqw, float fill) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kb][e] = key_of(kb, e) > dqw ? sacc[kb][e] : fill;
+}
+
 // Operands of one extra matrix instruction per 32-key block that puts the key part of the
 // ALiBi bias into the score accumulator: with r = slope log2(e) / cs split as
 // 2^a (hi + lo) in float16, A row m holds (2^a kappa, 2^a kappa) and every B column

@@ -363,7 +363,9 @@ __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc
     constexpr int DB = D / 32;
     // the stride test exists only in the dilated instantiations
     constexpr float fill = MODE == 0 ? INFINITY : -INFINITY;
-    if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, DIL ? dmask : 0, fill);
+    if (D == 64 && kind == 3) mask_causal(sacc, dq, fill);
+    else if (D == 64 && kind == 4) mask_far(sacc, dq - w, fill);
+    else if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, DIL ? dmask : 0, fill);
     else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s, DIL ? dmask : 0, fill);
     if (MODE == 1) {
         // excluded keys stay -inf
@@ -477,11 +479,18 @@ struct TileCtx {
         return (t < ts_end ? t : tw_begin + (t - ts_end)) * BK;
     }
     // 0 = every pair in the key set, 1 = cut by the window edges, 2 = also holds sinks,
-    // -1 = no pair in the key set (wave-uniform: this wavefront's queries [qa, qb])
+    // 3 = cut by the causal edge only, 4 = cut by the far window edge only (3 and 4 with
+    // ONE_SIDED, for contiguous windows), -1 = no pair in the key set (wave-uniform: this
+    // wavefront's queries [qa, qb])
+    template <bool ONE_SIDED>
     __device__ __forceinline__ int kind_of(int j0) const {
         if (qa >= N || j0 > qb || (qa - (j0 + BK - 1) >= w && j0 >= s)) return -1;
-        if ((j0 + BK - 1 <= qa) && ((qb - j0 < w && dmask == 0) || j0 + BK - 1 < s)) return 0;
-        return j0 >= s ? 1 : 2;
+        const bool causal_ok = j0 + BK - 1 <= qa, far_ok = qb - j0 < w;
+        if (causal_ok && ((far_ok && dmask == 0) || j0 + BK - 1 < s)) return 0;
+        if (j0 < s) return 2;
+        if (ONE_SIDED && dmask == 0 && far_ok) return 3;
+        if (ONE_SIDED && dmask == 0 && causal_ok) return 4;
+        return 1;
     }
 };
 
@@ -518,8 +527,8 @@ __device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
     if (t + 2 < cx.n_tiles) load_k<D>(k_fill, cx, lo, cx.j0_of(t + 2));
     const int j0 = cx.j0_of(t), j1 = cx.j0_of(t + 1);
     if (has1) load_v<D, VF16>(v_fill, cx, lo, j1);
-    const int kind0 = cx.kind_of(j0);
-    const int kind1 = has1 ? cx.kind_of(j1) : -1;
+    const int kind0 = cx.template kind_of<D == 64>(j0);
+    const int kind1 = has1 ? cx.template kind_of<D == 64>(j1) : -1;
     if (kind1 >= 0) qk_tile<D, MODE, ALIBI>(k_next, lo, bo, qreg, s_next, cx.i, j1);
     if (kind0 >= 0) weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run);
     if (kind1 >= 0)
@@ -544,7 +553,7 @@ __device__ __forceinline__ void plain_step(uint16_t *__restrict__ k_fill,
         load_v<D, VF16>(v_fill, cx, lo, j1);
     }
     const int j0 = cx.j0_of(t);
-    const int kind = cx.kind_of(j0);
+    const int kind = cx.template kind_of<D == 64>(j0);
     if (kind >= 0) {
         f32x16_t sacc[2];
         const float bq = cx.slope_l2 * (float)(cx.i - j0);
@@ -709,7 +718,7 @@ void prefill_mfma_kernel(MfmaParams p) {
         if (cx.n_tiles > 1) load_k<D>(kbuf1, cx, lo, cx.j0_of(1));
         __syncthreads();
         {
-            const int j0 = cx.j0_of(0), kind0 = cx.kind_of(j0);
+            const int j0 = cx.j0_of(0), kind0 = cx.template kind_of<D == 64>(j0);
             if (kind0 >= 0) {
                 qk_tile<D, MODE, ALIBI>(kbuf0, lo, bo, qreg, sa, i, j0);
                 prep_scores<D, MODE, ALIBI, DIL>(sa, oacc, m_run, l_run, cx.cs,
