@@ -158,33 +158,71 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
     const int64_t b = rest / p.n_ktiles;
     const int64_t h0 = (int64_t)hg * PACK_HG;
     const int nh = p.Hkv - h0 < PACK_HG ? (int)(p.Hkv - h0) : PACK_HG;
+    constexpr int R = T::KPT;
+    if constexpr (!PACK_V) {
+        // keys only: every load of the block is issued before the first store (the images
+        // may not be assumed disjoint from the inputs, so a store would order later loads
+        // after it)
+        uint4 xk[R][PACK_HG];
+        float4 t0[R], t1[R];
 #pragma unroll
-    for (int r = 0; r < T::KPT; ++r) {
-        const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
-        const int64_t j = (int64_t)jt * BK + row;
-        const bool in = j < p.N;
-        float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
-        if (ROT && in) {
-            const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
-            t0 = as_float4(ldg16(t));
-            t1 = as_float4(ldg16(t + 4));
-        }
-        const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
-        const int vslot = (row * T::C + (c ^ vswz<D>(row))) * 8;
-#pragma unroll
-        for (int u = 0; u < PACK_HG; ++u) {
-            if (u >= nh) break;
-            const int64_t hkv = h0 + u;
-            uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
-            if (in) {
-                const int64_t off = ((b * p.N + j) * p.Hkv + hkv) * D + c * 8;
-                xk = ldg16(p.k + off);
-                xk = ROT ? rotate_chunk(xk, t0, t1) : convert_chunk(xk);
-                if (PACK_V) xv = convert_chunk(ldg16(p.v + off));
+        for (int r = 0; r < R; ++r) {
+            const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+            const int64_t j = (int64_t)jt * BK + row;
+            const bool in = j < p.N;
+            t0[r] = make_float4(1.f, 0.f, 1.f, 0.f);
+            t1[r] = t0[r];
+            if (ROT && in) {
+                const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
+                t0[r] = as_float4(ldg16(t));
+                t1[r] = as_float4(ldg16(t + 4));
             }
-            const int64_t img = ((b * p.Hkv + hkv) * p.n_ktiles + jt) * T::IMG;
-            stg16(p.kimg + img + kslot, xk);
-            if (PACK_V) stg16(p.vimg + img + vslot, xv);
+#pragma unroll
+            for (int u = 0; u < PACK_HG; ++u) {
+                xk[r][u] = make_uint4(0, 0, 0, 0);
+                if (in && u < nh) xk[r][u] = ldg16(p.k + ((b * p.N + j) * p.Hkv + h0 + u) * D + c * 8);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+            const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
+#pragma unroll
+            for (int u = 0; u < PACK_HG; ++u) {
+                if (u >= nh) break;
+                const int64_t img = ((b * p.Hkv + h0 + u) * p.n_ktiles + jt) * T::IMG;
+                stg16(p.kimg + img + kslot, ROT ? rotate_chunk(xk[r][u], t0[r], t1[r]) : convert_chunk(xk[r][u]));
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+            const int64_t j = (int64_t)jt * BK + row;
+            const bool in = j < p.N;
+            float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
+            if (ROT && in) {
+                const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
+                t0 = as_float4(ldg16(t));
+                t1 = as_float4(ldg16(t + 4));
+            }
+            const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
+            const int vslot = (row * T::C + (c ^ vswz<D>(row))) * 8;
+#pragma unroll
+            for (int u = 0; u < PACK_HG; ++u) {
+                if (u >= nh) break;
+                const int64_t hkv = h0 + u;
+                uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
+                if (in) {
+                    const int64_t off = ((b * p.N + j) * p.Hkv + hkv) * D + c * 8;
+                    xk = ldg16(p.k + off);
+                    xk = ROT ? rotate_chunk(xk, t0, t1) : convert_chunk(xk);
+                    xv = convert_chunk(ldg16(p.v + off));
+                }
+                const int64_t img = ((b * p.Hkv + hkv) * p.n_ktiles + jt) * T::IMG;
+                stg16(p.kimg + img + kslot, xk);
+                stg16(p.vimg + img + vslot, xv);
+            }
         }
     }
 }
