@@ -438,11 +438,7 @@ void bwd_dq_kernel(BwdParams p) {
         if (iq < N) {
             const float4 x = *reinterpret_cast<const float4 *>(ol + row * T::OSTR + 4 * c4);
             const int64_t off = (((int64_t)b * p.N + iq) * p.Hq + h) * D + 4 * c4;
-            if (p.out_bf16)
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.dq) + off) =
-                    make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
-            else
-                *reinterpret_cast<float4 *>(static_cast<float *>(p.dq) + off) = x;
+            store_out4<false>(p.dq, p.out_bf16, off, x.x, x.y, x.z, x.w);
         }
     }
 }
@@ -663,17 +659,9 @@ void bwd_dkv_kernel(BwdParams p) {
                 k0 = u0.x; k1 = u0.y; k2 = u1.x; k3 = u1.y;
             }
             const int64_t off = (((int64_t)b * p.N + j) * p.Hkv + hkv) * D + d0;
-            if (p.out_bf16) {
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.dk) + off) =
-                    make_uint2(pack_bf16x2(k0, k1), pack_bf16x2(k2, k3));
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.dv) + off) =
-                    make_uint2(pack_bf16x2(dv[db][4 * r], dv[db][4 * r + 1]),
-                               pack_bf16x2(dv[db][4 * r + 2], dv[db][4 * r + 3]));
-            } else {
-                *reinterpret_cast<float4 *>(static_cast<float *>(p.dk) + off) = make_float4(k0, k1, k2, k3);
-                *reinterpret_cast<float4 *>(static_cast<float *>(p.dv) + off) =
-                    make_float4(dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2], dv[db][4 * r + 3]);
-            }
+            store_out4<false>(p.dk, p.out_bf16, off, k0, k1, k2, k3);
+            store_out4<false>(p.dv, p.out_bf16, off, dv[db][4 * r], dv[db][4 * r + 1], dv[db][4 * r + 2],
+                       dv[db][4 * r + 3]);
         }
 }
 
@@ -929,11 +917,7 @@ void bwd_dkv2_kernel(BwdParams p) {
             }
             void *dst = role_p ? p.dv : p.dk;
             const int64_t off = (((int64_t)b * p.N + j) * p.Hkv + hkv) * D + d0;
-            if (p.out_bf16)
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst) + off) =
-                    make_uint2(pack_bf16x2(x0, x1), pack_bf16x2(x2, x3));
-            else
-                *reinterpret_cast<float4 *>(static_cast<float *>(dst) + off) = make_float4(x0, x1, x2, x3);
+            store_out4<false>(dst, p.out_bf16, off, x0, x1, x2, x3);
         }
 }
 

@@ -68,6 +68,31 @@ __device__ __forceinline__ uint4 convert_chunk_scaled(uint4 x, float f) {
                       to_f16_pair_scaled(x.z, f), to_f16_pair_scaled(x.w, f));
 }
 
+// Four output values at element offset off of a float32 or bf16 output. STREAM: streaming
+// (non-temporal) stores, for outputs the kernel does not read again whose stores cover
+// whole cache lines: they stay out of L2, which is left to the K/V tiles other workgroups
+// still read. Scattered partial-line stores are better merged in L2 (plain stores).
+template <bool STREAM>
+__device__ __forceinline__ void store_out4(void *out, bool bf16, int64_t off, float a, float b,
+                                           float c, float d) {
+    if (bf16) {
+        const uint64_t v = (uint64_t)pack_bf16x2(a, b) | ((uint64_t)pack_bf16x2(c, d) << 32);
+        uint64_t *dst = reinterpret_cast<uint64_t *>(static_cast<uint16_t *>(out) + off);
+        if (STREAM) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+    } else {
+        float *dst = static_cast<float *>(out) + off;
+        if (STREAM) {
+            __builtin_nontemporal_store(a, dst);
+            __builtin_nontemporal_store(b, dst + 1);
+            __builtin_nontemporal_store(c, dst + 2);
+            __builtin_nontemporal_store(d, dst + 3);
+        } else {
+            *reinterpret_cast<float4 *>(dst) = make_float4(a, b, c, d);
+        }
+    }
+}
+
 // Buffer -> LDS transfers: ROUNDS rounds of 1 KB per wavefront; lane l of round i lands at
 // bytes 16 l of that round's kilobyte (wavefront wave fills kilobytes wave * ROUNDS + i).
 // off[i] is this lane's source offset.

@@ -822,11 +822,7 @@ void prefill_mfma_kernel(MfmaParams p) {
                 if (iq < N) {
                     const float4 x = *reinterpret_cast<const float4 *>(ol + qrow * T::OSTR + 4 * c4);
                     const int64_t off = ((qrow0 + (iq - qpos0)) * p.Hq + h) * D + 4 * c4;
-                    if (p.out_bf16)
-                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.o) + off) =
-                            make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
-                    else
-                        *reinterpret_cast<float4 *>(static_cast<float *>(p.o) + off) = x;
+                    store_out4<true>(p.o, p.out_bf16, off, x.x, x.y, x.z, x.w);  // whole rows
                 }
             }
         }
