@@ -4,7 +4,10 @@ One step = one swa_prefill over the SWAT-340M-shaped layer (B=8, H=16, N=4096, d
 w=512, sigmoid + balanced ALiBi + RoPE, bf16 in / fp32 accumulate) with inputs already in
 HBM. The value is in-window TFLOP/s: 4 * B * H_q * d * sum_i |K(i)| per step, counting
 only the two contractions inside the band (SWAT: Sliding Window Attention Training, linear
-O(N w) cost), divided by the timed wall clock of K steps.
+O(N w) cost), divided by the timed wall clock of K steps. After the W warm-up steps the
+step keeps running untimed for 0.2 s (settle_steps in the line): the GPU's clocks ramp up
+over the first milliseconds of sustained load, and the timed steps should see the steady
+state.
 
 The JSON line also carries:
   roofline      the prefill kernel against the bf16 matrix-core peak, with its average
@@ -39,6 +42,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "SWA prefill in-window TFLOP/s (% MFMA peak); decode tok/s (% HBM BW)"
 KERNEL_SRC = os.path.join(ROOT, "sliding_window_attention_prefill_amd", "csrc", "prefill_mfma.hip")
+SETTLE_S = 0.2   # untimed steady load before the timed prefill steps (clock ramp-up)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic_swat340m.json")
 
 
@@ -100,6 +104,16 @@ def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the GPU's clocks ramp up over the first few milliseconds of sustained load: keep
+    # stepping (untimed) until SETTLE_S of it has passed, so the timed steps see the
+    # steady state (reported as settle_steps)
+    settle = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        for _ in range(10):
+            step()
+        settle += 10
+        torch.cuda.synchronize()
     # per-launch HIP events on the launch stream give the kernel's average duration
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -112,7 +126,7 @@ def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-    return wall, kernel_ms
+    return wall, kernel_ms, settle
 
 
 def bench_decode(cfg, out_dtype, copies=1):
@@ -344,13 +358,13 @@ def main():
 
     cfg = {"c2": wl.C2, "c3": wl.C3, "c5": wl.C5}[args.workload]
     out_dtype = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
-    wall, kernel_ms = bench_prefill(cfg, args.steps, args.warmup, out_dtype)
+    wall, kernel_ms, settle = bench_prefill(cfg, args.steps, args.warmup, out_dtype)
     flops = prefill_flops(cfg)
     value = flops * args.steps / wall / 1e12
     achieved = flops / (kernel_ms / 1e3) / 1e12
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup,
+        "steps": args.steps, "warmup": args.warmup, "settle_steps": settle,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "H_q": cfg.H_q, "H_kv": cfg.H_kv,
