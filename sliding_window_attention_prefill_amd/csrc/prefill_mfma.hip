@@ -692,12 +692,8 @@ void prefill_mfma_kernel(MfmaParams p) {
         cx.n_tiles = ts_end + (tw_end - tw_begin + 1);
         cx.ts_end = ts_end; cx.tw_begin = tw_begin;
         cx.cs = p.cs;
-        cx.slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;  // bias in base-2 units
+        cx.slope_l2 = 0.0f;  // set below, once its load has joined the others
     }
-    // softmax: key part -(slope log2(e) / cs) kappa of the unscaled product; sigmoid: the
-    // whole bias of the negated logit, key part slope log2(e) kappa plus the query part
-    const BiasOperands bo = MODE == 0 ? bias_operands(ALIBI ? -cx.slope_l2 : 0.0f, lane, ALIBI)
-                                      : bias_operands(ALIBI ? cx.slope_l2 / p.cs : 0.0f, lane);
 
     LaneOffsets<D> lo;
 #pragma unroll
@@ -719,27 +715,50 @@ void prefill_mfma_kernel(MfmaParams p) {
         lo.dvraw[r] = (uint32_t)row * (p.chunked ? (uint32_t)(2 * D) : p.row_bytes) + c * 16;
     }
 
+    // ---- first transfers: K tile 0 (and 1 when pipelined) and V tile 0, in flight while the
+    // query fragment and the slope load
+    const float slope = ALIBI ? p.slopes[h] : 0.0f;
+    load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
+    load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
+    if (T::PIPE && cx.n_tiles > 1) load_k<D>(kbuf1, cx, lo, cx.j0_of(1));
+
     // ---- this lane's query fragment (B operand of S^T = K Q^T): rotated, float16; for
-    // sigmoid scaled by -cs first, so that the product is the negated base-2 logit
+    // sigmoid scaled by -cs first, so that the product is the negated base-2 logit. Every
+    // load is issued before the first use (a lane past the end reads the last row and
+    // drops it), so the fragment costs one memory round trip.
     f16x8_t qreg[KS];
     {
-        const uint16_t *qrow = p.q + ((qrow0 + (i - qpos0)) * p.Hq + h) * D;
+        const bool in = i < N;
+        const int ic = in ? i : N - 1;
+        const uint16_t *qrow = p.q + ((qrow0 + (ic - qpos0)) * p.Hq + h) * D;
+        const float4 *trow = rope ? reinterpret_cast<const float4 *>(p.rope + (int64_t)ic * D)
+                                  : nullptr;
+        uint4 xq[KS];
+        float4 t0[KS], t1[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            xq[ks] = *reinterpret_cast<const uint4 *>(qrow + ks * 16 + g * 8);
+            if (rope) {
+                t0[ks] = trow[ks * 4 + g * 2];
+                t1[ks] = trow[ks * 4 + g * 2 + 1];
+            }
+        }
         const float qs = -p.cs;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (i < N) {
-                x = *reinterpret_cast<const uint4 *>(qrow + ks * 16 + g * 8);
-                if (rope) {
-                    const float4 *t = reinterpret_cast<const float4 *>(p.rope + ((int64_t)i * (D / 2) + ks * 8 + g * 4) * 2);
-                    x = MODE == 0 ? rotate_chunk_scaled(x, t[0], t[1], qs) : rotate_chunk(x, t[0], t[1]);
-                } else {
-                    x = MODE == 0 ? convert_chunk_scaled(x, qs) : convert_chunk(x);
-                }
-            }
-            qreg[ks] = __builtin_bit_cast(f16x8_t, x);
+            uint4 x;
+            if (rope) x = MODE == 0 ? rotate_chunk_scaled(xq[ks], t0[ks], t1[ks], qs) : rotate_chunk(xq[ks], t0[ks], t1[ks]);
+            else x = MODE == 0 ? convert_chunk_scaled(xq[ks], qs) : convert_chunk(xq[ks]);
+            qreg[ks] = __builtin_bit_cast(f16x8_t, in ? x : make_uint4(0, 0, 0, 0));
         }
     }
+
+    // ALiBi bias in base-2 units. Softmax: the key part -(slope log2(e) / cs) kappa of the
+    // unscaled product; sigmoid: the whole bias of the negated logit, key part
+    // slope log2(e) kappa plus the query part
+    if (ALIBI) cx.slope_l2 = slope * LOG2E;
+    const BiasOperands bo = MODE == 0 ? bias_operands(ALIBI ? -cx.slope_l2 : 0.0f, lane, ALIBI)
+                                      : bias_operands(ALIBI ? cx.slope_l2 / p.cs : 0.0f, lane);
 
     f32x16_t oacc[DB];
 #pragma unroll
@@ -751,9 +770,6 @@ void prefill_mfma_kernel(MfmaParams p) {
     if constexpr (T::PIPE) {
         // ---- prologue: K tiles 0 and 1, V tile 0; scores of tile 0
         f32x16_t sa[2], sb[2];
-        load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
-        load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
-        if (cx.n_tiles > 1) load_k<D>(kbuf1, cx, lo, cx.j0_of(1));
         __syncthreads();
         {
             const int j0 = cx.j0_of(0), kind0 = cx.template kind_of<D == 64>(j0);
@@ -777,8 +793,6 @@ void prefill_mfma_kernel(MfmaParams p) {
             __syncthreads();
         }
     } else {
-        load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
-        load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
         __syncthreads();
         for (int t = 0; t < cx.n_tiles; t += 2) {
             plain_step<D, MODE, ALIBI, VF16, DIL>(kbuf1, vbuf1, kbuf0, vbuf0, cx, lo, bo, qreg, oacc,
