@@ -341,27 +341,31 @@ void bwd_dq_kernel(BwdParams p) {
     tr_offsets<D>(lane, toff);
 
     // this lane's query and output-gradient fragments (B operands), rotated float16
+    // (every load in flight at once: a lane past the end reads the last row and drops it)
     f16x8_t qreg[KS], greg[KS];
+    const bool in = i < N;
+    const int ic = in ? i : N - 1;
     {
         const int64_t qslice = ((int64_t)b * p.Hq + h) * p.n_tiles * T::IMG;
-        const int it = i / BK, ri = i % BK;
+        const int it = ic / BK, ri = ic % BK;
+        uint4 xq[KS], xg[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 xq = make_uint4(0, 0, 0, 0), xg = xq;
-            if (i < N) {
-                const int64_t off = qslice + (int64_t)it * T::IMG + slot_of<D>(ri, 2 * ks + g);
-                xq = ldg16(p.qimg + off);
-                xg = ldg16(p.gimg + off);
-            }
-            qreg[ks] = __builtin_bit_cast(f16x8_t, xq);
-            greg[ks] = __builtin_bit_cast(f16x8_t, xg);
+            const int64_t off = qslice + (int64_t)it * T::IMG + slot_of<D>(ri, 2 * ks + g);
+            xq[ks] = ldg16(p.qimg + off);
+            xg[ks] = ldg16(p.gimg + off);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qreg[ks] = __builtin_bit_cast(f16x8_t, in ? xq[ks] : make_uint4(0, 0, 0, 0));
+            greg[ks] = __builtin_bit_cast(f16x8_t, in ? xg[ks] : make_uint4(0, 0, 0, 0));
         }
     }
     float l2 = 0.0f, dl = 0.0f;
-    if (MODE == 1 && i < N) {
-        const float2 st = reinterpret_cast<const float2 *>(p.stats)[((int64_t)b * p.Hq + h) * p.n_tiles * BK + i];
-        l2 = st.x;
-        dl = st.y;
+    if (MODE == 1) {
+        const float2 st = reinterpret_cast<const float2 *>(p.stats)[((int64_t)b * p.Hq + h) * p.n_tiles * BK + ic];
+        l2 = in ? st.x : 0.0f;
+        dl = in ? st.y : 0.0f;
     }
     const float slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;
     const BiasOperands bo = bias_operands(ALIBI ? slope_l2 / p.cs : 0.0f, lane);
@@ -503,20 +507,24 @@ void bwd_dkv_kernel(BwdParams p) {
     tr_offsets<D>(lane, toff);
 
     // this lane's key and value fragments (B operands of S = Q K^T and dP = dO V^T)
+    // (every load in flight at once: a lane past the end reads the last row and drops it)
     f16x8_t kreg[KS], vreg[KS];
     {
+        const bool jin = j < N;
+        const int jc = jin ? j : N - 1;
         const int64_t slice = ((int64_t)b * p.Hkv + hkv) * p.n_tiles * T::IMG;
-        const int jt = j / BK, rj = j % BK;
+        const int jt = jc / BK, rj = jc % BK;
+        uint4 xk[KS], xv[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            uint4 xk = make_uint4(0, 0, 0, 0), xv = xk;
-            if (j < N) {
-                const int64_t off = slice + (int64_t)jt * T::IMG + slot_of<D>(rj, 2 * ks + g);
-                xk = ldg16(p.kimg + off);
-                xv = ldg16(p.vimg + off);
-            }
-            kreg[ks] = __builtin_bit_cast(f16x8_t, xk);
-            vreg[ks] = __builtin_bit_cast(f16x8_t, xv);
+            const int64_t off = slice + (int64_t)jt * T::IMG + slot_of<D>(rj, 2 * ks + g);
+            xk[ks] = ldg16(p.kimg + off);
+            xv[ks] = ldg16(p.vimg + off);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            kreg[ks] = __builtin_bit_cast(f16x8_t, jin ? xk[ks] : make_uint4(0, 0, 0, 0));
+            vreg[ks] = __builtin_bit_cast(f16x8_t, jin ? xv[ks] : make_uint4(0, 0, 0, 0));
         }
     }
 
@@ -733,15 +741,17 @@ void bwd_dkv2_kernel(BwdParams p) {
     // this lane's key (P role) or value (dX role) fragment
     f16x8_t kv[KS];
     {
+        // every load in flight at once: a lane past the end reads the last row and drops it
         const uint16_t *img = role_p ? p.kimg : p.vimg;
+        const bool jin = j < N;
+        const int jc = jin ? j : N - 1;
         const int64_t slice = ((int64_t)b * p.Hkv + hkv) * p.n_tiles * T::IMG;
-        const int jt = j / BK, rj = j % BK;
+        const int jt = jc / BK, rj = jc % BK;
+        uint4 x[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            uint4 x = make_uint4(0, 0, 0, 0);
-            if (j < N) x = ldg16(img + slice + (int64_t)jt * T::IMG + slot_of<D>(rj, 2 * ks + g));
-            kv[ks] = __builtin_bit_cast(f16x8_t, x);
-        }
+        for (int ks = 0; ks < KS; ++ks) x[ks] = ldg16(img + slice + (int64_t)jt * T::IMG + slot_of<D>(rj, 2 * ks + g));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kv[ks] = __builtin_bit_cast(f16x8_t, jin ? x[ks] : make_uint4(0, 0, 0, 0));
     }
     f32x16_t acc[DB];
 #pragma unroll
