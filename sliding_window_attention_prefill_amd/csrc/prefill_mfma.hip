@@ -276,29 +276,31 @@ __global__ __launch_bounds__(256) void chunk_gather_kernel(GatherParams p) {
         }
         const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
         const int vslot = VF16 ? (row * T::C + (c ^ vswz<D>(row))) * 8 : (row * T::C + c) * 8;
+        // the row's loads for every head first, then its stores
+        const uint16_t *ksrc = src == 1 ? p.k_new : src == 2 ? p.k_ring : p.k_sink;
+        const uint16_t *vsrc = src == 1 ? p.v_new : src == 2 ? p.v_ring : p.v_sink;
+        uint4 xk[PACK_HG], xv[PACK_HG];
+#pragma unroll
+        for (int e = 0; e < PACK_HG; ++e) {
+            const int64_t hkv = h0 + e;
+            xk[e] = xv[e] = make_uint4(0, 0, 0, 0);
+            if (src != 0 && e < nh) {
+                const int64_t off =
+                    src == 1 ? ((cs.row0 + (j - cs.p0)) * p.Hkv + hkv) * D + c * 8
+                    : src == 2 ? ((b * p.Hkv + hkv) * p.w_ring + j % p.w_ring) * D + c * 8
+                               : ((b * p.Hkv + hkv) * p.s + j) * D + c * 8;
+                xk[e] = ldg16(ksrc + off);
+                xv[e] = ldg16(vsrc + off);
+            }
+        }
 #pragma unroll
         for (int e = 0; e < PACK_HG; ++e) {
             if (e >= nh) break;
-            const int64_t hkv = h0 + e;
-            uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
-            if (src == 1) {
-                const int64_t off = ((cs.row0 + (j - cs.p0)) * p.Hkv + hkv) * D + c * 8;
-                xk = ldg16(p.k_new + off);
-                xk = ROT ? rotate_chunk(xk, t0, t1) : convert_chunk(xk);
-                xv = ldg16(p.v_new + off);
-            } else if (src == 2) {
-                const int64_t off = ((b * p.Hkv + hkv) * p.w_ring + j % p.w_ring) * D + c * 8;
-                xk = convert_chunk(ldg16(p.k_ring + off));
-                xv = ldg16(p.v_ring + off);
-            } else if (src == 3) {
-                const int64_t off = ((b * p.Hkv + hkv) * p.s + j) * D + c * 8;
-                xk = convert_chunk(ldg16(p.k_sink + off));
-                xv = ldg16(p.v_sink + off);
-            }
-            if (VF16) xv = convert_chunk(xv);
-            const int64_t img = ((b * p.Hkv + hkv) * p.n_ktiles + u) * T::IMG;
-            stg16(p.kimg + img + kslot, xk);
-            stg16(p.vimg + img + vslot, xv);
+            // chunk rows are rotated here; ring and sink keys are stored rotated
+            const uint4 k = (ROT && src == 1) ? rotate_chunk(xk[e], t0, t1) : convert_chunk(xk[e]);
+            const int64_t img = ((b * p.Hkv + h0 + e) * p.n_ktiles + u) * T::IMG;
+            stg16(p.kimg + img + kslot, k);
+            stg16(p.vimg + img + vslot, VF16 ? convert_chunk(xv[e]) : xv[e]);
         }
     }
 }
@@ -326,37 +328,63 @@ __device__ __forceinline__ uint32_t rotate_pair_bf16(uint32_t w, float c, float 
 template <int D>
 __global__ __launch_bounds__(256) void chunk_append_kernel(ChunkAppendParams p) {
     constexpr int C = D / 8;
+    constexpr int U = 4;   // elements per thread whose loads are in flight together
     const int64_t b = blockIdx.x / p.n_rtiles;
     const int rt = blockIdx.x % p.n_rtiles;
     const ChunkSeq cs = chunk_seq(p.cg, b);
     if (!cs.valid || rt * BK >= cs.n) return;
     const int rows = cs.n - rt * BK < BK ? cs.n - rt * BK : BK;
     const int64_t per_row = p.Hkv * C;
-    for (int64_t e = threadIdx.x; e < rows * per_row; e += 256) {
-        const int r = rt * BK + (int)(e / per_row);
-        const int64_t hkv = (e % per_row) / C;
-        const int c = (int)(e % C);
-        const int64_t pos = (int64_t)cs.p0 + r;
-        const bool to_ring = r >= cs.n - p.w_ring, to_sink = pos < p.s;
-        if (!to_ring && !to_sink) continue;
-        const int64_t src = ((cs.row0 + r) * p.Hkv + hkv) * D + c * 8;
-        uint4 xk = ldg16(p.k_new + src);
-        const uint4 xv = ldg16(p.v_new + src);
-        if (p.rope) {
-            const float4 t0 = as_float4(ldg16(p.rope + (pos * (D / 2) + c * 4) * 2));
-            const float4 t1 = as_float4(ldg16(p.rope + (pos * (D / 2) + c * 4) * 2 + 4));
-            xk = make_uint4(rotate_pair_bf16(xk.x, t0.x, t0.y), rotate_pair_bf16(xk.y, t0.z, t0.w),
-                            rotate_pair_bf16(xk.z, t1.x, t1.y), rotate_pair_bf16(xk.w, t1.z, t1.w));
+    const int64_t total = rows * per_row;
+    for (int64_t e0 = threadIdx.x; e0 < total; e0 += 256 * U) {
+        // loads of U elements first (the ring and sink stores may not be assumed disjoint
+        // from the chunk, so a store would hold back the loads behind it)
+        uint4 xk[U], xv[U];
+        float4 t0[U], t1[U];
+        bool live[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e = e0 + 256 * u;
+            const int r = rt * BK + (int)(e / per_row);
+            const int64_t pos = (int64_t)cs.p0 + r;
+            live[u] = e < total && (r >= cs.n - p.w_ring || pos < p.s);
+            xk[u] = xv[u] = make_uint4(0, 0, 0, 0);
+            t0[u] = make_float4(1.f, 0.f, 1.f, 0.f);
+            t1[u] = t0[u];
+            if (live[u]) {
+                const int64_t hkv = (e % per_row) / C;
+                const int c = (int)(e % C);
+                const int64_t src = ((cs.row0 + r) * p.Hkv + hkv) * D + c * 8;
+                xk[u] = ldg16(p.k_new + src);
+                xv[u] = ldg16(p.v_new + src);
+                if (p.rope) {
+                    t0[u] = as_float4(ldg16(p.rope + (pos * (D / 2) + c * 4) * 2));
+                    t1[u] = as_float4(ldg16(p.rope + (pos * (D / 2) + c * 4) * 2 + 4));
+                }
+            }
         }
-        if (to_ring) {
-            const int64_t dst = ((b * p.Hkv + hkv) * p.w_ring + pos % p.w_ring) * D + c * 8;
-            stg16(p.k_ring + dst, xk);
-            stg16(p.v_ring + dst, xv);
-        }
-        if (to_sink) {
-            const int64_t dst = ((b * p.Hkv + hkv) * p.s + pos) * D + c * 8;
-            stg16(p.k_sink + dst, xk);
-            stg16(p.v_sink + dst, xv);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!live[u]) continue;
+            const int64_t e = e0 + 256 * u;
+            const int r = rt * BK + (int)(e / per_row);
+            const int64_t hkv = (e % per_row) / C;
+            const int c = (int)(e % C);
+            const int64_t pos = (int64_t)cs.p0 + r;
+            uint4 k = xk[u];
+            if (p.rope)
+                k = make_uint4(rotate_pair_bf16(k.x, t0[u].x, t0[u].y), rotate_pair_bf16(k.y, t0[u].z, t0[u].w),
+                               rotate_pair_bf16(k.z, t1[u].x, t1[u].y), rotate_pair_bf16(k.w, t1[u].z, t1[u].w));
+            if (r >= cs.n - p.w_ring) {
+                const int64_t dst = ((b * p.Hkv + hkv) * p.w_ring + pos % p.w_ring) * D + c * 8;
+                stg16(p.k_ring + dst, k);
+                stg16(p.v_ring + dst, xv[u]);
+            }
+            if (pos < p.s) {
+                const int64_t dst = ((b * p.Hkv + hkv) * p.s + pos) * D + c * 8;
+                stg16(p.k_sink + dst, k);
+                stg16(p.v_sink + dst, xv[u]);
+            }
         }
     }
 }
