@@ -22,6 +22,8 @@ The JSON line also carries:
                 TFLOP/s of whole swa_prefill_chunk calls;
   backward      the training backward (swa_prefill_backward) of this layer and of the
                 Mistral-7B-shaped one, in TFLOP/s of its five band contractions;
+  elementwise   the standalone rotation (swa_rope_apply on this layer's q) and ring append
+                (a 2,048-token chunk into 4,096-slot rings), algorithmic GB/s against HBM;
   cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -206,6 +208,56 @@ def bench_decode(cfg, out_dtype, copies=1):
     }
 
 
+def _event_ms(fn, reps: int = 20) -> float:
+    """Average duration of fn() over reps calls, from HIP events on the current stream."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_elementwise():
+    """The standalone rotation and ring append, HBM-bound: swa_rope_apply in place on the
+    SWAT-340M layer's q [8, 4096, 16, 64] bf16, and swa_kv_append of a 2,048-token chunk per
+    sequence (8 sequences, 8 kv heads, d 128, bf16) into 4,096-slot rings. Algorithmic
+    bytes: every element read and written once, plus the rotation angles of each position
+    (float32 cos, sin per pair) once."""
+    import torch
+    import sliding_window_attention_prefill_amd as swa
+    import swa_workloads as wl
+
+    out = []
+    cfg = wl.C2
+    q, _, _ = wl.prefill_inputs(cfg, device="cuda")
+    table = swa.swa_rope_table(cfg.N, cfg.d, cfg.rope_theta)
+    pos0 = torch.zeros(cfg.B, dtype=torch.int32, device="cuda")
+    ms = _event_ms(lambda: swa.swa_rope_apply(q, pos0, table))
+    nbytes = 2 * q.numel() * 2 + cfg.B * cfg.N * (cfg.d // 2) * 8
+    out.append({"op": "swa_rope_apply", "workload": "q_bf16_B8_N4096_H16_d64", "us_per_call": round(ms * 1e3, 2),
+                "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / ms / 1e6, 1),
+                "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)})
+    S, n_new, Hkv, d, w = 8, 2048, 8, 128, 4096
+    g = torch.Generator(device="cuda").manual_seed(7)
+    k = torch.randn((S, n_new, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((S, n_new, Hkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    cache = swa.SwaCache.empty(S, Hkv, w, 0, d, torch.bfloat16, device="cuda")
+    table = swa.swa_rope_table(w + n_new, d, 1e6)
+    pos = torch.full((S,), 1000, dtype=torch.int32, device="cuda")
+    ms = _event_ms(lambda: swa.swa_kv_append(cache, k, v, pos, rope_table=table))
+    nbytes = 2 * (2 * k.numel() * 2) + S * n_new * (d // 2) * 8
+    out.append({"op": "swa_kv_append", "workload": "chunk2048_bf16_S8_Hkv8_d128_w4096", "us_per_call": round(ms * 1e3, 2),
+                "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / ms / 1e6, 1),
+                "hbm_frac": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)})
+    return out
+
+
 def bench_chunk(cfg, out_dtype):
     """Chunked prefill over the ring cache: step t prefills rows [hist + t * chunk, hist +
     (t + 1) * chunk) of every sequence (gather, attention, append in one swa_prefill_chunk
@@ -332,6 +384,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-elementwise", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=8)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes three times (the "
@@ -383,6 +436,8 @@ def main():
                                  for c in (wl.DECODE_W4096, wl.DECODE_W32K)]
     if not args.no_chunk:
         result["chunk_prefill"] = bench_chunk(wl.CHUNK_W4096, torch.float32)
+    if not args.no_elementwise:
+        result["elementwise"] = bench_elementwise()
     if not args.no_backward:
         result["backward"] = [bench_backward(c) for c in (cfg, wl.C3)]
     if not args.no_cpu_baseline:

@@ -62,6 +62,52 @@ __global__ __launch_bounds__(128) void kv_append_kernel(CacheArgs c, const void 
     }
 }
 
+// Vector form for d % 8 == 0 and 16-byte aligned tensors: a thread moves one 8-element chunk
+// of one (sequence, token, kv head) row with 16-byte accesses; same writers as above.
+template <int DT>
+__global__ __launch_bounds__(256) void kv_append8_kernel(CacheArgs c, const void *__restrict__ k_new,
+                                                         const void *__restrict__ v_new,
+                                                         const int32_t *__restrict__ pos0,
+                                                         int64_t n_new, const float *__restrict__ rope,
+                                                         int64_t rope_rows) {
+    const int64_t c8 = c.d / 8;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= c.S * n_new * c.Hkv * c8) return;
+    const int64_t ch = idx % c8;
+    const int64_t row = idx / c8;   // (sq, n, hk)
+    const int64_t hk = row % c.Hkv;
+    const int64_t n = (row / c.Hkv) % n_new;
+    const int64_t sq = row / (c.Hkv * n_new);
+    const int64_t p0 = pos0[sq];
+    if (p0 < 0) return;
+    const int64_t p = p0 + n;
+    const bool to_ring = n >= n_new - c.w;
+    const bool to_sink = p < c.s;
+    if (!to_ring && !to_sink) return;
+    float kx[8], vx[8];
+    load8f<DT>(k_new, 8 * idx, kx);
+    load8f<DT>(v_new, 8 * idx, vx);
+    if (rope) {
+        if (p >= rope_rows) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) kx[m] = qnan();
+        } else {
+            const float *t = rope + (p * (c.d / 2) + 4 * ch) * 2;
+            rotate8(kx, as_float4(ldg16(t)), as_float4(ldg16(t + 4)));
+        }
+    }
+    if (to_ring) {
+        const int64_t dst = ((sq * c.Hkv + hk) * c.w + p % c.w) * c.d + 8 * ch;
+        store8f<DT>(c.k_ring, dst, kx);
+        store8f<DT>(c.v_ring, dst, vx);
+    }
+    if (to_sink) {
+        const int64_t dst = ((sq * c.Hkv + hk) * c.s + p) * c.d + 8 * ch;
+        store8f<DT>(c.k_sink, dst, kx);
+        store8f<DT>(c.v_sink, dst, vx);
+    }
+}
+
 // General decode: one block of 256 threads per (sequence, kv head) serves the G query heads
 // of the group. Keys are walked in chunks of KC staged in LDS as float32: sinks the window
 // no longer covers first, then ring positions max(0, p-w+1)..p in order.
@@ -881,6 +927,21 @@ hipError_t launch_kv_append(const CacheArgs &c, const void *k_new, const void *v
                             int64_t rope_rows, hipStream_t st) {
     const int64_t rows = c.S * n_new * c.Hkv;
     if (rows == 0) return hipSuccess;
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+                           reinterpret_cast<uintptr_t>(c.k_ring) | reinterpret_cast<uintptr_t>(c.v_ring) |
+                           reinterpret_cast<uintptr_t>(c.k_sink) | reinterpret_cast<uintptr_t>(c.v_sink) |
+                           reinterpret_cast<uintptr_t>(rope);
+    if (c.d % 8 == 0 && (bits & 15) == 0) {
+        const int64_t n = rows * (c.d / 8);
+        const dim3 grid((unsigned)((n + 255) / 256));
+        if (c.dt == 0)
+            hipLaunchKernelGGL(kv_append8_kernel<0>, grid, dim3(256), 0, st, c, k_new, v_new, pos0,
+                               n_new, rope, rope_rows);
+        else
+            hipLaunchKernelGGL(kv_append8_kernel<1>, grid, dim3(256), 0, st, c, k_new, v_new, pos0,
+                               n_new, rope, rope_rows);
+        return hipGetLastError();
+    }
     if (c.dt == 0)
         hipLaunchKernelGGL(kv_append_kernel<0>, dim3((unsigned)rows), dim3(128), 0, st, c, k_new,
                            v_new, pos0, n_new, rope, rope_rows);

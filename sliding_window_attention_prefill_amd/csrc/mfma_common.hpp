@@ -34,10 +34,6 @@ __device__ __forceinline__ float4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t
                        __uint_as_float(x[3]));
 }
 
-__device__ __forceinline__ float4 as_float4(uint4 x) {
-    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
-                       __uint_as_float(x.w));
-}
 
 // A dword of two bf16 inputs -> two float16 matrix operands, rotated by (c, s) or not.
 __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, float c, float s) {

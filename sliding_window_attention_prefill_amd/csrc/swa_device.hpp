@@ -84,6 +84,58 @@ template <> struct Elem<1> {
     }
 };
 
+__device__ __forceinline__ float4 as_float4(uint4 x) {
+    return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z),
+                       __uint_as_float(x.w));
+}
+
+// Eight consecutive elements (16-byte aligned) as floats, and back: one 16-byte access for
+// bf16, two for float32.
+template <int DT>
+__device__ __forceinline__ void load8f(const void *base, int64_t off, float (&x)[8]) {
+    if (DT == 1) {
+        const uint4 u = ldg16(static_cast<const uint16_t *>(base) + off);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            x[2 * m] = __uint_as_float(w[m] << 16);
+            x[2 * m + 1] = __uint_as_float(w[m] & 0xffff0000u);
+        }
+    } else {
+        const uint4 a = ldg16(static_cast<const float *>(base) + off);
+        const uint4 b = ldg16(static_cast<const float *>(base) + off + 4);
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int m = 0; m < 8; ++m) x[m] = __uint_as_float(w[m]);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void store8f(void *base, int64_t off, const float (&x)[8]) {
+    if (DT == 1) {
+        stg16(static_cast<uint16_t *>(base) + off,
+              make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                         pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])));
+    } else {
+        stg16(static_cast<float *>(base) + off,
+              make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                         __float_as_uint(x[3])));
+        stg16(static_cast<float *>(base) + off + 4,
+              make_uint4(__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]),
+                         __float_as_uint(x[7])));
+    }
+}
+
+// Rotate four interleaved pairs by the angles (cos, sin) in t0 = (c0, s0, c1, s1) and t1.
+__device__ __forceinline__ void rotate8(float (&x)[8], float4 t0, float4 t1) {
+    const float c[4] = {t0.x, t0.z, t1.x, t1.z}, sn[4] = {t0.y, t0.w, t1.y, t1.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float a = x[2 * m], b = x[2 * m + 1];
+        x[2 * m] = fmaf(-b, sn[m], a * c[m]);
+        x[2 * m + 1] = fmaf(a, sn[m], b * c[m]);
+    }
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x);
 
