@@ -856,15 +856,19 @@ void prefill_mfma_kernel(MfmaParams p) {
         }
         __syncthreads();
         if ((wave >> 2) == round) {
+            // this wavefront's 32 rows start at element obase; row r lies r * Hq * D further
+            // (32-bit offsets: Hq * D * 32 < 2^31 is a launch condition)
+            const int64_t obase = ((qrow0 + (qa - qpos0)) * p.Hq + h) * D;
+            void *ob = p.out_bf16 ? static_cast<void *>(static_cast<uint16_t *>(p.o) + obase)
+                                  : static_cast<void *>(static_cast<float *>(p.o) + obase);
+            const int rstride = (int)p.Hq * D;
 #pragma unroll
             for (int rr = 0; rr < 32 * C4 / 64; ++rr) {
                 const int ch = lane + 64 * rr;
                 const int qrow = ch / C4, c4 = ch % C4;
-                const int iq = qa + qrow;
-                if (iq < N) {
+                if (qa + qrow < N) {
                     const float4 x = *reinterpret_cast<const float4 *>(ol + qrow * T::OSTR + 4 * c4);
-                    const int64_t off = ((qrow0 + (iq - qpos0)) * p.Hq + h) * D + 4 * c4;
-                    store_out4<true>(p.o, p.out_bf16, off, x.x, x.y, x.z, x.w);  // whole rows
+                    store_out4<true>(ob, p.out_bf16, qrow * rstride + 4 * c4, x.x, x.y, x.z, x.w);  // whole rows
                 }
             }
         }
@@ -937,7 +941,8 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
     const int64_t img_slice = n_kt * BK * a.d * 2;
     const int64_t table = a.rope ? a.rope_rows * a.d * 4 : 0;
     return nb <= 0x7fffffff && a.B * a.Hkv * n_kt <= 0x7fffffff && slice < (int64_t(1) << 31) &&
-           img_slice < (int64_t(1) << 31) && table < (int64_t(1) << 31) && a.N < (int64_t(1) << 24);
+           img_slice < (int64_t(1) << 31) && table < (int64_t(1) << 31) && a.N < (int64_t(1) << 24) &&
+           a.Hq * a.d * 32 < (int64_t(1) << 31);
 }
 
 size_t prefill_mfma_workspace_bytes(const PrefillArgs &a) {
@@ -1063,6 +1068,7 @@ bool prefill_chunk_supported(const DecodeArgs &a, const CacheArgs &c, int64_t T,
     const int64_t img_slice = pl.n_ktiles * BK * c.d * 2;
     const int64_t table = a.rope ? a.rope_rows * c.d * 4 : 0;
     return nb <= 0x7fffffff && ngather <= 0x7fffffff && nappend <= 0x7fffffff &&
+           a.Hq * c.d * 32 < (int64_t(1) << 31) &&
            img_slice < (int64_t(1) << 31) && table < (int64_t(1) << 31);
 }
 
