@@ -115,18 +115,23 @@ __global__ __launch_bounds__(256) void bwd_pack_kv_kernel(PackKV p) {
             t1 = as_float4(ldg16(t + 4));
         }
         const int slot = slot_of<D>(row, c);
-        for (int e = 0; e < nh; ++e) {
-            const int64_t hkv = h0 + e;
-            uint4 xk = make_uint4(0, 0, 0, 0), xv = xk;
-            if (in) {
-                const int64_t off = ((b * p.N + j) * p.Hkv + hkv) * D + c * 8;
-                xk = ldg16(p.k + off);
-                xk = ROT ? rotate_chunk(xk, t0, t1) : convert_chunk(xk);
-                xv = convert_chunk(ldg16(p.v + off));
+        // the row's loads for every head first, then its stores
+        uint4 xk[4], xv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xk[e] = xv[e] = make_uint4(0, 0, 0, 0);
+            if (in && e < nh) {
+                const int64_t off = ((b * p.N + j) * p.Hkv + h0 + e) * D + c * 8;
+                xk[e] = ldg16(p.k + off);
+                xv[e] = ldg16(p.v + off);
             }
-            const int64_t img = ((b * p.Hkv + hkv) * p.n_tiles + jt) * T::IMG;
-            stg16(p.kimg + img + slot, xk);
-            stg16(p.vimg + img + slot, xv);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e >= nh) break;
+            const int64_t img = ((b * p.Hkv + h0 + e) * p.n_tiles + jt) * T::IMG;
+            stg16(p.kimg + img + slot, ROT ? rotate_chunk(xk[e], t0, t1) : convert_chunk(xk[e]));
+            stg16(p.vimg + img + slot, convert_chunk(xv[e]));
         }
     }
 }
@@ -167,34 +172,44 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(PackQ p) {
             t1 = as_float4(ldg16(t + 4));
         }
         const int slot = slot_of<D>(row, c);
-        for (int e = 0; e < nh; ++e) {
-            const int64_t h = h0 + e;
-            uint4 xq = make_uint4(0, 0, 0, 0), xg = xq;
-            float dot = 0.0f;
-            if (in) {
-                const int64_t off = ((b * p.N + i) * p.Hq + h) * D + c * 8;
-                xq = ldg16(p.q + off);
-                xq = ROT ? rotate_chunk(xq, t0, t1) : convert_chunk(xq);
-                float g8[8];
-                load8<OUT>(p.dout, off, g8);
-                xg = make_uint4(pack_f16x2(g8[0], g8[1]), pack_f16x2(g8[2], g8[3]),
-                                pack_f16x2(g8[4], g8[5]), pack_f16x2(g8[6], g8[7]));
-                if (MODE == 1) {
-                    float o8[8];
-                    load8<OUT>(p.o, off, o8);
+        // the row's loads for every head first (queries, output gradients, outputs and
+        // log-normalisers), then its conversions and stores
+        uint4 xq[4];
+        float g8[4][8], o8[4][8], lsev[4];
 #pragma unroll
-                    for (int m = 0; m < 8; ++m) dot = fmaf(g8[m], o8[m], dot);
+        for (int e = 0; e < 4; ++e) {
+            xq[e] = make_uint4(0, 0, 0, 0);
+            lsev[e] = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) g8[e][m] = o8[e][m] = 0.0f;
+            if (in && e < nh) {
+                const int64_t off = ((b * p.N + i) * p.Hq + h0 + e) * D + c * 8;
+                xq[e] = ldg16(p.q + off);
+                load8<OUT>(p.dout, off, g8[e]);
+                if (MODE == 1) {
+                    load8<OUT>(p.o, off, o8[e]);
+                    if (c == 0) lsev[e] = p.lse[(b * p.Hq + h0 + e) * p.N + i];
                 }
             }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e >= nh) break;
+            const int64_t h = h0 + e;
             const int64_t img = ((b * p.Hq + h) * p.n_tiles + it) * T::IMG;
-            stg16(p.qimg + img + slot, xq);
-            stg16(p.gimg + img + slot, xg);
+            stg16(p.qimg + img + slot, ROT ? rotate_chunk(xq[e], t0, t1) : convert_chunk(xq[e]));
+            stg16(p.gimg + img + slot,
+                  make_uint4(pack_f16x2(g8[e][0], g8[e][1]), pack_f16x2(g8[e][2], g8[e][3]),
+                             pack_f16x2(g8[e][4], g8[e][5]), pack_f16x2(g8[e][6], g8[e][7])));
             if (MODE == 1) {
+                float dot = 0.0f;
+#pragma unroll
+                for (int m = 0; m < 8; ++m) dot = fmaf(g8[e][m], o8[e][m], dot);
                 // the C chunks of a row sit in C consecutive lanes
                 dot = T::C == 8 ? group8_sum(dot) : group16_sum(dot);
                 if (c == 0) {
                     float2 st;
-                    st.x = in ? p.lse[(b * p.Hq + h) * p.N + i] * LOG2E : INFINITY;
+                    st.x = in ? lsev[e] * LOG2E : INFINITY;
                     st.y = in ? dot : 0.0f;
                     reinterpret_cast<float2 *>(p.stats)[(b * p.Hq + h) * (int64_t)p.n_tiles * BK + i] = st;
                 }
@@ -403,7 +418,7 @@ void bwd_dq_kernel(BwdParams p) {
                     if (MODE == 0) {
                         const float pe = __builtin_amdgcn_rcpf(
                             1.0f + __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], -p.cs, -bq)));
-                        sacc[kb2][e] = dacc[kb2][e] * pe * (1.0f - pe);
+                        sacc[kb2][e] = dacc[kb2][e] * fmaf(-pe, pe, pe);   // dP p (1 - p)
                     } else {
                         const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], p.cs, bq) - l2);
                         sacc[kb2][e] = pe * (dacc[kb2][e] - dl);
@@ -609,7 +624,7 @@ void bwd_dkv_kernel(BwdParams p) {
                         float pe, dxe;
                         if (MODE == 0) {
                             pe = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(x, -p.cs, -lb)));
-                            dxe = dacc[e] * pe * (1.0f - pe);
+                            dxe = dacc[e] * fmaf(-pe, pe, pe);   // dP p (1 - p)
                         } else {
                             pe = __builtin_amdgcn_exp2f(fmaf(x, p.cs, lb) - l2v[e4]);
                             dxe = pe * (dacc[e] - dlv[e4]);
@@ -874,7 +889,7 @@ void bwd_dkv2_kernel(BwdParams p) {
                             const int e = 4 * u + e4;
                             const f16x2_t h2 = __builtin_bit_cast(f16x2_t, wv[e >> 1]);
                             const float pe = (float)h2[e & 1];
-                            sd[qb][e] = MODE == 0 ? sd[qb][e] * pe * (1.0f - pe)
+                            sd[qb][e] = MODE == 0 ? sd[qb][e] * fmaf(-pe, pe, pe)
                                                   : pe * (sd[qb][e] - dlv[e4]);
                         }
                     }
