@@ -145,6 +145,7 @@ struct PackQ {
     const float *rope;
     int64_t N, Hq;
     int n_tiles;
+    float qs;          // factor on the query image: -scale log2(e) for sigmoid, else 1
 };
 
 // One block per (batch, 64-position tile, up to four query heads): rotated queries and the
@@ -197,7 +198,13 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(PackQ p) {
             if (e >= nh) break;
             const int64_t h = h0 + e;
             const int64_t img = ((b * p.Hq + h) * p.n_tiles + it) * T::IMG;
-            stg16(p.qimg + img + slot, ROT ? rotate_chunk(xq[e], t0, t1) : convert_chunk(xq[e]));
+            // sigmoid: the query image carries -scale log2(e), so that the score product is
+            // the negated base-2 logit (the dk/dv kernels undo the factor on dK)
+            if (MODE == 0)
+                stg16(p.qimg + img + slot, ROT ? rotate_chunk_scaled(xq[e], t0, t1, p.qs)
+                                               : convert_chunk_scaled(xq[e], p.qs));
+            else
+                stg16(p.qimg + img + slot, ROT ? rotate_chunk(xq[e], t0, t1) : convert_chunk(xq[e]));
             stg16(p.gimg + img + slot,
                   make_uint4(pack_f16x2(g8[e][0], g8[e][1]), pack_f16x2(g8[e][2], g8[e][3]),
                              pack_f16x2(g8[e][4], g8[e][5]), pack_f16x2(g8[e][6], g8[e][7])));
@@ -383,7 +390,10 @@ void bwd_dq_kernel(BwdParams p) {
         dl = in ? st.y : 0.0f;
     }
     const float slope_l2 = ALIBI ? p.slopes[h] * LOG2E : 0.0f;
-    const BiasOperands bo = bias_operands(ALIBI ? slope_l2 / p.cs : 0.0f, lane);
+    // softmax: key part -(slope log2(e) / cs) kappa of the unscaled product; sigmoid (query
+    // image scaled by -cs): the whole bias of the negated logit, key and query parts
+    const BiasOperands bo = MODE == 0 ? bias_operands(ALIBI ? -slope_l2 : 0.0f, lane, ALIBI)
+                                      : bias_operands(ALIBI ? slope_l2 / p.cs : 0.0f, lane);
 
     f32x16_t acc[DB];
 #pragma unroll
@@ -406,18 +416,19 @@ void bwd_dq_kernel(BwdParams p) {
         if (kind >= 0) {
             f32x16_t sacc[2], dacc[2];
             const uint16_t *kl = lds + cur * T::IMG, *vl = lds + (2 + cur) * T::IMG;
-            qk_tile_off<D, ALIBI>(kl, koff, bo, qreg, sacc);
+            qk_tile_off<D, ALIBI>(kl, koff, bo, (MODE == 0 && ALIBI) ? query_term(bo, i - j0) : bo.b,
+                                  qreg, sacc);
             qk_tile_off<D, false>(vl, koff, bo, greg, dacc);
-            if (kind == 1) mask_tile<false>(sacc, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s);
-            else if (kind == 2) mask_tile<true>(sacc, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s);
+            constexpr float fill = MODE == 0 ? INFINITY : -INFINITY;
+            if (kind == 1) mask_tile<false>(sacc, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s, 0, fill);
+            else if (kind == 2) mask_tile<true>(sacc, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s, 0, fill);
             const float bq = slope_l2 * (float)(i - j0);
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     if (MODE == 0) {
-                        const float pe = __builtin_amdgcn_rcpf(
-                            1.0f + __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], -p.cs, -bq)));
+                        const float pe = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sacc[kb2][e]));
                         sacc[kb2][e] = dacc[kb2][e] * fmaf(-pe, pe, pe);   // dP p (1 - p)
                     } else {
                         const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], p.cs, bq) - l2);
@@ -585,12 +596,16 @@ void bwd_dkv_kernel(BwdParams p) {
             const uint16_t *gl = ql + T::IMG;
             const float *stl = reinterpret_cast<const float *>(ql + 2 * T::IMG);
             const float slope_l2 = ALIBI ? p.slopes[hq] * LOG2E : 0.0f;
-            const BiasOperands bo = bias_operands(ALIBI ? -slope_l2 / p.cs : 0.0f, lane);
-            const float lb = slope_l2 * (float)(i0 - j);   // key part of the bias
+            // rows are queries here: softmax adds (slope log2(e) / cs) m for query offset m;
+            // sigmoid (query tiles scaled by -cs) the whole bias -slope log2(e) (i0 + m - j)
+            const BiasOperands bo = MODE == 0 ? bias_operands(ALIBI ? slope_l2 : 0.0f, lane, ALIBI)
+                                              : bias_operands(ALIBI ? -slope_l2 / p.cs : 0.0f, lane);
+            const f16x8_t bb = (MODE == 0 && ALIBI) ? query_term(bo, j - i0) : bo.b;
+            const float lb = slope_l2 * (float)(i0 - j);   // key part of the bias (softmax)
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const f32x16_t zero = {};
-                f32x16_t sacc = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[qb], bo.b, zero, 0, 0, 0) : zero;
+                f32x16_t sacc = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[qb], bb, zero, 0, 0, 0) : zero;
                 f32x16_t dacc = zero;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -619,11 +634,11 @@ void bwd_dkv_kernel(BwdParams p) {
                             const int dij = iq - j;
                             const bool ok = iq >= qlo && iq < qhi && iq < N && j < N && dij >= 0 &&
                                             (dij < p.w || j < p.s);
-                            x = ok ? x : -INFINITY;
+                            x = ok ? x : (MODE == 0 ? INFINITY : -INFINITY);
                         }
                         float pe, dxe;
                         if (MODE == 0) {
-                            pe = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(x, -p.cs, -lb)));
+                            pe = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
                             dxe = dacc[e] * fmaf(-pe, pe, pe);   // dP p (1 - p)
                         } else {
                             pe = __builtin_amdgcn_exp2f(fmaf(x, p.cs, lb) - l2v[e4]);
@@ -673,8 +688,10 @@ void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int d0 = 32 * db + 8 * r + 4 * g;
-            float k0 = dk[db][4 * r] * p.scale, k1 = dk[db][4 * r + 1] * p.scale;
-            float k2 = dk[db][4 * r + 2] * p.scale, k3 = dk[db][4 * r + 3] * p.scale;
+            // sigmoid accumulated dK against the query image scaled by -cs
+            const float dks = MODE == 0 ? -p.scale / p.cs : p.scale;
+            float k0 = dk[db][4 * r] * dks, k1 = dk[db][4 * r + 1] * dks;
+            float k2 = dk[db][4 * r + 2] * dks, k3 = dk[db][4 * r + 3] * dks;
             if (p.rope != nullptr) {
                 const float4 c = as_float4(ldg16(p.rope + ((int64_t)j * (D / 2) + d0 / 2) * 2));
                 const float2 u0 = unrotate(k0, k1, make_float2(c.x, c.y));
@@ -812,13 +829,17 @@ void bwd_dkv2_kernel(BwdParams p) {
         f32x16_t sd[2];                                       // P (P role) or dP (dX role)
         if (any) {
             const float slope_l2 = ALIBI ? p.slopes[hq] * LOG2E : 0.0f;
-            const BiasOperands bo = bias_operands(ALIBI ? -slope_l2 / p.cs : 0.0f, lane);
-            const float lb = slope_l2 * (float)(i0 - j);   // key part of the bias
+            // as in bwd_dkv_kernel: softmax adds (slope log2(e) / cs) m, sigmoid the whole
+            // bias of the negated logit
+            const BiasOperands bo = MODE == 0 ? bias_operands(ALIBI ? slope_l2 : 0.0f, lane, ALIBI)
+                                              : bias_operands(ALIBI ? -slope_l2 / p.cs : 0.0f, lane);
+            const f16x8_t bb = (MODE == 0 && ALIBI) ? query_term(bo, j - i0) : bo.b;
+            const float lb = slope_l2 * (float)(i0 - j);   // key part of the bias (softmax)
             const uint16_t *al = role_p ? ql : gl;          // A rows: Q for S, dO for dP
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 const f32x16_t zero = {};
-                f32x16_t a = (ALIBI && role_p) ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[qb], bo.b, zero, 0, 0, 0) : zero;
+                f32x16_t a = (ALIBI && role_p) ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[qb], bb, zero, 0, 0, 0) : zero;
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const f16x8_t ar = *reinterpret_cast<const f16x8_t *>(al + qb * 32 * D + qoff[ks]);
@@ -847,10 +868,10 @@ void bwd_dkv2_kernel(BwdParams p) {
                                 const int dij = iq - j;
                                 const bool ok = iq >= qlo && iq < qhi && iq < N && j < N && dij >= 0 &&
                                                 (dij < p.w || j < p.s);
-                                x = ok ? x : -INFINITY;
+                                x = ok ? x : (MODE == 0 ? INFINITY : -INFINITY);
                             }
                             sd[qb][e] = MODE == 0
-                                ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(fmaf(x, -p.cs, -lb)))
+                                ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x))
                                 : __builtin_amdgcn_exp2f(fmaf(x, p.cs, lb) - l2v[e4]);
                         }
                     }
@@ -932,7 +953,9 @@ void bwd_dkv2_kernel(BwdParams p) {
             float x0 = acc[db][4 * r], x1 = acc[db][4 * r + 1];
             float x2 = acc[db][4 * r + 2], x3 = acc[db][4 * r + 3];
             if (!role_p) {
-                x0 *= p.scale; x1 *= p.scale; x2 *= p.scale; x3 *= p.scale;
+                // sigmoid accumulated dK against the query image scaled by -cs
+                const float dks = MODE == 0 ? -p.scale / p.cs : p.scale;
+                x0 *= dks; x1 *= dks; x2 *= dks; x3 *= dks;
                 if (p.rope != nullptr) {
                     const float4 c = as_float4(ldg16(p.rope + ((int64_t)j * (D / 2) + d0 / 2) * 2));
                     const float2 u0 = unrotate(x0, x1, make_float2(c.x, c.y));
@@ -1029,6 +1052,7 @@ hipError_t launch_bwd_d(const PrefillArgs &a, const BwdPlan &pl, const void *q, 
         pq.q = static_cast<const uint16_t *>(q); pq.dout = dout; pq.o = o; pq.lse = lse;
         pq.qimg = qimg; pq.gimg = gimg; pq.stats = stats; pq.rope = a.rope; pq.N = a.N;
         pq.Hq = a.Hq; pq.n_tiles = nt;
+        pq.qs = a.mode == 0 ? -a.scale * LOG2E : 1.0f;
         const unsigned nb = (unsigned)(a.B * nt * ((a.Hq + 3) / 4));
 #define SWA_PACKQ(R, O, M) hipLaunchKernelGGL((bwd_pack_q_kernel<D, R, O, M>), dim3(nb), dim3(256), 0, st, pq)
         if (a.mode == 1) {
