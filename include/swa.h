@@ -64,11 +64,13 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * keys span r (w - 1) + 1 positions; the sinks are unchanged. The matrix-core path takes r a
  * power of two (other r run on the general kernel); the cache entry points take no
  * dilation.
- * bf16 inputs with d in {64, 128} and 16-byte aligned tensors run on the matrix cores,
- * which form the score product from float16 operands (rotated q and k) and the value
- * product from float16 (softmax) or bf16 (sigmoid) operands, with float32 accumulation:
- * those inputs must stay within the float16 range (|x| < 65504), and |slope| / scale below
- * 2^24. Other shapes run on a general float32 vector kernel.
+ * bf16 inputs with d in {64, 128}, H_q * d below 2^26 and 16-byte aligned tensors run on the
+ * matrix cores, which form the score product from float16 operands (rotated q and k; for
+ * sigmoid q is also multiplied by -scale * log2(e) before its rounding, and the ALiBi term
+ * enters the product through float16 splits of the slope and of the query offset) and the
+ * value product from float16 (softmax) or bf16 (sigmoid) operands, with float32
+ * accumulation: those inputs must stay within the float16 range (|x| < 65504), and
+ * |slope| / scale below 2^24. Other shapes run on a general float32 vector kernel.
  */
 typedef struct swa_prefill_params {
     int64_t B, H_q, H_kv, N, d;
