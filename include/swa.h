@@ -229,8 +229,9 @@ swa_status swa_decode(const swa_decode_params *p, const swa_cache *c, const void
  * position q_pos[q] - key k_new[q] (not yet rotated) and value v_new[q], both [num_seqs,
  * H_kv, d] in the cache dtype - is written to the ring (and to the sink store when
  * q_pos[q] < s) exactly as swa_kv_append with n_new = 1 writes it, and query q[q] is then
- * answered as swa_decode answers it. One launch instead of two: every (sequence, kv head)
- * is handled by a single workgroup, which uses the token it wrote without reading it back.
+ * answered as swa_decode answers it. The append costs no launch of its own: the workgroup
+ * whose key range holds q_pos writes the token and uses it without reading it back (long
+ * windows over few sequences add the merge launch that swa_decode also uses).
  * A sequence whose q_pos is invalid (negative, or outside the rotation table) gets NaN
  * outputs and its cache is left untouched. Other arguments as in swa_decode.
  */

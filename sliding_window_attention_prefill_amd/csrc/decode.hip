@@ -5,7 +5,7 @@
 // Positions 0..s-1 are also kept in a sink store beside the ring (Sliding Window Attention
 // glossary, "attention sink"; Sliding-window beats linear attention, SWA(64, 4)). Keys are
 // stored rotated at their own absolute position, so a decode step only rotates its query.
-#include "swa_device.hpp"
+#include "mfma_common.hpp"
 #include "swa_kernels.hpp"
 
 namespace swa {
@@ -253,21 +253,17 @@ __global__ __launch_bounds__(256) void decode_general_kernel(DecodeGen a, const 
     }
 }
 
-// Fast decode for a bf16 cache, d in {64, 128}, up to 8 query heads per kv head. One block
-// of 256 threads per (sequence, kv head) issues every K and V load of a 128-key chunk before
-// any arithmetic, so the whole working set of the step is in flight at once:
-//   score pass: 4 threads per key, each a quarter of the row, reduced with two shuffles;
-//   weights:    one wavefront per head, keys across lanes (wavefront max / sum reductions);
-//   value pass: thread (key group, 8-column chunk) accumulates 8 columns for every head,
-//               then the key groups are summed through LDS.
-// With APPEND the block first writes the new token (rotated key, value) to its ring slot
-// and sink entry, keeps it in LDS and uses that copy for position q_pos, so the slot it
-// wrote is never read back within the launch.
-// Split-KV: with nsplit > 1 the key list of a query is cut into nsplit contiguous, chunk-
-// aligned ranges, one block each; a block writes its unnormalised partial output with its
-// running maximum and sum to the workspace, and decode_combine_kernel merges the partials
-// (log-sum-exp rescaling for softmax, a plain sum for sigmoid). Only the block whose range
-// holds the query's own position appends the new token.
+// Decode for a bf16 cache, d in {64, 128}, G = H_q / H_kv in {1, 2, 4, 8}: the whole-window
+// kernel (w + s <= 128) and the matrix-core kernel (longer windows) below share these
+// arguments.
+// With APPEND a block first writes the new token (rotated key, value) to its ring slot and
+// sink entry, keeps it in LDS and uses that copy for position q_pos, so the slot it wrote is
+// never read back within the launch.
+// Split-KV: with nsplit > 1 the key list of a query is cut into nsplit contiguous ranges, one
+// block each; a block writes its unnormalised partial output with its running maximum and
+// sum to the workspace, and decode_combine_kernel merges the partials (log-sum-exp
+// rescaling for softmax, a plain sum for sigmoid). Only the block whose range holds the
+// query's own position appends the new token.
 struct DecodeFast {
     int S, Hq, Hkv, G, w, s, mode;
     int nsplit;          // key ranges per (sequence, kv head); 1 = no split
@@ -279,29 +275,6 @@ struct DecodeFast {
     uint16_t *k_ring, *v_ring, *k_sink, *v_sink;
 };
 
-constexpr int DEC_KC = 128;  // keys per chunk
-
-template <int D>
-struct DecLds {
-    static constexpr int C8 = D / 8;          // 16-byte chunks per row
-    static constexpr int KG = 256 / C8;       // key groups of the value pass
-    static constexpr int VK = DEC_KC / KG;    // keys per thread in the value pass
-    static constexpr int QE = D / 4;          // elements per thread in the score pass
-    // a head's query is kept as four quarters of QE values, each padded by 4 floats, so the
-    // four quarters that one wavefront reads at once sit in different banks
-    static constexpr int QQ = QE + 4;         // floats per stored quarter
-    static constexpr int QG = 4 * QQ;         // floats per stored head
-};
-
-template <int D>
-size_t decode_fast_lds(int G) {
-    using L = DecLds<D>;
-    return sizeof(float) * ((size_t)G * L::QG + (size_t)G * DEC_KC + 2 * D + 3 * 8 +
-                            (size_t)L::KG * G * D);
-}
-
-__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
-
 // Block barrier that orders LDS accesses only: global loads in flight stay in flight.
 __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -309,275 +282,7 @@ __device__ __forceinline__ void lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int D, int G, int OUT, bool APPEND>
-__global__ __launch_bounds__(256) void decode_fast_kernel(DecodeFast a, const uint16_t *__restrict__ q,
-                                                          const int32_t *__restrict__ q_pos,
-                                                          void *__restrict__ o,
-                                                          const uint16_t *__restrict__ k_new,
-                                                          const uint16_t *__restrict__ v_new) {
-    using L = DecLds<D>;
-    extern __shared__ float lds[];
-    float *qs = lds;                    // [G][4][QQ] rotated queries * scale * log2(e)
-    float *sc = qs + G * L::QG;         // [G][KC] scores, then weights
-    float *kn = sc + G * DEC_KC;        // [D] appended key (as stored)
-    float *vn = kn + D;                 // [D] appended value
-    float *ml = vn + D;                 // [3][8] max, sum, correction per head
-    float *red = ml + 24;               // [KG][G][D] partial outputs
-
-    const int split = blockIdx.x % a.nsplit, bsh = blockIdx.x / a.nsplit;
-    const int sq = bsh / a.Hkv, hk = bsh % a.Hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int p = q_pos[sq];
-    const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
-    if (!valid) {
-        // the combine kernel flags split outputs itself
-        if (a.nsplit == 1)
-            for (int idx = tid; idx < G * D; idx += 256)
-                Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G) * D + idx, qnan());
-        return;
-    }
-    // this block's range of the query's key list (sinks first, then the window)
-    const int lo_w = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
-    const int n_all = (a.s < lo_w ? a.s : lo_w) + (p - lo_w + 1);
-    const int per = ((n_all + a.nsplit - 1) / a.nsplit + DEC_KC - 1) / DEC_KC * DEC_KC;
-    const int k_begin = split * per < n_all ? split * per : n_all;
-    const int k_end = k_begin + per < n_all ? k_begin + per : n_all;
-    const bool owns_new = k_begin <= n_all - 1 && n_all - 1 < k_end;   // the query's own key
-    const int64_t ring_base = ((int64_t)sq * a.Hkv + hk) * a.w * D;
-    const int64_t sink_base = ((int64_t)sq * a.Hkv + hk) * a.s * D;
-    const int half = D / 2;
-
-    // ---- the new token (fused append) and the queries, rotated at position p
-    if (APPEND && owns_new && tid < half) {
-        const int64_t src = ((int64_t)sq * a.Hkv + hk) * D + 2 * tid;
-        float k0 = bf16_bits_to_f32(k_new[src]), k1 = bf16_bits_to_f32(k_new[src + 1]);
-        const uint32_t vv = *reinterpret_cast<const uint32_t *>(v_new + src);
-        if (a.rope) {
-            const float2 cs = reinterpret_cast<const float2 *>(a.rope)[(int64_t)p * half + tid];
-            const float r0 = fmaf(-k1, cs.y, k0 * cs.x);
-            k1 = fmaf(k0, cs.y, k1 * cs.x);
-            k0 = r0;
-        }
-        const uint32_t kk = pack_bf16x2(k0, k1);
-        *reinterpret_cast<uint32_t *>(a.k_ring + ring_base + (int64_t)(p % a.w) * D + 2 * tid) = kk;
-        *reinterpret_cast<uint32_t *>(a.v_ring + ring_base + (int64_t)(p % a.w) * D + 2 * tid) = vv;
-        if (p < a.s) {
-            *reinterpret_cast<uint32_t *>(a.k_sink + sink_base + (int64_t)p * D + 2 * tid) = kk;
-            *reinterpret_cast<uint32_t *>(a.v_sink + sink_base + (int64_t)p * D + 2 * tid) = vv;
-        }
-        kn[2 * tid] = bf16_bits_to_f32(kk & 0xffffu);
-        kn[2 * tid + 1] = bf16_bits_to_f32(kk >> 16);
-        vn[2 * tid] = bf16_bits_to_f32(vv & 0xffffu);
-        vn[2 * tid + 1] = bf16_bits_to_f32(vv >> 16);
-    }
-    for (int idx = tid; idx < G * half; idx += 256) {
-        const int g = idx / half, t = idx % half;
-        const int64_t src = ((int64_t)sq * a.Hq + hk * G + g) * D + 2 * t;
-        float x0 = bf16_bits_to_f32(q[src]), x1 = bf16_bits_to_f32(q[src + 1]);
-        if (a.rope) {
-            const float2 cs = reinterpret_cast<const float2 *>(a.rope)[(int64_t)p * half + t];
-            const float r0 = fmaf(-x1, cs.y, x0 * cs.x);
-            x1 = fmaf(x0, cs.y, x1 * cs.x);
-            x0 = r0;
-        }
-        const int col = 2 * t;   // a quarter holds QE consecutive columns
-        qs[g * L::QG + (col / L::QE) * L::QQ + col % L::QE] = x0 * a.cs;
-        qs[g * L::QG + (col / L::QE) * L::QQ + col % L::QE + 1] = x1 * a.cs;
-    }
-    if (tid < 8) {
-        ml[tid] = -INFINITY;
-        ml[8 + tid] = 0.0f;
-        ml[16 + tid] = 1.0f;
-    }
-    const int lo = lo_w;
-    const int n_sink = a.s < lo ? a.s : lo;
-    const int n_keys = k_end;
-    // ring slot of window position lo + m (0 <= m < w): lo mod w + m, less w past the end
-    // (rows past the key list, which are never read, get slot 0)
-    const int slot_lo = lo % a.w;
-    auto ring_slot = [&](int P) {
-        const int sl = slot_lo + (P - lo);
-        return sl < a.w ? sl : (sl - a.w < a.w ? sl - a.w : 0);
-    };
-
-    // value-pass ownership: 8 columns, keys kg, kg + KG, ...
-    const int c8 = tid % L::C8, kg = tid / L::C8;
-    float acc[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[g][c] = 0.0f;
-    __syncthreads();
-
-    // K rows of the next chunk are requested as soon as this chunk's scores are formed, V rows
-    // as soon as its values are added; the block barriers inside a chunk order LDS only, so
-    // those loads stay in flight across them.
-    uint4 kx[2][L::QE / 8];
-    int kpos[2];
-    uint4 vx[L::VK];
-    int vpos[L::VK];
-    auto load_k = [&](int cc) {
-        const int nk = n_keys - cc < DEC_KC ? n_keys - cc : DEC_KC;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int slot = tid + 256 * r, e = slot / 4, qq = slot % 4;
-            const int ee = cc + e;
-            const int P = ee < n_sink ? ee : lo + (ee - n_sink);
-            kpos[r] = P;
-            const bool from_mem = e < nk && !(APPEND && P == p);
-            const uint16_t *row = ee < n_sink ? a.k_sink + sink_base + (int64_t)P * D
-                                              : a.k_ring + ring_base + (int64_t)ring_slot(P) * D;
-#pragma unroll
-            for (int u = 0; u < L::QE / 8; ++u)
-                kx[r][u] = from_mem ? ld16(row + qq * L::QE + 8 * u) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto load_v = [&](int cc) {
-        const int nk = n_keys - cc < DEC_KC ? n_keys - cc : DEC_KC;
-#pragma unroll
-        for (int r = 0; r < L::VK; ++r) {
-            const int e = kg + L::KG * r, ee = cc + e;
-            const int P = ee < n_sink ? ee : lo + (ee - n_sink);
-            vpos[r] = P;
-            const bool from_mem = e < nk && !(APPEND && P == p);
-            const uint16_t *row = ee < n_sink ? a.v_sink + sink_base + (int64_t)P * D
-                                              : a.v_ring + ring_base + (int64_t)ring_slot(P) * D;
-            vx[r] = from_mem ? ld16(row + 8 * c8) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    if (k_begin < n_keys) {
-        load_k(k_begin);
-        load_v(k_begin);
-    }
-    for (int c0 = k_begin; c0 < n_keys; c0 += DEC_KC) {
-        const int nk = n_keys - c0 < DEC_KC ? n_keys - c0 : DEC_KC;
-        const bool more = c0 + DEC_KC < n_keys;
-        // -- scores (base 2): q.k * scale log2e + slope log2e (p - P)
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int slot = tid + 256 * r, e = slot / 4, qq = slot % 4;
-            const int P = kpos[r];
-            float kf[L::QE];
-#pragma unroll
-            for (int u = 0; u < L::QE / 8; ++u) {
-                const uint32_t w4[4] = {kx[r][u].x, kx[r][u].y, kx[r][u].z, kx[r][u].w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    kf[8 * u + 2 * m] = __uint_as_float(w4[m] << 16);
-                    kf[8 * u + 2 * m + 1] = __uint_as_float(w4[m] & 0xffff0000u);
-                }
-            }
-            if (APPEND && P == p && e < nk) {
-#pragma unroll
-                for (int c = 0; c < L::QE; ++c) kf[c] = kn[qq * L::QE + c];
-            }
-            float part[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float acc_d = 0.0f;
-#pragma unroll
-                for (int c = 0; c < L::QE; ++c) acc_d = fmaf(qs[g * L::QG + qq * L::QQ + c], kf[c], acc_d);
-                part[g] = acc_d;
-            }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                part[g] += __shfl_xor(part[g], 1, 64);
-                part[g] += __shfl_xor(part[g], 2, 64);
-            }
-            if (qq == 0 && e < nk) {
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float slope = a.slopes ? a.slopes[hk * G + g] * 1.4426950408889634f : 0.0f;
-                    sc[g * DEC_KC + e] = fmaf(slope, (float)(p - P), part[g]);
-                }
-            }
-        }
-        if (more) load_k(c0 + DEC_KC);
-        lds_sync();
-        // -- weights: one wavefront per head, keys across lanes
-        for (int g = wave; g < G; g += 4) {
-            float x0 = lane < nk ? sc[g * DEC_KC + lane] : -INFINITY;
-            float x1 = lane + 64 < nk ? sc[g * DEC_KC + lane + 64] : -INFINITY;
-            if (a.mode == 0) {
-                x0 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x0));
-                x1 = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x1));
-            } else {
-                const float m_old = ml[g];
-                const float m_new = fmaxf(m_old, wave_max(fmaxf(x0, x1)));
-                x0 = __builtin_amdgcn_exp2f(x0 - m_new);
-                x1 = __builtin_amdgcn_exp2f(x1 - m_new);
-                const float sum = wave_sum(x0 + x1);
-                if (lane == 0) {
-                    const float corr = __builtin_amdgcn_exp2f(m_old - m_new);
-                    ml[8 + g] = ml[8 + g] * corr + sum;
-                    ml[16 + g] = corr;
-                    ml[g] = m_new;
-                }
-            }
-            if (lane < nk) sc[g * DEC_KC + lane] = x0;
-            if (lane + 64 < nk) sc[g * DEC_KC + lane + 64] = x1;
-        }
-        lds_sync();
-        // -- values: acc[g][c] = acc * corr + sum_e w[g][e] v[e][8 c8 + c]
-        if (a.mode == 1) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float corr = ml[16 + g];
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc[g][c] *= corr;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < L::VK; ++r) {
-            const int e = kg + L::KG * r;
-            if (e < nk) {
-                float vf[8];
-                const uint32_t w4[4] = {vx[r].x, vx[r].y, vx[r].z, vx[r].w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    vf[2 * m] = __uint_as_float(w4[m] << 16);
-                    vf[2 * m + 1] = __uint_as_float(w4[m] & 0xffff0000u);
-                }
-                if (APPEND && vpos[r] == p) {
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) vf[c] = vn[8 * c8 + c];
-                }
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const float wgt = sc[g * DEC_KC + e];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(wgt, vf[c], acc[g][c]);
-                }
-            }
-        }
-        if (more) load_v(c0 + DEC_KC);
-        lds_sync();
-    }
-    // ---- sum the key groups and normalise
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) red[(kg * G + g) * D + 8 * c8 + c] = acc[g][c];
-    __syncthreads();
-    float *pp = a.nsplit > 1 ? a.part + (((int64_t)bsh * a.nsplit + split) * G) * (D + 2) : nullptr;
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int g = idx / D, col = idx % D;
-        float sum = 0.0f;
-        for (int r = 0; r < L::KG; ++r) sum += red[(r * G + g) * D + col];
-        if (a.nsplit > 1) {
-            pp[g * (D + 2) + col] = sum;
-        } else {
-            if (a.mode == 1) sum /= ml[8 + g];
-            Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + g) * D + col, sum);
-        }
-    }
-    if (a.nsplit > 1 && tid < G) {
-        pp[tid * (D + 2) + D] = ml[tid];          // running maximum (base 2), -inf if empty
-        pp[tid * (D + 2) + D + 1] = ml[8 + tid];  // running sum
-    }
-}
-
-// Merge of the split partials of decode_fast_kernel: one block per (sequence, kv head).
+// Merge of the split partials of decode_mfma_kernel: one block per (sequence, kv head).
 // softmax: o = sum_k acc_k 2^(m_k - M) / sum_k l_k 2^(m_k - M) with M the largest m_k;
 // sigmoid: o = sum_k acc_k. A query whose position cannot be served gets NaN.
 template <int D, int G, int OUT>
@@ -829,25 +534,455 @@ __global__ __launch_bounds__(NT) void decode_window_kernel(DecodeFast a, const u
     }
 }
 
+// Matrix-core decode for long windows (bf16 cache, d in {64, 128}). One block of four
+// wavefronts per (sequence, kv head, key range), with the key ranges of the split scheme
+// above; each wavefront walks its own 32-key tiles of the range (tiles wave, wave + 4, ...)
+// with no block barrier inside the walk, and the four partial results are merged at the end.
+//   scores  S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K rows are the A operand exactly
+//           as stored, loaded from memory straight into registers. Column n of the B operand
+//           holds, for n < G, the bf16 part hi of query head n (rotated, times scale log2 e)
+//           and, for G <= n < 2G, the bf16 remainder lo of head n - G, so that hi + lo keeps
+//           about 16 bits of the query; a lane exchange adds the two columns, after which both
+//           lanes of a head hold its full base-2 logit.
+//   weights ALiBi, the end-of-range cut and the running maximum (lazy rescale, as in the
+//           prefill kernels) on the vector unit.
+//   values  O^T += V^T P^T: V rows go buffer -> LDS (two tiles per wavefront, 16-byte chunks
+//           XOR-swizzled by row) and come back through transposing LDS reads; the weights
+//           enter as bf16 hi / lo columns again, so both products are exact up to float32
+//           accumulation.
+// Sink keys and window keys form separate tiles, so that each tile reads a single store.
+template <int D>
+struct DecM {
+    static constexpr int KS = D / 16;              // k-steps of the score product
+    static constexpr int DB = D / 32;              // 32-row blocks of O^T
+    static constexpr int C = D / 8;                // 16-byte chunks per row
+    static constexpr int TE = 32 * D;              // bf16 elements of one V tile
+    static constexpr int ROUNDS = TE * 2 / 1024;   // 1 KB transfers per tile and wavefront
+};
+
+// Chunk c of V tile row r sits at chunk c ^ dec_vswz(r), which spreads the transposing reads
+// over all banks.
+template <int D>
+__device__ __forceinline__ constexpr int dec_vswz(int r) {
+    return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
+}
+
+// V tiles (4 wavefronts x 2 x 32 rows x d bf16), reused by the merge for 4 x 2G x d floats;
+// then the appended key and value (d bf16 each), 4 x 8 x 2 floats of running state and the
+// query operand (d / 16 k-steps x 64 lanes x 16 bytes).
+__host__ __device__ constexpr size_t decode_mfma_vbytes(int d, int G) {
+    return (size_t)4 * 2 * 32 * d * 2 > (size_t)4 * 2 * G * d * 4 ? (size_t)4 * 2 * 32 * d * 2
+                                                                   : (size_t)4 * 2 * G * d * 4;
+}
+size_t decode_mfma_lds(int d, int G) {
+    return decode_mfma_vbytes(d, G) + (size_t)4 * d + 4 * 8 * 2 * 4 + (size_t)d / 16 * 64 * 16;
+}
+
+// Buffer offsets are 32-bit: each (sequence, kv head) slice of the ring and of the sink
+// store stays below 2 GB.
+bool decode_mfma_fits(int64_t w, int64_t s, int d) {
+    return w * d * 2 < ((int64_t)1 << 31) && s * d * 2 < ((int64_t)1 << 31);
+}
+
+constexpr uint32_t DEC_OOB = 0x80000000u;  // past every store: buffer reads return zero
+
+// One 32-key tile of a query's key list: sink tiles first, then window tiles.
+struct DecTile {
+    bool sink;  // rows come from the sink store
+    int base;   // sink index / window offset of row 0
+    int lim;    // rows below lim hold keys
+    int u0;     // p - (position of row 0)
+};
+
+struct DecCtx {
+    __amdgpu_buffer_rsrc_t rk_ring, rv_ring, rk_sink, rv_sink;
+    uint32_t row_bytes;
+    int w, slot_lo, n_sink, n_win, n_st, p;
+    int t_end;          // tiles at or past t_end are empty (no rows, no transfers)
+    int lane, col, half;
+    bool qcol, lo_part;
+    float slope_l2;
+
+    __device__ __forceinline__ DecTile tile(int tt) const {
+        DecTile t;
+        t.sink = tt < n_st;
+        t.base = t.sink ? 32 * tt : 32 * (tt - n_st);
+        t.lim = tt < t_end ? (t.sink ? n_sink : n_win) - t.base : 0;
+        t.u0 = t.sink ? p - t.base : n_win - 1 - t.base;
+        return t;
+    }
+    // byte offset of tile row r in its store (DEC_OOB past the key list)
+    __device__ __forceinline__ uint32_t row_off(const DecTile &t, int r) const {
+        int slot = t.base + r;
+        if (!t.sink) {
+            slot += slot_lo;
+            if (slot >= w) slot -= w;
+        }
+        return r < t.lim ? (uint32_t)slot * row_bytes : DEC_OOB;
+    }
+};
+
+// V tile rows -> LDS: round i moves slots 64 i .. 64 i + 63 (slot = row * C + stored chunk
+// position), lane l the slot 64 i + l.
+template <int D>
+__device__ __forceinline__ void dec_load_v(const DecCtx &cx, uint16_t *dst, const DecTile &t) {
+    using M = DecM<D>;
+    const __amdgpu_buffer_rsrc_t r = t.sink ? cx.rv_sink : cx.rv_ring;
+#pragma unroll
+    for (int i = 0; i < M::ROUNDS; ++i) {
+        const int slot = 64 * i + cx.lane, row = slot / M::C;
+        const int c = (slot % M::C) ^ dec_vswz<D>(row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(dst + 512 * i), 16,
+                                                 cx.row_off(t, row) + 16 * c, 0, 0, 0);
+    }
+}
+// K tile as the A operand: lane l holds row l % 32, chunk 2 ks + l / 32 for k-step ks.
+template <int D>
+__device__ __forceinline__ void dec_load_k(const DecCtx &cx, bf16x8_t (&kr)[D / 16], const DecTile &t) {
+    const __amdgpu_buffer_rsrc_t r = t.sink ? cx.rk_sink : cx.rk_ring;
+    const uint32_t o0 = cx.row_off(t, cx.col) + 16 * cx.half;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        kr[ks] = __builtin_bit_cast(bf16x8_t, buf_load16(r, o0 + 32 * ks));
+}
+
+// Wait until only the KS + ROUNDS transfers this step started are outstanding, whatever
+// order they were issued in: the current tile's V rows have landed. The memory clobber
+// keeps the LDS reads below the wait.
+template <int D>
+__device__ __forceinline__ void wait_own_tile() {
+    using M = DecM<D>;
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(M::KS + M::ROUNDS) : "memory");
+}
+
+// One tile of a wavefront's walk: start the transfers of the next tile (V into v_fill, K into
+// k_next; past the range they are out-of-range reads that move nothing, so every step issues
+// the same count), then scores, weights and the value product of this tile (K in k_cur, V in
+// v_cur). The two V buffers are distinct restrict pointers, so that reads of v_cur do not
+// wait for the transfer into v_fill.
+template <int D, int G, bool APPEND>
+__device__ __forceinline__ void dec_step(const DecCtx &cx, uint16_t *__restrict__ v_cur,
+                                         uint16_t *__restrict__ v_fill, bf16x8_t (&k_cur)[D / 16],
+                                         bf16x8_t (&k_next)[D / 16], const uint4 *qop,
+                                         f32x16_t (&oacc)[D / 32], float &m_run, float &l_run,
+                                         int mode, int tt, int t_new,
+                                         const uint32_t *knew, const uint32_t *vnew) {
+    using M = DecM<D>;
+    const DecTile t = cx.tile(tt);
+    // the previous step's reads of v_fill are complete before its refill starts
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    {
+        const DecTile tn = cx.tile(tt + 4);
+        dec_load_v<D>(cx, v_fill, tn);
+        dec_load_k<D>(cx, k_next, tn);
+    }
+    // the appended token replaces what its ring slot held before this launch
+    const bool has_new = APPEND && tt == t_new;
+    const int r_new = cx.n_win - 1 - t.base;
+    if (has_new && cx.col == r_new) {
+#pragma unroll
+        for (int ks = 0; ks < M::KS; ++ks) {
+            const uint32_t *kp = knew + 4 * (2 * ks + cx.half);
+            k_cur[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(kp[0], kp[1], kp[2], kp[3]));
+        }
+    }
+    f32x16_t s = {};
+#pragma unroll
+    for (int ks = 0; ks < M::KS; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_cur[ks], __builtin_bit_cast(bf16x8_t, qop[64 * ks + cx.lane]),
+                                                    s, 0, 0, 0);
+    // hi + lo columns, then ALiBi and the cut: element e is row 8 (e / 4) + 4 half + e % 4
+    const int partner = cx.lo_part ? cx.lane - G : cx.lane + G;
+    const float u0 = (float)(t.u0 - 4 * cx.half);
+    const int lim = t.lim - 4 * cx.half;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int kr = 8 * (e >> 2) + (e & 3);
+        const float full = s[e] + __shfl(s[e], partner, 64);
+        s[e] = kr < lim ? fmaf(cx.slope_l2, u0 - (float)kr, full) : -INFINITY;
+    }
+    if (mode == 0) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            s[e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-s[e]));
+    } else {
+        float mt = s[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float m_new = fmaxf(m_run, mt);
+        // keep a stale maximum while the new one exceeds it by less than 8 (weights stay
+        // below 2^8); the merge uses the same maximum
+        const bool need = m_new > m_run + 8.0f;
+        if (__any(need)) {
+            const float corr = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+            for (int db = 0; db < M::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+            l_run *= corr;
+            m_run = need ? m_new : m_run;
+        }
+        float ls = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            s[e] = __builtin_amdgcn_exp2f(s[e] - m_run);
+            ls += s[e];
+        }
+        l_run += ls;
+    }
+    // P^T operand of step j (keys 16 j + 4 half + {0..3, 8..11}): elements 8 j .. 8 j + 7,
+    // as bf16 hi (columns < G) or lo (columns G .. 2G - 1)
+    uint4 pk[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        float x[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float v = s[8 * j + m];
+            const float hi = bf16_bits_to_f32(f32_to_bf16_bits(v));
+            x[m] = cx.lo_part ? v - hi : v;
+        }
+        const uint4 pp = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                    pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+        pk[j] = cx.qcol ? pp : make_uint4(0, 0, 0, 0);
+    }
+    wait_own_tile<D>();
+    if (has_new) {
+        // the tile's own transfer has landed: the new value over its row
+        if (cx.lane < M::C) {
+            const int pos = (r_new * M::C + (cx.lane ^ dec_vswz<D>(r_new))) * 8;
+            const uint32_t *vp = vnew + 4 * cx.lane;
+            *reinterpret_cast<uint4 *>(v_cur + pos) = make_uint4(vp[0], vp[1], vp[2], vp[3]);
+        }
+    }
+    // transposing read: lane (G4, rr, a) supplies row 4 (G4 / 2) + rr and column group
+    // 16 (G4 % 2) + 4 a of the 8 x 32 block one read covers
+    const int G4 = cx.lane >> 4, rr = (cx.lane >> 2) & 3, a = cx.lane & 3;
+    const int row_l = 4 * (G4 >> 1) + rr, cb = 2 * (G4 & 1) + (a >> 1);
+    const int fq = dec_vswz<D>(rr) >> 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int db = 0; db < M::DB; ++db) {
+            const int vo = row_l * D + (4 * (db ^ fq) + cb) * 8 + 4 * (a & 1);
+            const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(v_cur + 16 * j * D + vo));
+            const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(v_cur + (16 * j + 8) * D + vo));
+            const s16x8_t a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8),
+                                                               __builtin_bit_cast(bf16x8_t, pk[j]),
+                                                               oacc[db], 0, 0, 0);
+        }
+}
+
+// Two wavefronts per SIMD: two blocks per CU keep 16 tiles of transfers in flight.
+template <int D, int G, int OUT, bool APPEND>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeFast a, const uint16_t *__restrict__ q,
+                                                          const int32_t *__restrict__ q_pos,
+                                                          void *__restrict__ o,
+                                                          const uint16_t *__restrict__ k_new,
+                                                          const uint16_t *__restrict__ v_new) {
+    using M = DecM<D>;
+    extern __shared__ uint4 dlds4[];
+    uint16_t *lds = reinterpret_cast<uint16_t *>(dlds4);
+    const size_t vbytes = decode_mfma_vbytes(D, G);
+    uint32_t *knew = reinterpret_cast<uint32_t *>(lds + vbytes / 2);   // [D / 2] bf16 pairs
+    uint32_t *vnew = knew + D / 2;
+    float *mls = reinterpret_cast<float *>(vnew + D / 2);               // [4][G][2]
+    uint4 *qop = reinterpret_cast<uint4 *>(mls + 4 * 8 * 2);            // [D / 16][64]
+
+    const int split = blockIdx.x % a.nsplit, bsh = blockIdx.x / a.nsplit;
+    const int sq = bsh / a.Hkv, hk = bsh % a.Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int p = q_pos[sq];
+    const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
+    if (!valid) {
+        // the combine kernel flags split outputs itself
+        if (a.nsplit == 1)
+            for (int idx = tid; idx < G * D; idx += 256)
+                Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G) * D + idx, qnan());
+        return;
+    }
+    // the key list: n_sink sinks, then window positions lo .. p; its tiles, and this block's
+    // range of them
+    const int lo = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
+    const int n_sink = a.s < lo ? a.s : lo, n_win = p - lo + 1;
+    const int n_st = (n_sink + 31) / 32, n_t = n_st + (n_win + 31) / 32;
+    const int per = (n_t + a.nsplit - 1) / a.nsplit;
+    const int t_begin = split * per < n_t ? split * per : n_t;
+    const int t_end = t_begin + per < n_t ? t_begin + per : n_t;
+    const bool owns_new = t_begin <= n_t - 1 && n_t - 1 < t_end;   // the query's own key
+    const int64_t ring_base = ((int64_t)sq * a.Hkv + hk) * a.w * D;
+    const int64_t sink_base = ((int64_t)sq * a.Hkv + hk) * a.s * D;
+    const int half_d = D / 2;
+
+    // ---- the new token (fused append): ring slot and sink entry, and a copy in LDS
+    if (APPEND && owns_new && tid < half_d) {
+        const int64_t src = ((int64_t)sq * a.Hkv + hk) * D + 2 * tid;
+        float k0 = bf16_bits_to_f32(k_new[src]), k1 = bf16_bits_to_f32(k_new[src + 1]);
+        const uint32_t vv = *reinterpret_cast<const uint32_t *>(v_new + src);
+        if (a.rope) {
+            const float2 cs = reinterpret_cast<const float2 *>(a.rope)[(int64_t)p * half_d + tid];
+            const float r0 = fmaf(-k1, cs.y, k0 * cs.x);
+            k1 = fmaf(k0, cs.y, k1 * cs.x);
+            k0 = r0;
+        }
+        const uint32_t kk = pack_bf16x2(k0, k1);
+        *reinterpret_cast<uint32_t *>(a.k_ring + ring_base + (int64_t)(p % a.w) * D + 2 * tid) = kk;
+        *reinterpret_cast<uint32_t *>(a.v_ring + ring_base + (int64_t)(p % a.w) * D + 2 * tid) = vv;
+        if (p < a.s) {
+            *reinterpret_cast<uint32_t *>(a.k_sink + sink_base + (int64_t)p * D + 2 * tid) = kk;
+            *reinterpret_cast<uint32_t *>(a.v_sink + sink_base + (int64_t)p * D + 2 * tid) = vv;
+        }
+        knew[tid] = kk;
+        vnew[tid] = vv;
+    }
+
+    DecCtx cx;
+    cx.row_bytes = 2 * D;
+    cx.rk_ring = make_rsrc(a.k_ring + ring_base, (uint32_t)(a.w * D * 2));
+    cx.rv_ring = make_rsrc(a.v_ring + ring_base, (uint32_t)(a.w * D * 2));
+    cx.rk_sink = make_rsrc(a.s > 0 ? a.k_sink + sink_base : a.k_ring, (uint32_t)(a.s * D * 2));
+    cx.rv_sink = make_rsrc(a.s > 0 ? a.v_sink + sink_base : a.v_ring, (uint32_t)(a.s * D * 2));
+    cx.w = a.w; cx.slot_lo = lo % a.w; cx.n_sink = n_sink; cx.n_win = n_win; cx.n_st = n_st;
+    cx.p = p;
+    cx.t_end = t_end;
+    cx.lane = lane; cx.col = lane & 31; cx.half = lane >> 5;
+    cx.qcol = cx.col < 2 * G; cx.lo_part = cx.col >= G;
+    const int g = cx.col & (G - 1);
+    cx.slope_l2 = a.slopes ? a.slopes[hk * G + g] * 1.4426950408889634f : 0.0f;
+
+    // ---- this wavefront's tiles, padded to an even count with an empty tile; the first
+    // transfers are in flight while the query is formed
+    const int first = t_begin + wave;
+    const int n_my = first < t_end ? (t_end - first + 3) / 4 : 0;
+    const int n_pad = (n_my + 1) & ~1;
+    uint16_t *vb0 = lds + wave * 2 * M::TE, *vb1 = vb0 + M::TE;
+    bf16x8_t ka[M::KS], kb[M::KS];
+    {
+        const DecTile t0 = cx.tile(first);   // empty past the range
+        dec_load_v<D>(cx, vb0, t0);
+        dec_load_k<D>(cx, ka, t0);
+    }
+
+    // ---- B operand of the score product, kept in LDS for the four wavefronts: column
+    // n = lane % 32, k-slice 8 (lane / 32) of each k-step; rotated at p, times scale log2(e),
+    // split into bf16 hi / lo. Wavefront wave forms k-steps wave, wave + 4, ...
+    {
+        constexpr int KW = (M::KS + 3) / 4;   // k-steps per wavefront
+        const uint16_t *qrow = q + ((int64_t)sq * a.Hq + hk * G + g) * D;
+        const float4 *trow = a.rope ? reinterpret_cast<const float4 *>(a.rope + (int64_t)p * D) : nullptr;
+        uint4 xq[KW];
+        float4 t0[KW], t1[KW];
+#pragma unroll
+        for (int u = 0; u < KW; ++u) {
+            const int ks = wave + 4 * u;
+            if (ks < M::KS) {
+                xq[u] = ldg16(qrow + 16 * ks + 8 * cx.half);
+                if (trow) {
+                    t0[u] = trow[4 * ks + 2 * cx.half];
+                    t1[u] = trow[4 * ks + 2 * cx.half + 1];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < KW; ++u) {
+            const int ks = wave + 4 * u;
+            if (ks >= M::KS) continue;
+            const uint32_t wq[4] = {xq[u].x, xq[u].y, xq[u].z, xq[u].w};
+            float x[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                x[2 * m] = bf16_bits_to_f32(wq[m] & 0xffffu);
+                x[2 * m + 1] = bf16_bits_to_f32(wq[m] >> 16);
+            }
+            if (trow) rotate8(x, t0[u], t1[u]);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float v = x[m] * a.cs;
+                const float hi = bf16_bits_to_f32(f32_to_bf16_bits(v));
+                x[m] = cx.lo_part ? v - hi : v;
+            }
+            const uint4 pq = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                        pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+            qop[64 * ks + lane] = cx.qcol ? pq : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    f32x16_t oacc[M::DB];
+#pragma unroll
+    for (int db = 0; db < M::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.0f;
+    float m_run = -1e30f, l_run = 0.0f;
+    const int t_new = APPEND && owns_new ? n_t - 1 : -1;
+    lds_sync();   // the query operand and the appended token (tile transfers stay in flight)
+
+    for (int i = 0; i < n_pad; i += 2) {
+        dec_step<D, G, APPEND>(cx, vb0, vb1, ka, kb, qop, oacc, m_run, l_run, a.mode,
+                               first + 4 * i, t_new, knew, vnew);
+        dec_step<D, G, APPEND>(cx, vb1, vb0, kb, ka, qop, oacc, m_run, l_run, a.mode,
+                               first + 4 * (i + 1), t_new, knew, vnew);
+    }
+
+    // ---- merge the four wavefronts: per head g, columns g (hi) and g + G (lo)
+    l_run += __shfl_xor(l_run, 32, 64);   // lanes l and l + 32 saw different keys
+    __syncthreads();                      // every V tile has been read
+    float *red = reinterpret_cast<float *>(lds);   // [4][2G][D]
+    if (cx.qcol) {
+#pragma unroll
+        for (int db = 0; db < M::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                red[(wave * 2 * G + cx.col) * D + 32 * db + 8 * (e >> 2) + 4 * cx.half + (e & 3)] = oacc[db][e];
+    }
+    if (cx.col < G && cx.half == 0) {
+        mls[(wave * G + cx.col) * 2] = m_run;
+        mls[(wave * G + cx.col) * 2 + 1] = l_run;
+    }
+    __syncthreads();
+    float *pp = a.nsplit > 1 ? a.part + (((int64_t)bsh * a.nsplit + split) * G) * (D + 2) : nullptr;
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int hg = idx / D, c = idx % D;
+        float mx = mls[hg * 2];
+#pragma unroll
+        for (int wv = 1; wv < 4; ++wv) mx = fmaxf(mx, mls[(wv * G + hg) * 2]);
+        float sum = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) {
+            const float f = a.mode == 1 ? __builtin_amdgcn_exp2f(mls[(wv * G + hg) * 2] - mx) : 1.0f;
+            sum = fmaf(red[(wv * 2 * G + hg) * D + c] + red[(wv * 2 * G + G + hg) * D + c], f, sum);
+            den = fmaf(mls[(wv * G + hg) * 2 + 1], f, den);
+        }
+        if (a.nsplit > 1) {
+            pp[hg * (D + 2) + c] = sum;
+            if (c == 0) {
+                pp[hg * (D + 2) + D] = mx;        // running maximum (base 2)
+                pp[hg * (D + 2) + D + 1] = den;   // running sum
+            }
+        } else {
+            if (a.mode == 1) sum /= den;
+            Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hk * G + hg) * D + c, sum);
+        }
+    }
+}
+
 template <int D, int G, int OUT, bool APPEND>
 hipError_t launch_fast_t(const DecodeFast &f, const void *q, const int32_t *q_pos, void *o,
                          const void *k_new, const void *v_new, hipStream_t st) {
-    if (f.w + f.s <= 128 && G <= 4) {
-        hipLaunchKernelGGL((decode_window_kernel<D, G, OUT, APPEND, 512>), dim3((unsigned)(f.S * f.Hkv)),
-                           dim3(512), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
-                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
-        return hipGetLastError();
-    }
     if (f.w + f.s <= 128) {
-        hipLaunchKernelGGL((decode_window_kernel<D, G, OUT, APPEND, 256>), dim3((unsigned)(f.S * f.Hkv)),
-                           dim3(256), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
-                           static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
-        return hipGetLastError();
+        if constexpr (G <= 4) {
+            hipLaunchKernelGGL((decode_window_kernel<D, G, OUT, APPEND, 512>), dim3((unsigned)(f.S * f.Hkv)),
+                               dim3(512), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
+                               static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
+            return hipGetLastError();
+        }
+        return hipErrorNotSupported;   // decode_fast_ok sends G = 8 to the general kernel
     }
-    const size_t lds = decode_fast_lds<D>(G);
-    hipLaunchKernelGGL((decode_fast_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv * f.nsplit)),
-                       dim3(256), lds, st, f, static_cast<const uint16_t *>(q), q_pos, o,
-                       static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, OUT, APPEND>), dim3((unsigned)(f.S * f.Hkv * f.nsplit)),
+                       dim3(256), decode_mfma_lds(D, G), st, f, static_cast<const uint16_t *>(q),
+                       q_pos, o, static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
     if (f.nsplit > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -882,8 +1017,8 @@ bool decode_fast_ok(const DecodeArgs &a, const CacheArgs &c) {
     const int64_t G = a.Hq / c.Hkv;
     if (c.dt != 1 || (c.d != 64 && c.d != 128) || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
     if (c.S * c.Hkv * 64 > 0x7fffffff || c.w > (1 << 30) || c.s > (1 << 30)) return false;
-    const size_t lds = c.d == 64 ? decode_fast_lds<64>((int)G) : decode_fast_lds<128>((int)G);
-    return lds <= 64 * 1024;
+    // whole-window kernel up to four query heads per kv head; matrix-core kernel beyond
+    return c.w + c.s <= 128 ? G <= 4 : decode_mfma_fits(c.w, c.s, (int)c.d);
 }
 
 // Key ranges per (sequence, kv head) for the chunked decode: about two blocks per CU in
