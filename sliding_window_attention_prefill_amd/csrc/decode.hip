@@ -302,14 +302,19 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeFast a,
             out = 0.0f;
             for (int k = 0; k < a.nsplit; ++k) out += pp[(k * G + g) * (D + 2) + col];
         } else {
-            float M = -INFINITY;
-            for (int k = 0; k < a.nsplit; ++k) M = fmaxf(M, pp[(k * G + g) * (D + 2) + D]);
-            float num = 0.0f, den = 0.0f;
+            // one pass, online: the loads of every range are independent of the running
+            // maximum, so they are all in flight together
+            float M = -INFINITY, num = 0.0f, den = 0.0f;
+#pragma unroll 8
             for (int k = 0; k < a.nsplit; ++k) {
                 const float *e = pp + (k * G + g) * (D + 2);
-                const float f = __builtin_amdgcn_exp2f(e[D] - M);  // empty range: 2^-inf = 0
-                num = fmaf(e[col], f, num);
-                den = fmaf(e[D + 1], f, den);
+                const float m = e[D], x = e[col], l = e[D + 1];
+                const float M2 = fmaxf(M, m);
+                const float fo = __builtin_amdgcn_exp2f(M - M2);   // 2^-inf = 0 at the start
+                const float fn = __builtin_amdgcn_exp2f(m - M2);
+                num = fmaf(num, fo, x * fn);
+                den = fmaf(den, fo, l * fn);
+                M = M2;
             }
             out = num / den;
         }
