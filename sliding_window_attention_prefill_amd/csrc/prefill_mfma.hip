@@ -141,8 +141,10 @@ struct PackParams {
 };
 
 // ---------------------------------------------------------------------------------------
-// Pre-pass: every 64-key tile, once, into its LDS image. One block per (batch, tile, group of
-// up to four kv heads): the rotation angles of a position are read once for the group.
+// Pre-pass: every 64-key tile, once, into its LDS image. One block per (batch, tile, part of
+// the tile, group of up to four kv heads), each thread one 16-byte chunk per head: the
+// rotation angles of a position are read once for the group, and the grid holds several
+// rounds of blocks, so that the loads of later blocks overlap the stores of earlier ones.
 // K image: rotated (or converted) float16; V image (PACK_V): converted float16. Rows past
 // the sequence end are zero.
 constexpr int PACK_HG = 4;  // kv heads per pre-pass block
@@ -153,12 +155,14 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
     const int n_hg = (int)((p.Hkv + PACK_HG - 1) / PACK_HG);
     const int bid = blockIdx.x, tid = threadIdx.x;
     const int hg = bid % n_hg;
-    const int rest = bid / n_hg;
+    const int rest0 = bid / n_hg;
+    const int pt = rest0 % T::KPT;           // this block's chunks: 256 pt .. 256 pt + 255
+    const int rest = rest0 / T::KPT;
     const int jt = rest % p.n_ktiles;
     const int64_t b = rest / p.n_ktiles;
     const int64_t h0 = (int64_t)hg * PACK_HG;
     const int nh = p.Hkv - h0 < PACK_HG ? (int)(p.Hkv - h0) : PACK_HG;
-    constexpr int R = T::KPT;
+    constexpr int R = 1;
     if constexpr (!PACK_V) {
         // keys only: every load of the block is issued before the first store (the images
         // may not be assumed disjoint from the inputs, so a store would order later loads
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
         float4 t0[R], t1[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+            const int cidx = tid + 256 * (r + pt), row = cidx / T::C, c = cidx % T::C;
             const int64_t j = (int64_t)jt * BK + row;
             const bool in = j < p.N;
             t0[r] = make_float4(1.f, 0.f, 1.f, 0.f);
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+            const int cidx = tid + 256 * (r + pt), row = cidx / T::C, c = cidx % T::C;
             const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
 #pragma unroll
             for (int u = 0; u < PACK_HG; ++u) {
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
     } else {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int cidx = tid + 256 * r, row = cidx / T::C, c = cidx % T::C;
+            const int cidx = tid + 256 * (r + pt), row = cidx / T::C, c = cidx % T::C;
             const int64_t j = (int64_t)jt * BK + row;
             const bool in = j < p.N;
             float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
@@ -896,8 +900,10 @@ hipError_t launch_gp(const MfmaParams &mp, int nb, int mode, bool alibi, hipStre
     return launch_main<D, GP, 0, false>(mp, nb, alibi, st);
 }
 
+// nblocks: (batch, tile, kv-head group) triples; each gets KPT blocks.
 template <int D>
 hipError_t launch_pack(const PackParams &pp, int nblocks, bool rot, bool pack_v, hipStream_t st) {
+    nblocks *= Tile<D>::KPT;
     if (rot) {
         if (pack_v) hipLaunchKernelGGL((prefill_pack_kernel<D, true, true>), dim3((unsigned)nblocks), dim3(256), 0, st, pp);
         else hipLaunchKernelGGL((prefill_pack_kernel<D, true, false>), dim3((unsigned)nblocks), dim3(256), 0, st, pp);
@@ -940,7 +946,9 @@ bool prefill_mfma_supported(const PrefillArgs &a) {
     const int64_t slice = (a.N * a.Hkv) * a.d * 2;
     const int64_t img_slice = n_kt * BK * a.d * 2;
     const int64_t table = a.rope ? a.rope_rows * a.d * 4 : 0;
-    return nb <= 0x7fffffff && a.B * a.Hkv * n_kt <= 0x7fffffff && slice < (int64_t(1) << 31) &&
+    const int64_t pack_blocks = a.B * n_kt * ((a.Hkv + PACK_HG - 1) / PACK_HG) * Tile<128>::KPT;
+    return nb <= 0x7fffffff && a.B * a.Hkv * n_kt <= 0x7fffffff && pack_blocks <= 0x7fffffff &&
+           slice < (int64_t(1) << 31) &&
            img_slice < (int64_t(1) << 31) && table < (int64_t(1) << 31) && a.N < (int64_t(1) << 24) &&
            a.Hq * a.d * 32 < (int64_t(1) << 31);
 }
