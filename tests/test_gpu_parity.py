@@ -329,7 +329,8 @@ def test_decode_c4_full_workload():
 @pytest.mark.parametrize("mode", [wl.SIGMOID, wl.SOFTMAX])
 @pytest.mark.parametrize("S,Hq,Hkv,d,w,s", [(5, 8, 2, 128, 16, 3), (3, 4, 4, 64, 7, 0),
                                              (4, 32, 8, 128, 64, 4), (3, 16, 2, 128, 200, 2),
-                                             (2, 2, 1, 96, 33, 40), (3, 8, 1, 64, 20, 1)])
+                                             (2, 2, 1, 96, 33, 40), (3, 8, 1, 64, 20, 1),
+                                             (4, 8, 1, 64, 150, 40), (3, 4, 2, 128, 100, 70)])
 def test_fused_append_decode_matches_oracle(mode, S, Hq, Hkv, d, w, s):
     """swa_decode_append (one launch: append the step's token, then answer its query) equals
     the oracle ring step by step, and leaves the same cache contents as the oracle."""

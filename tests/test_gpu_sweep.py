@@ -127,7 +127,9 @@ def test_fused_decode_random_shapes(case):
 @pytest.mark.parametrize("S,Hq,Hkv,d,w,s,mode", [
     (1, 8, 2, 128, 3000, 0, wl.SOFTMAX), (2, 4, 4, 64, 2500, 4, wl.SIGMOID),
     (1, 32, 8, 128, 4096, 0, wl.SOFTMAX), (3, 2, 1, 64, 1100, 7, wl.SOFTMAX),
-    (1, 8, 2, 128, 5000, 0, wl.SIGMOID), (2, 8, 8, 128, 1400, 3, wl.SOFTMAX)])
+    (1, 8, 2, 128, 5000, 0, wl.SIGMOID), (2, 8, 8, 128, 1400, 3, wl.SOFTMAX),
+    # several sink tiles ahead of the window tiles, eight query heads per kv head
+    (2, 8, 1, 64, 1500, 70, wl.SOFTMAX), (2, 16, 2, 128, 1200, 45, wl.SIGMOID)])
 @pytest.mark.parametrize("fused", [False, True], ids=["decode", "fused"])
 def test_split_kv_decode_long_windows(S, Hq, Hkv, d, w, s, mode, fused):
     """Long windows with few sequences run split over several blocks per (sequence, kv
