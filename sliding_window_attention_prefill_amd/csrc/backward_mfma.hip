@@ -148,22 +148,25 @@ struct PackQ {
     float qs;          // factor on the query image: -scale log2(e) for sigmoid, else 1
 };
 
-// One block per (batch, 64-position tile, up to four query heads): rotated queries and the
-// output gradient as float16 images; for softmax the row statistics (rows past N get an
-// infinite log-normaliser, so their weights vanish).
+// One block per (batch, 64-position tile, part of the tile, up to four query heads), each
+// thread one 16-byte chunk per head: rotated queries and the output gradient as float16
+// images; for softmax the row statistics (rows past N get an infinite log-normaliser, so
+// their weights vanish). Tile parts give the grid several rounds of blocks, whose loads and
+// stores overlap.
 template <int D, bool ROT, int OUT, int MODE>
 __global__ __launch_bounds__(256) void bwd_pack_q_kernel(PackQ p) {
     using T = BT<D>;
     const int n_hg = (int)((p.Hq + 3) / 4);
     const int hg = blockIdx.x % n_hg;
-    const int rest = blockIdx.x / n_hg;
+    const int rest0 = blockIdx.x / n_hg;
+    const int pt = rest0 % T::KPT;   // this block's chunks: 256 pt .. 256 pt + 255
+    const int rest = rest0 / T::KPT;
     const int it = rest % p.n_tiles;
     const int64_t b = rest / p.n_tiles;
     const int64_t h0 = (int64_t)hg * 4;
     const int nh = p.Hq - h0 < 4 ? (int)(p.Hq - h0) : 4;
-#pragma unroll
-    for (int r = 0; r < T::KPT; ++r) {
-        const int cidx = threadIdx.x + 256 * r, row = cidx / T::C, c = cidx % T::C;
+    {
+        const int cidx = threadIdx.x + 256 * pt, row = cidx / T::C, c = cidx % T::C;
         const int64_t i = (int64_t)it * BK + row;
         const bool in = i < p.N;
         float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
@@ -1053,7 +1056,7 @@ hipError_t launch_bwd_d(const PrefillArgs &a, const BwdPlan &pl, const void *q, 
         pq.qimg = qimg; pq.gimg = gimg; pq.stats = stats; pq.rope = a.rope; pq.N = a.N;
         pq.Hq = a.Hq; pq.n_tiles = nt;
         pq.qs = a.mode == 0 ? -a.scale * LOG2E : 1.0f;
-        const unsigned nb = (unsigned)(a.B * nt * ((a.Hq + 3) / 4));
+        const unsigned nb = (unsigned)(a.B * nt * ((a.Hq + 3) / 4) * BT<D>::KPT);
 #define SWA_PACKQ(R, O, M) hipLaunchKernelGGL((bwd_pack_q_kernel<D, R, O, M>), dim3(nb), dim3(256), 0, st, pq)
         if (a.mode == 1) {
             if (rot) { if (a.out_dt == 1) SWA_PACKQ(true, 1, 1); else SWA_PACKQ(true, 0, 1); }
