@@ -1026,8 +1026,8 @@ bool decode_fast_ok(const DecodeArgs &a, const CacheArgs &c) {
     return c.w + c.s <= 128 ? G <= 4 : decode_mfma_fits(c.w, c.s, (int)c.d);
 }
 
-// Key ranges per (sequence, kv head) for the chunked decode: about two blocks per CU in
-// total, and at least 512 keys per range.
+// Key ranges per (sequence, kv head) for the matrix-core decode: about two blocks per CU in
+// total (the kernel's register use allows two), and at least 512 keys per range.
 int64_t decode_nsplit(const CacheArgs &c) {
     if (c.w + c.s <= 128) return 1;            // whole-window kernel
     const int64_t bh = c.S * c.Hkv;
