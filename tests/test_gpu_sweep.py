@@ -178,3 +178,46 @@ def test_split_kv_decode_long_windows(S, Hq, Hkv, d, w, s, mode, fused):
     qn = torch.randn((S, Hq, d), generator=g).to(torch.bfloat16).to(DEV)
     out = swa.swa_decode(qn, bad, cache, mode=mode, rope_table=table, out_dtype=torch.float32)
     assert torch.isnan(out).all()
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d,w,s,mode", [
+    (2, 8, 2, 128, 2000, 3, wl.SOFTMAX), (3, 4, 1, 64, 300, 5, wl.SIGMOID)])
+def test_long_window_decode_bf16_output(S, Hq, Hkv, d, w, s, mode):
+    """Fused append + decode with bf16 outputs on windows past 128 keys (the first shape runs
+    split over several key ranges): every step against the oracle ring, rounded once to bf16
+    like the stored output."""
+    g = torch.Generator().manual_seed(17 * S + w)
+    cache = swa.SwaCache.empty(S, Hkv, w, s, d, torch.bfloat16)
+    ring = oracle.Ring(S, Hkv, w, s, d)
+    start = torch.tensor([(w // 2) if q_ % 2 == 0 else (w + 40 + 13 * q_) for q_ in range(S)])
+    theta = 1e4
+    steps = 3
+    table = swa.swa_rope_table(int(start.max()) + steps + 1, d, theta)
+    for q_ in range(S):
+        n0 = int(start[q_])
+        pos_all = torch.full((S,), -1, dtype=torch.int32)
+        pos_all[q_] = 0
+        kh = torch.randn((S, n0, Hkv, d), generator=g).to(torch.bfloat16)
+        vh = torch.randn((S, n0, Hkv, d), generator=g).to(torch.bfloat16)
+        swa.swa_kv_append(cache, kh.to(DEV), vh.to(DEV), pos_all.to(DEV), rope_table=table)
+        ring.append(kh, vh, pos_all, rope_theta=theta)
+    slopes = tuple(np.linspace(-0.3, 0.3, Hq).tolist())
+    sl = torch.tensor(slopes, dtype=torch.float32, device=DEV)
+    ws = torch.empty(max(swa.swa_decode_workspace_bytes(cache, Hq, mode=mode,
+                                                        out_dtype=torch.bfloat16), 1),
+                     dtype=torch.uint8, device=DEV)
+    for step in range(steps):
+        pos = (start + step).to(torch.int32)
+        kn = torch.randn((S, Hkv, d), generator=g).to(torch.bfloat16)
+        vn = torch.randn((S, Hkv, d), generator=g).to(torch.bfloat16)
+        qn = torch.randn((S, Hq, d), generator=g).to(torch.bfloat16)
+        out = swa.swa_decode_append(qn.to(DEV), kn.to(DEV), vn.to(DEV), pos.to(DEV), cache,
+                                    mode=mode, alibi_slopes=sl, rope_table=table,
+                                    out_dtype=torch.bfloat16, workspace=ws)
+        assert out.dtype == torch.bfloat16
+        ring.append(kn[:, None], vn[:, None], pos, rope_theta=theta)
+        ref = ring.decode(qn, pos, H_q=Hq, mode=mode, slopes=slopes, rope_theta=theta)
+        torch.cuda.synchronize()
+        ref_r = torch.from_numpy(np.asarray(ref)).to(torch.bfloat16).to(torch.float64).numpy()
+        max_rel, sum_rel = errors(out.float().cpu().double().numpy(), ref_r)
+        assert max_rel <= 2e-2 and sum_rel <= 2e-3, (step, max_rel, sum_rel)
