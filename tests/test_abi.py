@@ -162,6 +162,13 @@ def test_decode_workspace_bytes_split_kv(lib):
     assert wsb(1, 8, 4096, 0, 128, 32) == 4 * 1 * 8 * 8 * 4 * (128 + 2)
     # at most 64 ranges
     assert wsb(1, 1, 1 << 20, 0, 64, 2) == 4 * 1 * 1 * 64 * 2 * (64 + 2)
+    # eight query heads per kv head on a long window: split like the others
+    assert wsb(1, 2, 4096, 0, 128, 16) == 4 * 1 * 2 * 8 * 8 * (128 + 2)
+    # general kernel, no workspace: eight heads per kv head on a short window, and a ring
+    # slice per (sequence, kv head) of 2 GB (32-bit buffer offsets)
+    assert wsb(1, 2, 64, 4, 128, 16) == 0
+    assert wsb(1, 1, 1 << 23, 0, 128, 4) == 0
+    assert wsb(1, 1, (1 << 23) - 1, 0, 128, 4) == 4 * 1 * 1 * 64 * 4 * (128 + 2)
 
 
 def _dparams(H_q=4, mode=1, rope_table=None, rope_rows=0):
