@@ -313,7 +313,8 @@ __global__ __launch_bounds__(256) void chunk_gather_kernel(GatherParams p) {
 // ring slot (p0 + r) mod w when it is among the last w rows (a later row of the same call
 // would overwrite it), and to the sink store when p0 + r < s. Keys are rotated at their
 // position in float32 and rounded once to bf16, as the single-token append stores them.
-// One block per (sequence, 64 rows); a thread moves 8 elements of one (row, kv head).
+// Eight blocks per (sequence, 64 rows), taking interleaved runs of the tile's 16-byte chunks;
+// a thread moves 8 elements of one (row, kv head) per chunk.
 struct ChunkAppendParams {
     ChunkGeom cg;
     const uint16_t *k_new, *v_new;
@@ -321,6 +322,7 @@ struct ChunkAppendParams {
     const float *rope;
     int64_t Hkv, w_ring, s;
     int n_rtiles;                      // 64-row tiles per sequence in the grid
+    int n_parts;                       // blocks per (sequence, 64-row tile)
 };
 
 __device__ __forceinline__ uint32_t rotate_pair_bf16(uint32_t w, float c, float s) {
@@ -333,14 +335,16 @@ template <int D>
 __global__ __launch_bounds__(256) void chunk_append_kernel(ChunkAppendParams p) {
     constexpr int C = D / 8;
     constexpr int U = 4;   // elements per thread whose loads are in flight together
-    const int64_t b = blockIdx.x / p.n_rtiles;
-    const int rt = blockIdx.x % p.n_rtiles;
+    const int part = blockIdx.x % p.n_parts;
+    const int64_t b = blockIdx.x / p.n_parts / p.n_rtiles;
+    const int rt = (blockIdx.x / p.n_parts) % p.n_rtiles;
     const ChunkSeq cs = chunk_seq(p.cg, b);
     if (!cs.valid || rt * BK >= cs.n) return;
     const int rows = cs.n - rt * BK < BK ? cs.n - rt * BK : BK;
     const int64_t per_row = p.Hkv * C;
     const int64_t total = rows * per_row;
-    for (int64_t e0 = threadIdx.x; e0 < total; e0 += 256 * U) {
+    // the parts of a tile take interleaved runs of 256 U elements
+    for (int64_t e0 = (int64_t)part * 256 * U + threadIdx.x; e0 < total; e0 += (int64_t)p.n_parts * 256 * U) {
         // loads of U elements first (the ring and sink stores may not be assumed disjoint
         // from the chunk, so a store would hold back the loads behind it)
         uint4 xk[U], xv[U];
@@ -1160,7 +1164,10 @@ hipError_t launch_prefill_chunk(const DecodeArgs &a, const CacheArgs &c, const v
     ap.rope = a.rope;
     ap.Hkv = c.Hkv; ap.w_ring = c.w; ap.s = c.s;
     ap.n_rtiles = (int)((max_q + BK - 1) / BK);
-    const int nb = (int)(c.S * ap.n_rtiles);
+    // several blocks per tile (a tile holds 64 H_kv d / 8 chunks, 8192 at H_kv 8, d 128), so
+    // that the grid fills the chip; one block per tile if the grid would outgrow 32-bit ids
+    ap.n_parts = c.S * ap.n_rtiles * 8 <= 0x7fffffff ? 8 : 1;
+    const int nb = (int)(c.S * ap.n_rtiles * ap.n_parts);
     if (c.d == 64) hipLaunchKernelGGL(chunk_append_kernel<64>, dim3((unsigned)nb), dim3(256), 0, st, ap);
     else hipLaunchKernelGGL(chunk_append_kernel<128>, dim3((unsigned)nb), dim3(256), 0, st, ap);
     return hipGetLastError();
