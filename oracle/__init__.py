@@ -18,7 +18,9 @@ beyond those are pinned only by the agreement of the two implementations.
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import os
+import platform
 import subprocess
 import threading
 
@@ -26,20 +28,51 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "swa_oracle.c")
-_LIB = os.path.join(_HERE, "libswa_oracle.so")
 _lock = threading.Lock()
 _lib = None
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo; the machine type where that is
+    missing)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.machine()
+
+
+def _host_tag() -> str:
+    """A short tag of the host CPU (model and feature flags): the library is compiled for
+    the host it runs on (-march=native), so each CPU kind gets its own build."""
+    flags = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("flags"):
+                    flags = line
+                    break
+    except OSError:
+        pass
+    return hashlib.sha1((cpu_model() + flags).encode()).hexdigest()[:12]
+
+
+_LIB = os.path.join(_HERE, "libswa_oracle_%s.so" % _host_tag())
 
 SIGMOID = 0
 SOFTMAX = 1
 
 
 def build(force: bool = False) -> str:
-    """Compile the C oracle with gcc (-O2, OpenMP) into oracle/libswa_oracle.so."""
+    """Compile the C oracle with gcc (-O3 -march=native, OpenMP) for this host into
+    oracle/libswa_oracle_<cpu tag>.so."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall", "-Werror",
-               "-o", tmp, _SRC, "-lm"]
+        cmd = ["gcc", "-O3", "-march=native", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+               "-Wall", "-Werror", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -295,10 +295,20 @@ int swa_oracle_decode(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, 
     double *qt = (double *)malloc(sizeof(double) * (size_t)d);
     double *x = (double *)malloc(sizeof(double) * (size_t)(w + s));
     const double **vv = (const double **)malloc(sizeof(double *) * (size_t)(w + s));
-    if (!qt || !x || !vv) { free(qt); free(x); free(vv); return -1; }
+    int64_t *slot_of = (int64_t *)malloc(sizeof(int64_t) * (size_t)w);
+    if (!qt || !x || !vv || !slot_of) { free(qt); free(x); free(vv); free(slot_of); return -1; }
     for (int64_t sq = 0; sq < S; ++sq) {
         int64_t p = q_pos[sq];
         int64_t lo = p - w + 1 > 0 ? p - w + 1 : 0;
+        /* which slot records each position lo..p (-1: none); a position recorded by two
+         * slots is not a ring state */
+        for (int64_t e = 0; e < w; ++e) slot_of[e] = -1;
+        for (int64_t t = 0; t < w; ++t) {
+            int64_t P = ring_pos[sq * w + t];
+            if (P < lo || P > p) continue;
+            if (slot_of[P - lo] >= 0) { free(qt); free(x); free(vv); free(slot_of); return -1; }
+            slot_of[P - lo] = t;
+        }
         for (int64_t h = 0; h < Hq; ++h) {
             int64_t hk = h / group;
             const double *qh = q + (sq * Hq + h) * d;
@@ -314,14 +324,13 @@ int swa_oracle_decode(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, 
             }
             /* ring entries in position order lo..p */
             for (int64_t P = lo; P <= p; ++P) {
-                for (int64_t t = 0; t < w; ++t) {
-                    if (ring_pos[sq * w + t] != P) continue;
-                    const double *kj = k_ring + ((sq * Hkv + hk) * w + t) * d;
-                    double bias = slopes ? slopes[h] * (double)(p - P) : 0.0;
-                    x[n] = scale * dot(qt, kj, d) + bias;
-                    vv[n] = v_ring + ((sq * Hkv + hk) * w + t) * d;
-                    ++n;
-                }
+                int64_t t = slot_of[P - lo];
+                if (t < 0) continue;
+                const double *kj = k_ring + ((sq * Hkv + hk) * w + t) * d;
+                double bias = slopes ? slopes[h] * (double)(p - P) : 0.0;
+                x[n] = scale * dot(qt, kj, d) + bias;
+                vv[n] = v_ring + ((sq * Hkv + hk) * w + t) * d;
+                ++n;
             }
             weights(x, n, mode);
             double *oh = o + (sq * Hq + h) * d;
@@ -330,7 +339,7 @@ int swa_oracle_decode(int64_t S, int64_t Hq, int64_t Hkv, int64_t d, int64_t w, 
                 for (int64_t c = 0; c < d; ++c) oh[c] += x[e] * vv[e][c];
         }
     }
-    free(qt); free(x); free(vv);
+    free(qt); free(x); free(vv); free(slot_of);
     return 0;
 }
 
