@@ -1098,10 +1098,26 @@ size_t decode_workspace_bytes(const DecodeArgs &a, const CacheArgs &c) {
     return sizeof(float) * (size_t)(c.S * c.Hkv * ns * (a.Hq / c.Hkv) * (c.d + 2));
 }
 
+// The fast kernels read q, the cache rows, the appended token and the rotation angles with
+// 16-byte vector loads and buffer-to-LDS transfers, store the fused append in 4-byte words and
+// keep the split partials as float32: every tensor they touch must sit on a 16-byte boundary.
+// Calls with a tensor off that boundary take the general kernel (which needs no workspace).
+bool decode_fast_aligned(const DecodeArgs &a, const CacheArgs &c, const void *q, const void *o,
+                         const void *k_new, const void *v_new, const void *ws) {
+    const uintptr_t bits = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(o) |
+                           reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+                           reinterpret_cast<uintptr_t>(c.k_ring) | reinterpret_cast<uintptr_t>(c.v_ring) |
+                           reinterpret_cast<uintptr_t>(c.k_sink) | reinterpret_cast<uintptr_t>(c.v_sink) |
+                           reinterpret_cast<uintptr_t>(a.rope) |
+                           (decode_nsplit(c) > 1 ? reinterpret_cast<uintptr_t>(ws) : 0);
+    return (bits & 15) == 0;
+}
+
 hipError_t launch_decode(const DecodeArgs &a, const CacheArgs &c, const void *q,
                          const int32_t *q_pos, void *o, void *ws, size_t, hipStream_t st) {
     if (c.S == 0) return hipSuccess;
-    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, nullptr, nullptr, ws, st);
+    if (decode_fast_ok(a, c) && decode_fast_aligned(a, c, q, o, nullptr, nullptr, ws))
+        return launch_decode_fast(a, c, q, q_pos, o, nullptr, nullptr, ws, st);
     const int64_t G = a.Hq / c.Hkv;
     int KC = 64;
     while (KC > 8 && decode_general_lds(G, c.d, KC) > 64 * 1024) KC /= 2;
@@ -1125,7 +1141,8 @@ hipError_t launch_decode_append(const DecodeArgs &a, const CacheArgs &c, const v
                                 const void *k_new, const void *v_new, const int32_t *q_pos,
                                 void *o, void *ws, size_t ws_bytes, hipStream_t st) {
     if (c.S == 0) return hipSuccess;
-    if (decode_fast_ok(a, c)) return launch_decode_fast(a, c, q, q_pos, o, k_new, v_new, ws, st);
+    if (decode_fast_ok(a, c) && decode_fast_aligned(a, c, q, o, k_new, v_new, ws))
+        return launch_decode_fast(a, c, q, q_pos, o, k_new, v_new, ws, st);
     // general shapes: the append kernel, then the decode kernel, in stream order
     const hipError_t e = launch_kv_append(c, k_new, v_new, q_pos, 1, a.rope, a.rope_rows, st);
     if (e != hipSuccess) return e;

@@ -103,16 +103,25 @@ C5 = PrefillConfig("gemma3_local_bf16_Hq16_Hkv8_N131072_d128_w1024", "bf16", B=1
                    slopes=tuple(balanced_alibi_slopes(16)), heavy_k_frac=0.01, seed=5)
 
 # Decode at long windows (measurement only): the C3 layer shape with its 4,096-token window
-# over 64 sequences, and a global-attention-style 32K window over 8 sequences, which runs
-# split over several blocks per (sequence, kv head). Both caches outgrow the last-level cache.
+# over 64 sequences, and a 32K sliding window over 8 sequences (positions past the window),
+# which runs split over several blocks per (sequence, kv head). Both caches outgrow the
+# last-level cache.
 DECODE_W4096 = DecodeConfig("mistral7b_window_decode_bf16_S64_Hq32_Hkv8_d128_w4096", "bf16",
                             num_seqs=64, H_q=32, H_kv=8, d=128, w=4096, s=0, mode=SOFTMAX,
                             rope_theta=1e6, slopes=None, len_lo=8192, len_hi=32768, steps=32,
                             seed=6)
-DECODE_W32K = DecodeConfig("global_window_decode_bf16_S8_Hq32_Hkv8_d128_w32768", "bf16",
+DECODE_W32K = DecodeConfig("sliding_w32k_decode_bf16_S8_Hq32_Hkv8_d128_w32768", "bf16",
                            num_seqs=8, H_q=32, H_kv=8, d=128, w=32768, s=0, mode=SOFTMAX,
                            rope_theta=1e6, slopes=None, len_lo=40000, len_hi=60000, steps=32,
                            seed=7)
+# A global layer of a Gemma-3-style local/global stack (Sliding Window Attention glossary,
+# "interleaving local and global layers": the global layers see the whole 128K context):
+# a cache of the full 131,072-token context, every query position below it (so each key set
+# is the whole history), at the local layer's head shape (H_q 16, H_kv 8, d 128), softmax.
+DECODE_GLOBAL_128K = DecodeConfig("gemma3_global_decode_bf16_S2_Hq16_Hkv8_d128_ctx131072",
+                                  "bf16", num_seqs=2, H_q=16, H_kv=8, d=128, w=131072, s=0,
+                                  mode=SOFTMAX, rope_theta=1e6, slopes=None, len_lo=98304,
+                                  len_hi=131000, steps=32, seed=9)
 
 
 @dataclass(frozen=True)

@@ -35,3 +35,32 @@ def assert_parity(got, ref, in_dtype: str, label: str = ""):
         assert max_rel <= TOL_BF16_MAX, "%s max_rel %.3e" % (label, max_rel)
         assert sum_rel <= TOL_BF16_SUM, "%s sum_rel %.3e" % (label, sum_rel)
     return max_rel, sum_rel
+
+
+def errors_blocked(got, ref, block: int = 4096):
+    """errors() over a [B, N, ...] pair in blocks of rows along N, so that outputs of a
+    whole long sequence are compared without float64 copies of the whole tensor. Returns
+    (max|err| / max|ref|, sum|err| / sum|ref|) over every element."""
+    ref = np.asarray(ref)
+    assert tuple(got.shape) == ref.shape, (tuple(got.shape), ref.shape)
+    emax = rmax = esum = rsum = 0.0
+    for a in range(0, ref.shape[1], block):
+        g = got[:, a:a + block].detach().to("cpu", torch.float64).numpy()
+        r = ref[:, a:a + block].astype(np.float64, copy=False)
+        assert np.all(np.isfinite(g)), "non-finite output in rows %d.." % a
+        e = np.abs(g - r)
+        emax = max(emax, float(e.max()))
+        rmax = max(rmax, float(np.abs(r).max()))
+        esum += float(e.sum())
+        rsum += float(np.abs(r).sum())
+    return emax / max(rmax, 1e-300), esum / max(rsum, 1e-300)
+
+
+def misaligned(t):
+    """The same values at a data pointer 4 bytes past a 16-byte boundary."""
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    off = 4 // t.element_size()
+    out = flat[off:off + t.numel()].view(t.shape)
+    out.copy_(t)
+    assert out.data_ptr() % 16 != 0
+    return out
