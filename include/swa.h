@@ -69,8 +69,12 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * sigmoid q is also multiplied by -scale * log2(e) before its rounding, and the ALiBi term
  * enters the product through float16 splits of the slope and of the query offset) and the
  * value product from float16 (softmax) or bf16 (sigmoid) operands, with float32
- * accumulation: those inputs must stay within the float16 range (|x| < 65504), and
- * |slope| / scale below 2^24. Other shapes run on a general float32 vector kernel.
+ * accumulation, and |slope| / scale below 2^24. Every operand taken as float16 saturates
+ * at +-65504, the largest finite float16, instead of overflowing: the rotated keys, the
+ * rotated queries (for sigmoid after the factor -scale * log2(e)) and, for softmax, the
+ * values. Inputs past that range thus give the attention of the saturated operands, with
+ * finite outputs; inputs within it are exact up to the float16 rounding. Other shapes run
+ * on a general float32 vector kernel, where nothing saturates.
  */
 typedef struct swa_prefill_params {
     int64_t B, H_q, H_kv, N, d;
@@ -108,7 +112,8 @@ size_t swa_prefill_workspace_bytes(const swa_prefill_params *p);
  * gradients). They take every shape swa_prefill takes. bf16 q, k, v with d in {64, 128}, a
  * contiguous window (dilation 0 or 1) and 16-byte aligned tensors (q, k, v, o, dout, dq, dk,
  * dv, rope_table) run on the matrix cores, with operands as in swa_prefill (float16
- * products, float32 accumulation), so dout must stay within the float16 range too; every
+ * products, float32 accumulation; the float16 operands of the inputs, dout among them,
+ * saturate at +-65504 as in swa_prefill, and v is taken as float16 in both modes); every
  * other shape, dilated windows included, runs on general float32 vector kernels. Each call
  * picks its path by these rules alone, so a forward and a backward may take different
  * paths: lse and o mean the same on both.
@@ -208,6 +213,12 @@ swa_status swa_kv_append(const swa_cache *c, const void *k_new, const void *v_ne
  *   q, o : [num_seqs, H_q, d]   (q not yet rotated; rotated here at q_pos)
  * H_q % cache->H_kv == 0. workspace: device memory of at least
  * swa_decode_workspace_bytes(p, c) bytes (may be NULL when that is 0).
+ * Paths: a bf16 cache with d in {64, 128} and H_q / H_kv in {1, 2, 4, 8} runs on vector
+ * kernels that read with 16-byte loads; they need q, o, the four cache tensors, the rotation
+ * table and (when the call splits the window into key ranges) the workspace on 16-byte
+ * boundaries. A call with any of them off that boundary, and every other shape, runs on a
+ * general float32 kernel with element accesses, which needs no workspace: the result is
+ * the same up to rounding.
  */
 typedef struct swa_decode_params {
     int64_t H_q;
@@ -233,7 +244,9 @@ swa_status swa_decode(const swa_decode_params *p, const swa_cache *c, const void
  * whose key range holds q_pos writes the token and uses it without reading it back (long
  * windows over few sequences add the merge launch that swa_decode also uses).
  * A sequence whose q_pos is invalid (negative, or outside the rotation table) gets NaN
- * outputs and its cache is left untouched. Other arguments as in swa_decode.
+ * outputs and its cache is left untouched. Other arguments as in swa_decode; the alignment
+ * rule there covers k_new and v_new too (off a 16-byte boundary, the append and the query
+ * run as two launches on the general kernels).
  */
 swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, const void *q,
                              const void *k_new, const void *v_new, const int32_t *q_pos,
@@ -241,6 +254,7 @@ swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, con
 
 /* Bytes of workspace swa_decode needs for this problem (0 when it needs none). */
 size_t swa_decode_workspace_bytes(const swa_decode_params *p, const swa_cache *c);
+
 
 /*
  * Chunked prefill over the ring cache, variable-length batch (a new chunk of each sequence

@@ -209,8 +209,8 @@ __global__ __launch_bounds__(256) void bwd_pack_q_kernel(PackQ p) {
             else
                 stg16(p.qimg + img + slot, ROT ? rotate_chunk(xq[e], t0, t1) : convert_chunk(xq[e]));
             stg16(p.gimg + img + slot,
-                  make_uint4(pack_f16x2(g8[e][0], g8[e][1]), pack_f16x2(g8[e][2], g8[e][3]),
-                             pack_f16x2(g8[e][4], g8[e][5]), pack_f16x2(g8[e][6], g8[e][7])));
+                  make_uint4(pack_f16x2_sat(g8[e][0], g8[e][1]), pack_f16x2_sat(g8[e][2], g8[e][3]),
+                             pack_f16x2_sat(g8[e][4], g8[e][5]), pack_f16x2_sat(g8[e][6], g8[e][7])));
             if (MODE == 1) {
                 float dot = 0.0f;
 #pragma unroll
@@ -238,7 +238,9 @@ struct BwdParams {
     const uint16_t *kimg, *vimg, *qimg, *gimg;
     const float *stats, *slopes, *rope;
     void *dq, *dk, *dv;
-    float *sink_k, *sink_v;  // [B, Hkv, sink_blocks * KP, D] partial dk~, dv of the sink blocks
+    // partial dk~, dv of the sink blocks from the extra workgroups, one slot per split:
+    // [B, Hkv, n_splits, sink_blocks * 128, D] float32 each
+    float *sink_k, *sink_v;
     int64_t N, Hq, Hkv, G;
     int n_tiles;             // 64-row tiles of every image slice
     int n_qtiles, n_hgroups; // dq grid
@@ -248,6 +250,13 @@ struct BwdParams {
     float cs, scale;
     int out_bf16;
 };
+
+// Element offset of key j's row in split sp's slot of the sink partials (times D).
+template <int D>
+__device__ __forceinline__ int64_t sink_slot_d(const BwdParams &p, int b, int hkv, int sp, int j) {
+    const int64_t sk = (int64_t)p.sink_blocks * 128;
+    return ((((int64_t)b * p.Hkv + hkv) * p.n_splits + sp) * sk + j) * D;
+}
 
 // Transposing-read offsets: lane (G4, rr, a) supplies row 8 h + 4 (G4 / 2) + rr of an 8 x 32
 // block and the column group 16 (G4 % 2) + 4 a of 32-column block db.
@@ -660,30 +669,43 @@ void bwd_dkv_kernel(BwdParams p) {
 
     // ---- epilogue
     if (SINK) {
+        // this split's partial into its own slot (no atomics: the block's own workgroup sums
+        // the slots in split order, so the result does not depend on timing)
         if (!active) return;
-        const int64_t sk = (int64_t)p.sink_blocks * T::KP;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
-                const int64_t off = (((int64_t)b * p.Hkv + hkv) * sk + j) * D + d;
-                atomicAdd(p.sink_k + off, dk[db][e]);
-                atomicAdd(p.sink_v + off, dv[db][e]);
+                const int64_t off = sink_slot_d<D>(p, b, hkv, split, j) + d;
+                p.sink_k[off] = dk[db][e];
+                p.sink_v[off] = dv[db][e];
             }
         return;
     }
     if (j >= N) return;
     if (p.sink_k != nullptr && kblk < p.sink_blocks) {
-        const int64_t sk = (int64_t)p.sink_blocks * T::KP;
+        f32x16_t sk_[DB], sv_[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sk_[db][e] = sv_[db][e] = 0.0f;
+        for (int sp = 0; sp < p.n_splits; ++sp)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const int64_t off = sink_slot_d<D>(p, b, hkv, sp, j) + d;
+                    sk_[db][e] += p.sink_k[off];
+                    sv_[db][e] += p.sink_v[off];
+                }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
-                const int64_t off = (((int64_t)b * p.Hkv + hkv) * sk + j) * D + d;
-                dk[db][e] += p.sink_k[off];
-                dv[db][e] += p.sink_v[off];
+                dk[db][e] += sk_[db][e];
+                dv[db][e] += sv_[db][e];
             }
     }
 #pragma unroll
@@ -925,28 +947,38 @@ void bwd_dkv2_kernel(BwdParams p) {
     }
 
     // ---- epilogue: the P role owns dv, the dX role dk
-    const int64_t sk = (int64_t)p.sink_blocks * T::KP;
     float *sink = role_p ? p.sink_v : p.sink_k;
     if (SINK) {
+        // this split's partial into its own slot, summed in split order below
         if (!active) return;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
-                atomicAdd(sink + (((int64_t)b * p.Hkv + hkv) * sk + j) * D + d, acc[db][e]);
+                sink[sink_slot_d<D>(p, b, hkv, split, j) + d] = acc[db][e];
             }
         return;
     }
     if (j >= N) return;
     if (sink != nullptr && kblk < p.sink_blocks) {
+        f32x16_t part[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
-                acc[db][e] += sink[(((int64_t)b * p.Hkv + hkv) * sk + j) * D + d];
-            }
+            for (int e = 0; e < 16; ++e) part[db][e] = 0.0f;
+        for (int sp = 0; sp < p.n_splits; ++sp)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int d = 32 * db + 8 * (e >> 2) + 4 * g + (e & 3);
+                    part[db][e] += sink[sink_slot_d<D>(p, b, hkv, sp, j) + d];
+                }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[db][e] += part[db][e];
     }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -995,7 +1027,10 @@ BwdPlan bwd_plan(const PrefillArgs &a) {
         pl.sink_blocks = (int)((s + KP - 1) / KP);
         pl.n_splits = (int)((beyond + pl.split_tiles * BK - 1) / (pl.split_tiles * BK));
     }
-    pl.sink = pl.sink_blocks ? 2 * (size_t)(a.B * a.Hkv * pl.sink_blocks * KP) * a.d * sizeof(float) : 0;
+    // one partial per split (summed in split order: deterministic)
+    pl.sink = pl.sink_blocks ? 2 * (size_t)(a.B * a.Hkv * pl.n_splits * pl.sink_blocks * KP) *
+                                   a.d * sizeof(float)
+                             : 0;
     return pl;
 }
 

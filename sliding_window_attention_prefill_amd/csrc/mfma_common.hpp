@@ -35,14 +35,23 @@ __device__ __forceinline__ float4 buf_load16f(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 
+// Two floats -> two float16 operands that saturate at +-65504, the largest finite float16,
+// where a plain conversion would overflow to infinity: an input operand past the float16
+// range enters the products clamped, and the outputs stay finite.
+constexpr float F16_MAX = 65504.0f;
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float a, float b) {
+    return pack_f16x2(__builtin_amdgcn_fmed3f(a, -F16_MAX, F16_MAX),
+                      __builtin_amdgcn_fmed3f(b, -F16_MAX, F16_MAX));
+}
+
 // A dword of two bf16 inputs -> two float16 matrix operands, rotated by (c, s) or not.
 __device__ __forceinline__ uint32_t rotate_pair(uint32_t w, float c, float s) {
     const float a = __uint_as_float(w << 16);
     const float b = __uint_as_float(w & 0xffff0000u);
-    return pack_f16x2(fmaf(-b, s, a * c), fmaf(a, s, b * c));
+    return pack_f16x2_sat(fmaf(-b, s, a * c), fmaf(a, s, b * c));
 }
 __device__ __forceinline__ uint32_t to_f16_pair(uint32_t w) {
-    return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+    return pack_f16x2_sat(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 __device__ __forceinline__ uint4 rotate_chunk(uint4 x, float4 t0, float4 t1) {
     return make_uint4(rotate_pair(x.x, t0.x, t0.y), rotate_pair(x.y, t0.z, t0.w),
@@ -57,7 +66,7 @@ __device__ __forceinline__ uint4 rotate_chunk_scaled(uint4 x, float4 t0, float4 
                       rotate_pair(x.z, t1.x * f, t1.y * f), rotate_pair(x.w, t1.z * f, t1.w * f));
 }
 __device__ __forceinline__ uint32_t to_f16_pair_scaled(uint32_t w, float f) {
-    return pack_f16x2(__uint_as_float(w << 16) * f, __uint_as_float(w & 0xffff0000u) * f);
+    return pack_f16x2_sat(__uint_as_float(w << 16) * f, __uint_as_float(w & 0xffff0000u) * f);
 }
 __device__ __forceinline__ uint4 convert_chunk_scaled(uint4 x, float f) {
     return make_uint4(to_f16_pair_scaled(x.x, f), to_f16_pair_scaled(x.y, f),

@@ -134,6 +134,23 @@ def test_backward_deterministic():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d,mode", [(64, wl.SIGMOID), (128, wl.SOFTMAX), (128, wl.SIGMOID)])
+def test_backward_deterministic_several_sink_splits(d, mode):
+    """Sinks that only the sink rule reaches over a long sequence: the extra workgroups split
+    the queries past the window into 1024-query pieces (N - (127 + w) = 4,809 gives 5
+    splits). Each split keeps its own partial and the block sums them in split order, so two
+    runs give bit-identical gradients, which also match the oracle."""
+    B, Hq, Hkv, N, w, s, theta = 1, 4, 2, 5000, 64, 5, 1e4
+    q, k, v, dout = _inputs(B, Hq, Hkv, N, d, seed=21 + d, scale=0.8)
+    r1 = _run(q, k, v, dout, w, s, mode, None, theta)
+    r2 = _run(q, k, v, dout, w, s, mode, None, theta)
+    for a, b in zip(r1[2:5], r2[2:5]):
+        assert torch.equal(a, b)
+    ref = oracle.backward(q, k, v, r1[5].cpu(), w=w, s=s, mode=mode, rope_theta=theta)
+    for name, got, r in (("dq", r1[2], ref[0]), ("dk", r1[3], ref[1]), ("dv", r1[4], ref[2])):
+        assert_parity(got, r, "bf16", name)
+
+
 def test_backward_swat340m_layer_one_sequence():
     """The SWAT-340M layer (B 8, H 16, N 4096, d 64, w 512, sigmoid + balanced ALiBi + RoPE)
     in the full launch; every gradient of sequence 0 against the oracle."""
