@@ -8,12 +8,13 @@
 //   K(i) = { j <= i : i - j < w or j < s },  p = sigmoid (no normalisation) or softmax.
 //
 // How (gfx950):
-//   * One workgroup (4 wavefronts at d = 64, 8 at d = 128) owns 32 query rows per wavefront:
-//     positions x GP query heads that share one kv head, so each K/V tile in LDS serves the
-//     whole group and is fetched by fewer workgroups.
-//   * It walks only the 64-key tiles that intersect its band of keys plus the sink tiles the window no longer covers (the block skipping the glossary describes
-//     for windowed exact-attention kernels). Tiles inside every row's key set run without
-//     the element predicate.
+//   * One workgroup of 4 wavefronts owns 32 query rows per wavefront: positions x GP query
+//     heads that share one kv head, so each K/V tile in LDS serves the whole group and is
+//     fetched by fewer workgroups.
+//   * It walks only the 64-key tiles that intersect its band of keys, plus the sink tiles the
+//     window no longer covers (the block skipping the glossary describes for windowed
+//     exact-attention kernels). Tiles inside every row's key set run without the element
+//     predicate.
 //   * Each wavefront computes S^T = K Q^T (32 keys x 32 queries per 32x32x16 matrix
 //     instruction), so a lane holds one query's scores; the scale and the bias fold into
 //     FMAs in base-2 units; sigmoid is 1 / (1 + 2^t), softmax is online with a lazily
@@ -21,13 +22,14 @@
 //   * Score operands are float16: q and k are widened from bf16, rotated in float32 and
 //     rounded once (inputs must stay within the float16 range, |x| < 65504).
 //   * A pre-pass rotates every key once into float16 tile images laid out exactly as LDS
-//     holds them (for softmax it also converts V to float16 images); the main kernel copies
-//     tiles with buffer-to-LDS transfers, which take no registers and no vector
-//     instructions. Sigmoid reads V rows as stored (bf16) with the same transfers, and its
-//     second product runs in bf16 with the weights rounded to bf16; softmax's runs in
-//     float16. V stays row-major in LDS: the transposing LDS read (ds_read_b64_tr_b16)
-//     delivers it in the operand layout of the second product, in the key order of the
-//     score registers.
+//     holds them (for softmax it also stores V transposed, as float16 images of V^T); the
+//     main kernel copies tiles with buffer-to-LDS transfers, which take no registers and no
+//     vector instructions. Sigmoid reads V rows as stored (bf16) with the same transfers,
+//     and its second product runs in bf16 with the weights rounded to bf16; those rows stay
+//     row-major in LDS and the transposing LDS read (ds_read_b64_tr_b16) delivers them in
+//     the operand layout of the second product. Softmax's second product runs in float16 and
+//     reads the V^T tile with plain 16-byte LDS reads (twice the bytes per read of the
+//     transposing one), its keys stored in the order of the score registers.
 //   * ALiBi: the key part of the bias enters the score accumulator through one more matrix
 //     instruction per 32-key block (exact key offsets against a two-term float16 split of
 //     the slope), so each score needs one FMA for scale and bias together.
@@ -68,6 +70,23 @@ __host__ __device__ __forceinline__ constexpr int kswz(int r) {
 template <int D>
 __host__ __device__ __forceinline__ constexpr int vswz(int r) {
     return D == 64 ? ((r >> 1) & 1) << 2 : (r & 3) << 2;
+}
+
+// Transposed value tiles (softmax): V^T, one row of the 64 keys per head dimension d,
+// float16. The second product takes V^T as its A operand, 8 consecutive k per lane, and
+// the k order of a 16-key step t must be the key order of the weights, which the score
+// registers hold as keys 16 t + 4 g + {0..3, 8..11} for lane half g. So within each
+// 16-key group the row stores the keys in the order 0-3, 8-11, 4-7, 12-15: stored position
+// p holds key vt_key(p), and lane half g of step t reads the 16 bytes at position 16 t + 8 g.
+// Chunk c (8 positions) of row d sits at chunk c ^ vtswz(d): the 16 rows one read covers at
+// one chunk then fall on 16 distinct bank groups.
+__host__ __device__ __forceinline__ constexpr int vt_key(int p) {
+    return (p & ~15) + ((p >> 3) & 1) * 4 + (p & 3) + ((p >> 2) & 1) * 8;
+}
+__host__ __device__ __forceinline__ constexpr int vtswz(int d) { return (d >> 1) & 7; }
+// element offset of chunk c of row d in a transposed tile image
+__host__ __device__ __forceinline__ constexpr int vt_slot(int d, int c) {
+    return (d * 8 + (c ^ vtswz(d))) * 8;
 }
 
 // A chunked call (prefill over the ring cache): sequence b owns the packed rows
@@ -199,9 +218,13 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
             }
         }
     } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int cidx = tid + 256 * (r + pt), row = cidx / T::C, c = cidx % T::C;
+        // keys as above; values transposed through LDS: this block's part holds head
+        // dimensions [DP pt, DP pt + DP) of all 64 keys
+        constexpr int DP = D / T::KPT;               // 32 head dimensions per part
+        constexpr int TPR = DP / 8;                  // threads per key row (16-byte chunks)
+        __shared__ __attribute__((aligned(16))) uint16_t tr[PACK_HG][DP][BK];
+        {
+            const int cidx = tid + 256 * pt, row = cidx / T::C, c = cidx % T::C;
             const int64_t j = (int64_t)jt * BK + row;
             const bool in = j < p.N;
             float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
@@ -210,22 +233,44 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
                 t0 = as_float4(ldg16(t));
                 t1 = as_float4(ldg16(t + 4));
             }
+            const int vr = tid / TPR, vd = DP * pt + 8 * (tid % TPR);   // value row, dims
+            const int64_t jv = (int64_t)jt * BK + vr;
+            uint4 xk[PACK_HG], xv[PACK_HG];
+#pragma unroll
+            for (int u = 0; u < PACK_HG; ++u) {
+                xk[u] = xv[u] = make_uint4(0, 0, 0, 0);
+                if (u < nh && in) xk[u] = ldg16(p.k + ((b * p.N + j) * p.Hkv + h0 + u) * D + c * 8);
+                if (u < nh && jv < p.N) xv[u] = ldg16(p.v + ((b * p.N + jv) * p.Hkv + h0 + u) * D + vd);
+            }
             const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
-            const int vslot = (row * T::C + (c ^ vswz<D>(row))) * 8;
 #pragma unroll
             for (int u = 0; u < PACK_HG; ++u) {
                 if (u >= nh) break;
-                const int64_t hkv = h0 + u;
-                uint4 xk = make_uint4(0, 0, 0, 0), xv = make_uint4(0, 0, 0, 0);
-                if (in) {
-                    const int64_t off = ((b * p.N + j) * p.Hkv + hkv) * D + c * 8;
-                    xk = ldg16(p.k + off);
-                    xk = ROT ? rotate_chunk(xk, t0, t1) : convert_chunk(xk);
-                    xv = convert_chunk(ldg16(p.v + off));
+                const int64_t img = ((b * p.Hkv + h0 + u) * p.n_ktiles + jt) * T::IMG;
+                stg16(p.kimg + img + kslot, ROT ? rotate_chunk(xk[u], t0, t1) : convert_chunk(xk[u]));
+                const uint4 f = convert_chunk(xv[u]);
+                const uint32_t w4[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    tr[u][vd - DP * pt + 2 * m][vr] = (uint16_t)(w4[m] & 0xffffu);
+                    tr[u][vd - DP * pt + 2 * m + 1][vr] = (uint16_t)(w4[m] >> 16);
                 }
-                const int64_t img = ((b * p.Hkv + hkv) * p.n_ktiles + jt) * T::IMG;
-                stg16(p.kimg + img + kslot, xk);
-                stg16(p.vimg + img + vslot, xv);
+            }
+        }
+        __syncthreads();
+        {
+            // thread: head dimension DP pt + tid / 8, stored chunk tid % 8 (positions 8 c ..
+            // 8 c + 7: keys 16 (c / 2) + 4 (c % 2) + {0..3, 8..11})
+            const int dl = tid / 8, c = tid % 8;
+            const int k0 = 16 * (c >> 1) + 4 * (c & 1);
+            const int d = DP * pt + dl;
+#pragma unroll
+            for (int u = 0; u < PACK_HG; ++u) {
+                if (u >= nh) break;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(&tr[u][dl][k0]);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(&tr[u][dl][k0 + 8]);
+                const int64_t img = ((b * p.Hkv + h0 + u) * p.n_ktiles + jt) * T::IMG;
+                stg16(p.vimg + img + vt_slot(d, c), make_uint4(lo.x, lo.y, hi.x, hi.y));
             }
         }
     }
@@ -252,6 +297,8 @@ struct GatherParams {
 template <int D, bool ROT, bool VF16>
 __global__ __launch_bounds__(256) void chunk_gather_kernel(GatherParams p) {
     using T = Tile<D>;
+    // softmax: the values of each head go through LDS to be stored transposed
+    __shared__ __attribute__((aligned(16))) uint16_t tr[VF16 ? PACK_HG : 1][VF16 ? D : 1][BK];
     const int n_hg = (int)((p.Hkv + PACK_HG - 1) / PACK_HG);
     const int bid = blockIdx.x, tid = threadIdx.x;
     const int hg = bid % n_hg;
@@ -279,7 +326,7 @@ __global__ __launch_bounds__(256) void chunk_gather_kernel(GatherParams p) {
             t1 = as_float4(ldg16(tb + 4));
         }
         const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
-        const int vslot = VF16 ? (row * T::C + (c ^ vswz<D>(row))) * 8 : (row * T::C + c) * 8;
+        const int vslot = (row * T::C + c) * 8;
         // the row's loads for every head first, then its stores
         const uint16_t *ksrc = src == 1 ? p.k_new : src == 2 ? p.k_ring : p.k_sink;
         const uint16_t *vsrc = src == 1 ? p.v_new : src == 2 ? p.v_ring : p.v_sink;
@@ -304,7 +351,34 @@ __global__ __launch_bounds__(256) void chunk_gather_kernel(GatherParams p) {
             const uint4 k = (ROT && src == 1) ? rotate_chunk(xk[e], t0, t1) : convert_chunk(xk[e]);
             const int64_t img = ((b * p.Hkv + h0 + e) * p.n_ktiles + u) * T::IMG;
             stg16(p.kimg + img + kslot, k);
-            stg16(p.vimg + img + vslot, VF16 ? convert_chunk(xv[e]) : xv[e]);
+            if constexpr (VF16) {
+                const uint4 f = convert_chunk(xv[e]);
+                const uint32_t w4[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    tr[e][8 * c + 2 * m][row] = (uint16_t)(w4[m] & 0xffffu);
+                    tr[e][8 * c + 2 * m + 1][row] = (uint16_t)(w4[m] >> 16);
+                }
+            } else {
+                stg16(p.vimg + img + vslot, xv[e]);
+            }
+        }
+    }
+    if constexpr (VF16) {
+        // the transposed value images: D rows of 8 stored chunks per head
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < D * 8 / 256; ++r) {
+            const int oc = tid + 256 * r, d = oc / 8, c = oc % 8;
+            const int k0 = 16 * (c >> 1) + 4 * (c & 1);
+#pragma unroll
+            for (int e = 0; e < PACK_HG; ++e) {
+                if (e >= nh) break;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(&tr[e][d][k0]);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(&tr[e][d][k0 + 8]);
+                const int64_t img = ((b * p.Hkv + h0 + e) * p.n_ktiles + u) * T::IMG;
+                stg16(p.vimg + img + vt_slot(d, c), make_uint4(lo.x, lo.y, hi.x, hi.y));
+            }
         }
     }
 }
@@ -405,6 +479,7 @@ template <int D>
 struct LaneOffsets {
     int k[D / 16];                   // LDS element offset of the K row read of score step ks
     int v[D / 32];                   // LDS element offset of the V transposing read, block db
+    int vt[4];                       // LDS element offset of the V^T read of step t (block 0)
     uint32_t dimg[Tile<D>::DMA_W];   // source byte offset in a packed tile image, per transfer
     uint32_t dvraw[Tile<D>::DMA_W];  // source byte offset in the V input rows, per transfer
 };
@@ -519,17 +594,20 @@ __device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const 
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t *)(vl + 16 * t * D + lo.v[db]));
-            const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4_t *)(vl + (16 * t + 8) * D + lo.v[db]));
-            const s16x8_t a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            if constexpr (VF16)
+            if constexpr (VF16) {
+                // V^T rows 32 db .. 32 db + 31 of the transposed tile: one 16-byte read
+                const f16x8_t a = *reinterpret_cast<const f16x8_t *>(vl + 32 * db * BK + lo.vt[t]);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    __builtin_bit_cast(f16x8_t, a8), __builtin_bit_cast(f16x8_t, pk), oacc[db], 0, 0, 0);
-            else
+                    a, __builtin_bit_cast(f16x8_t, pk), oacc[db], 0, 0, 0);
+            } else {
+                const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_t *)(vl + 16 * t * D + lo.v[db]));
+                const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4_t *)(vl + (16 * t + 8) * D + lo.v[db]));
+                const s16x8_t a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8_t, a8), __builtin_bit_cast(bf16x8_t, pk), oacc[db], 0, 0, 0);
+            }
         }
     }
 }
@@ -743,6 +821,10 @@ void prefill_mfma_kernel(MfmaParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) lo.v[db] = row_l * D + (4 * (db ^ fq) + cb) * 8 + 4 * (a & 1);
     }
+    // V^T read of step t: row qc (plus 32 db), stored chunk 2 t + g (the swizzle of row
+    // 32 db + qc equals that of row qc)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lo.vt[t] = vt_slot(qc, 2 * t + g);
 #pragma unroll
     for (int r = 0; r < T::DMA_W; ++r) {
         const int slot = (wave * T::DMA_W + r) * 64 + lane;  // 16-byte slot of the tile image
