@@ -1,29 +1,33 @@
 """Benchmark: sliding-window attention prefill (and ring-buffer decode) on one MI355X.
 
-One step = one swa_prefill over the SWAT-340M-shaped layer (B=8, H=16, N=4096, d=64,
-w=512, sigmoid + balanced ALiBi + RoPE, bf16 in / fp32 accumulate) with inputs already in
-HBM. The value is in-window TFLOP/s: 4 * B * H_q * d * sum_i |K(i)| per step, counting
-only the two contractions inside the band (SWAT: Sliding Window Attention Training, linear
-O(N w) cost), divided by the timed wall clock of K steps. After the W warm-up steps the
-step keeps running untimed for 0.2 s (settle_steps in the line): the GPU's clocks ramp up
-over the first milliseconds of sustained load, and the timed steps should see the steady
-state.
+One step = one swa_prefill over the Mistral-7B-shaped layer (B=1, H_q=32, H_kv=8, N=32768,
+d=128, w=4096, softmax, RoPE theta 1e6, bf16 in / fp32 accumulate, float32 output), the
+largest single-GPU prefill workload, with inputs already in HBM. The value is in-window
+TFLOP/s: 4 * B * H_q * d * sum_i |K(i)| per step, counting only the two contractions inside
+the band (SWAT: Sliding Window Attention Training, linear O(N w) cost), divided by the timed
+wall clock of K steps. After the W warm-up steps the step keeps running untimed for 0.2 s
+(settle_steps in the line): the GPU's clocks ramp up over the first milliseconds of
+sustained load, and the timed steps should see the steady state.
 
 The JSON line also carries:
-  roofline      the prefill kernel against the bf16 matrix-core peak, with its average
-                launch duration timed by HIP events on the launch stream;
+  roofline      the headline prefill call against the bf16 matrix-core peak, with its
+                average launch duration timed by HIP events on the launch stream;
+  prefill_legs  the other prefill workloads (the Gemma-3-style 128K local layer, the
+                SWAT-340M layer) and bf16-output variants, each timed the same way with
+                its own roofline;
   decode        the SWA(64, 4) decode workload (64 sequences, 256 steps of ring append +
                 decode) in tokens/s and algorithmic GB/s against HBM peak, with the cache
                 resident in the last-level cache (as specified) and, as decode_cold, with 18
                 cache copies in rotation so that the rings come from HBM; decode_long adds
-                two long-window decode workloads whose caches live in HBM;
+                two long-window decode workloads and decode_global a global layer over a
+                131,072-token cache, whose caches live in HBM;
   chunk_prefill chunked prefill over the ring cache (8 prompts x 2048 rows per step at the
                 Mistral-7B layer shape, histories past the 4,096-token window), in-window
                 TFLOP/s of whole swa_prefill_chunk calls;
-  backward      the training backward (swa_prefill_backward) of this layer and of the
-                Mistral-7B-shaped one, in TFLOP/s of its five band contractions;
-  elementwise   the standalone rotation (swa_rope_apply on this layer's q) and ring append
-                (a 2,048-token chunk into 4,096-slot rings), algorithmic GB/s against HBM;
+  backward      the training backward (swa_prefill_backward) of the SWAT-340M and
+                Mistral-7B-shaped layers, in TFLOP/s of its five band contractions;
+  elementwise   the standalone rotation (swa_rope_apply on the SWAT layer's q) and ring
+                append (a 2,048-token chunk into 4,096-slot rings), GB/s against HBM;
   cpu_baseline  the float64 CPU oracle timed on the host cores on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -45,7 +49,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "SWA prefill in-window TFLOP/s (% MFMA peak); decode tok/s (% HBM BW)"
 KERNEL_SRC = os.path.join(ROOT, "sliding_window_attention_prefill_amd", "csrc", "prefill_mfma.hip")
 SETTLE_S = 0.2   # untimed steady load before the timed prefill steps (clock ramp-up)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic_swat340m.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
 
 
 def in_window_keys(N: int, w: int, s: int) -> int:
@@ -72,9 +76,9 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch from the committed counter profile, if it was taken on the
-    current kernel source."""
+def stored_traffic(workload: str, out_dtype: str):
+    """HBM bytes per launch of one prefill call (pre-pass + main kernel) from the committed
+    counter profile, if it was taken on the current kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -82,7 +86,8 @@ def stored_traffic():
         return None
     if t.get("kernel_sha256_16") != kernel_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    e = t.get("workloads", {}).get("%s/%s" % (workload, out_dtype))
+    return None if e is None else e.get("hbm_bytes_per_launch")
 
 
 def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
@@ -132,11 +137,11 @@ def bench_prefill(cfg, steps: int, warmup: int, out_dtype):
 
 
 def bench_decode(cfg, out_dtype, copies=1):
-    """256 steps of ring append + decode over 64 sequences (one fused launch per step),
-    captured once in a HIP graph so the launches replay without host overhead; timed over
-    the whole replay. With copies > 1, step t works on cache copy t % copies, so that the
-    copies together outgrow the 256 MB last-level cache and each step reads its ring from
-    HBM (the step's work is the same: every sequence is past w + s tokens)."""
+    """cfg.steps steps of ring append + decode (one fused launch per step), captured once
+    in a HIP graph so the launches replay without host overhead; timed over the whole
+    replay. With copies > 1, step t works on cache copy t % copies, so that the copies
+    together outgrow the 256 MB last-level cache and each step reads its ring from HBM (the
+    step's work is the same)."""
     import torch
     import sliding_window_attention_prefill_amd as swa
     import swa_workloads as wl
@@ -186,11 +191,15 @@ def bench_decode(cfg, out_dtype, copies=1):
     cache_bytes = sum(t.numel() * t.element_size() for t in
                       (cache.k_ring, cache.v_ring, cache.k_sink, cache.v_sink) if t is not None)
     ob = 4 if out_dtype == torch.float32 else 2
-    n_keys = cfg.w + cfg.s  # every sequence is past w + s tokens
-    per_step = (S * cfg.H_kv * n_keys * cfg.d * el * 2      # ring + sink K and V read
+    # keys read per step: |K(p)| = min(p + 1, w + s) for each sequence's query position p
+    # (w + s once a sequence is past its window; the whole history for a global layer)
+    lens = st.lengths.to(torch.int64).cpu()
+    keys_all = sum(int(torch.clamp(lens + t + 1, max=cfg.w + cfg.s).sum()) for t in range(T))
+    per_step = (cfg.H_kv * keys_all / T * cfg.d * el * 2    # ring + sink K and V read
                 + S * cfg.H_q * cfg.d * el                  # q read
                 + S * cfg.H_q * cfg.d * ob                  # o written
                 + 2 * S * cfg.H_kv * cfg.d * el * 2)        # append: new k, v read + written
+    per_step = int(round(per_step))
     secs = ms / 1e3
     gbs = per_step * T / secs / 1e9
     return {
@@ -353,24 +362,46 @@ def bench_backward(cfg, steps: int = 5):
             "note": "bf16 gradients; pre-passes, dk/dv and dq kernels"}
 
 
-def cpu_baseline(cfg, sample_batches: int):
-    """The float64 oracle on the first `sample_batches` sequences of the batch (all heads,
-    all rows), timed on the host; reported in the metric's unit."""
+def cpu_baseline(cfg, sample_rows: int):
+    """The float64 oracle on a bounded sample of the workload: the last `sample_rows` query
+    rows of the first sequence, every head (rows past the window edge, each with a full key
+    set), timed on the host; reported in the metric's unit (in-window FLOPs of the sample
+    per second)."""
     import oracle
     import swa_workloads as wl
 
-    sub = cfg.with_(B=sample_batches)
+    sub = cfg.with_(B=1)
     q, k, v = wl.prefill_inputs(sub, device="cpu")
+    n = min(sample_rows, cfg.N)
+    rows = list(range(cfg.N - n, cfg.N))
+    oracle.build()
     t0 = time.perf_counter()
     oracle.prefill(q, k, v, w=sub.w, s=sub.s, mode=sub.mode, slopes=sub.slopes,
-                   rope_theta=sub.rope_theta)
+                   rope_theta=sub.rope_theta, rows=rows)
     secs = time.perf_counter() - t0
+    keys = sum(min(i + 1, cfg.w + cfg.s) for i in rows)
+    flops = 4.0 * cfg.H_q * cfg.d * keys
     return {
-        "value": round(prefill_flops(sub) / secs / 1e12, 6), "unit": "TFLOP/s",
-        "cores": oracle.threads(), "kind": "oracle",
-        "sample": "%d of %d sequences (all %d heads, all %d rows): %.1f s"
-                  % (sample_batches, cfg.B, cfg.H_q, cfg.N, secs),
+        "value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s",
+        "cores": oracle.threads(), "cpu": oracle.cpu_model(), "kind": "oracle",
+        "sample": "rows %d..%d of %d of sequence 0 (all %d heads, %.3g in-window FLOPs): "
+                  "%.1f s" % (rows[0], rows[-1], cfg.N, cfg.H_q, flops, secs),
     }
+
+
+def prefill_line(cfg, steps: int, warmup: int, out_name: str):
+    """One prefill workload timed as the headline step is: (wall, kernel_ms, settle) plus
+    its roofline object."""
+    import torch
+    out_dtype = torch.float32 if out_name == "f32" else torch.bfloat16
+    wall, kernel_ms, settle = bench_prefill(cfg, steps, warmup, out_dtype)
+    flops = prefill_flops(cfg)
+    achieved = flops / (kernel_ms / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": stored_traffic(cfg.name, out_name), "kernel_ms": round(kernel_ms, 5),
+            "algorithmic_bytes": prefill_bytes(cfg, 4 if out_name == "f32" else 2)}
+    return wall, kernel_ms, settle, roof
 
 
 def main():
@@ -378,14 +409,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c5"])
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c5"])
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-elementwise", action="store_true")
-    ap.add_argument("--cpu-sample-batches", type=int, default=8)
+    ap.add_argument("--cpu-sample-rows", type=int, default=8192,
+                    help="query rows of sequence 0 the CPU baseline computes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes three times (the "
                          "known-size kernel that scales the HBM byte counters), then exit")
@@ -409,12 +442,11 @@ def main():
         print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
         return
 
-    cfg = {"c2": wl.C2, "c3": wl.C3, "c5": wl.C5}[args.workload]
-    out_dtype = torch.float32 if args.out_dtype == "f32" else torch.bfloat16
-    wall, kernel_ms, settle = bench_prefill(cfg, args.steps, args.warmup, out_dtype)
+    cfgs = {"c2": wl.C2, "c3": wl.C3, "c5": wl.C5}
+    cfg = cfgs[args.workload]
+    wall, kernel_ms, settle, roof = prefill_line(cfg, args.steps, args.warmup, args.out_dtype)
     flops = prefill_flops(cfg)
     value = flops * args.steps / wall / 1e12
-    achieved = flops / (kernel_ms / 1e3) / 1e12
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "settle_steps": settle,
@@ -424,24 +456,35 @@ def main():
                    "N": cfg.N, "d": cfg.d, "w": cfg.w, "s": cfg.s,
                    "mode": "sigmoid" if cfg.mode == wl.SIGMOID else "softmax",
                    "out_dtype": args.out_dtype, "in_window_flops": flops},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": stored_traffic(), "kernel_ms": round(kernel_ms, 5),
-                     "algorithmic_bytes": prefill_bytes(cfg, 4 if args.out_dtype == "f32" else 2)},
+        "roofline": roof,
     }
+    if not args.no_legs:
+        legs = []
+        order = [("c5", "f32"), ("c2", "f32"), ("c3", "bf16"), ("c5", "bf16"), ("c2", "bf16")]
+        for name, od in order:
+            if name == args.workload and od == args.out_dtype:
+                continue
+            c = cfgs[name]
+            lw, lk, _, lroof = prefill_line(c, args.steps, args.warmup, od)
+            legs.append({"workload": c.name, "out_dtype": od,
+                         "ms_per_step": round(lw * 1e3 / args.steps, 4),
+                         "TFLOP_s": round(prefill_flops(c) * args.steps / lw / 1e12, 2),
+                         "roofline": lroof})
+        result["prefill_legs"] = legs
     if not args.no_decode:
         result["decode"] = bench_decode(wl.C4, torch.float32)
         result["decode_cold"] = bench_decode(wl.C4, torch.float32, copies=18)
         result["decode_long"] = [bench_decode(c, torch.float32)
                                  for c in (wl.DECODE_W4096, wl.DECODE_W32K)]
+        result["decode_global"] = bench_decode(wl.DECODE_GLOBAL_128K, torch.float32)
     if not args.no_chunk:
         result["chunk_prefill"] = bench_chunk(wl.CHUNK_W4096, torch.float32)
     if not args.no_elementwise:
         result["elementwise"] = bench_elementwise()
     if not args.no_backward:
-        result["backward"] = [bench_backward(c) for c in (cfg, wl.C3)]
+        result["backward"] = [bench_backward(c) for c in (wl.C2, wl.C3)]
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_batches)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample_rows)
     print(json.dumps(result), flush=True)
 
 
