@@ -255,6 +255,22 @@ swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, con
 /* Bytes of workspace swa_decode needs for this problem (0 when it needs none). */
 size_t swa_decode_workspace_bytes(const swa_decode_params *p, const swa_cache *c);
 
+/*
+ * swa_decode_append for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and the same kernels, with the split partials kept in a 4 MiB device
+ * array inside the library instead of a workspace. Each GPU the library runs on holds its own
+ * copy of that array from the first call on that device until the process ends; the first
+ * call on a device looks up the array's address (no allocation). The call allocates and frees
+ * nothing. Every call on one GPU shares that GPU's array, so calls that overlap in time on
+ * one GPU (on different streams, or from several threads) race and must not be issued.
+ * A problem whose swa_decode_workspace_bytes exceeds 4 MiB is rejected with
+ * SWA_ERR_UNSUPPORTED before anything is launched (use swa_decode_append with a workspace).
+ * Arguments, layouts and errors otherwise as swa_decode_append.
+ */
+swa_status swa_decode_append_static(const swa_decode_params *p, const swa_cache *c,
+                                    const void *q, const void *k_new, const void *v_new,
+                                    const int32_t *q_pos, void *o, void *stream);
 
 /*
  * Chunked prefill over the ring cache, variable-length batch (a new chunk of each sequence

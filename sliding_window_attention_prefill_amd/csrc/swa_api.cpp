@@ -280,6 +280,30 @@ swa_status swa_decode_append(const swa_decode_params *p, const swa_cache *c, con
     return hip_status(e);
 }
 
+swa_status swa_decode_append_static(const swa_decode_params *p, const swa_cache *c,
+                                    const void *q, const void *k_new, const void *v_new,
+                                    const int32_t *q_pos, void *o, void *stream) {
+    swa_status st = check_decode(p, c);
+    if (st != SWA_OK) return st;
+    if (c->num_seqs > 0 && (!q || !q_pos || !o || !k_new || !v_new)) return SWA_ERR_INVALID_ARGUMENT;
+    if (c->num_seqs * c->H_kv > 0x7fffffff) return SWA_ERR_UNSUPPORTED;
+    const swa::DecodeArgs a = decode_args(p, c->d);
+    const swa::CacheArgs ca = cache_args(c);
+    // the split partials must fit the library's scratch array (checked before any HIP call)
+    const size_t need = swa::decode_workspace_bytes(a, ca);
+    if (need > swa::decode_scratch_bytes()) return SWA_ERR_UNSUPPORTED;
+    if (c->num_seqs == 0) return SWA_OK;
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = swa::decode_scratch(&ws);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    const hipError_t e = swa::launch_decode_append(a, ca, q, k_new, v_new, q_pos, o, ws, need,
+                                                   static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return SWA_ERR_UNSUPPORTED;
+    return hip_status(e);
+}
+
 static bool aligned16(std::initializer_list<const void *> ptrs) {
     uintptr_t bits = 0;
     for (const void *x : ptrs) bits |= reinterpret_cast<uintptr_t>(x);

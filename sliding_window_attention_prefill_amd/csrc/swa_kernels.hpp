@@ -96,4 +96,9 @@ hipError_t launch_decode_append(const DecodeArgs &a, const CacheArgs &c, const v
                                 const void *k_new, const void *v_new, const int32_t *q_pos,
                                 void *o, void *ws, size_t ws_bytes, hipStream_t st);
 
+// The device scratch array for callers that cannot allocate: its size, and its address on
+// the current device (looked up once per device; *ptr is the address kernels may use).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void **ptr);
+
 }  // namespace swa

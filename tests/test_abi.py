@@ -286,3 +286,22 @@ def test_dilation_arguments(lib):
     # the workspace of the forward does not depend on the dilation
     assert lib.swa_prefill_workspace_bytes(ctypes.byref(_params(dilation=4))) == \
         lib.swa_prefill_workspace_bytes(ctypes.byref(_params()))
+
+
+def test_static_decode_rejects_problems_past_its_scratch(lib):
+    """swa_decode_append_static keeps the split partials in a 4 MiB array: a problem whose
+    partials need more (511 sequences, one kv head, eight query heads, d 128, a 1100-token
+    window: 511 x 2 ranges x 8 x 130 floats) is rejected before any launch; bad arguments
+    are rejected as in swa_decode_append."""
+    c = _cache(num_seqs=511, H_kv=1, w=1100, s=0, d=128, k_sink=None, v_sink=None)
+    p = swa.DecodeParams(8, 1, 0, 0.0, 0, None, None, 0)
+    need = lib.swa_decode_workspace_bytes(ctypes.byref(p), ctypes.byref(c))
+    assert need == 511 * 2 * 8 * 130 * 4 > 4 << 20
+    assert lib.swa_decode_append_static(ctypes.byref(p), ctypes.byref(c), DUMMY, DUMMY, DUMMY,
+                                        DUMMY, DUMMY, None) == 2
+    ok = _cache(num_seqs=2, H_kv=1, w=1100, s=0, d=128, k_sink=None, v_sink=None)
+    assert lib.swa_decode_append_static(ctypes.byref(p), ctypes.byref(ok), DUMMY, None, DUMMY,
+                                        DUMMY, DUMMY, None) == 1
+    p.mode = 7
+    assert lib.swa_decode_append_static(ctypes.byref(p), ctypes.byref(ok), DUMMY, DUMMY, DUMMY,
+                                        DUMMY, DUMMY, None) == 1
