@@ -16,9 +16,10 @@
 //     exact-attention kernels). Tiles inside every row's key set run without the element
 //     predicate.
 //   * Each wavefront computes S^T = K Q^T (32 keys x 32 queries per 32x32x16 matrix
-//     instruction), so a lane holds one query's scores; the scale and the bias fold into
-//     FMAs in base-2 units; sigmoid is 1 / (1 + 2^t), softmax is online with a lazily
-//     rescaled accumulator. O^T += V^T P^T takes the weights straight from registers.
+//     instruction), so a lane holds one query's scores; q enters scaled by scale x log2(e)
+//     (negated for sigmoid), so the product is a base-2 logit; sigmoid is 1 / (1 + 2^t),
+//     softmax is online with a lazily rescaled accumulator. O^T += V^T P^T takes the
+//     weights straight from registers.
 //   * Score operands are float16: q and k are widened from bf16, rotated in float32 and
 //     rounded once (inputs must stay within the float16 range, |x| < 65504).
 //   * A pre-pass rotates every key once into float16 tile images laid out exactly as LDS
@@ -501,10 +502,20 @@ __device__ __forceinline__ void qk_tile(const uint16_t *__restrict__ kl, const L
     else qk_tile_off<D, ALIBI>(kl, lo.k, bo, qreg, sacc);
 }
 
+// The largest of three floats in one v_max3_f32. Written as an instruction because the
+// compiler would otherwise first quiet each operand (one v_max per operand) when they come
+// straight from a matrix instruction; none of them is a signalling NaN here.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Scores of one tile made ready for weighting (run in the step that formed them): edge
 // masking (sigmoid scores are negated logits, so an excluded key gets +inf), and for
-// softmax the base-2 logits x log2(e) = cs * acc + bias_q (bias_q = slope log2(e) (i - j0),
-// zero without ALiBi) with the running maximum and the lazy rescale of the accumulator.
+// softmax the base-2 logits x log2(e) = acc + bias_q (the product of q scaled by cs; bias_q =
+// slope log2(e) (i - j0), zero without ALiBi) with the running maximum and the lazy rescale
+// of the accumulator.
 template <int D, int MODE, bool ALIBI, bool DIL>
 __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
                                             float &m_run, float &l_run, float cs, float bias_q,
@@ -517,20 +528,26 @@ __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc
     else if (kind == 1) mask_tile<false>(sacc, dq, jb, w, s, DIL ? dmask : 0, fill);
     else if (kind == 2) mask_tile<true>(sacc, dq, jb, w, s, DIL ? dmask : 0, fill);
     if (MODE == 1) {
-        // excluded keys stay -inf
+        // the product already is cs x (q.k) minus the bias's key part (q entered scaled by
+        // cs); the bias's query part is one add. Excluded keys stay -inf.
+        if (ALIBI) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                sacc[kb][e] = ALIBI ? fmaf(sacc[kb][e], cs, bias_q) : sacc[kb][e] * cs;
+                for (int e = 0; e < 16; ++e) sacc[kb][e] += bias_q;
+        }
+        // row maximum in three-operand steps, four independent chains (the scores come
+        // straight from the matrix unit; v_max3 takes them as they are)
         float mx[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            mx[u] = fmaxf(fmaxf(sacc[0][4 * u], sacc[0][4 * u + 1]), fmaxf(sacc[0][4 * u + 2], sacc[0][4 * u + 3]));
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            mx[u] = fmaxf(mx[u], fmaxf(fmaxf(sacc[1][4 * u], sacc[1][4 * u + 1]), fmaxf(sacc[1][4 * u + 2], sacc[1][4 * u + 3])));
-        float mt = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
+        for (int u = 0; u < 4; ++u) {
+            mx[u] = max3f(sacc[0][4 * u], sacc[0][4 * u + 1], sacc[0][4 * u + 2]);
+            mx[u] = max3f(mx[u], sacc[0][4 * u + 3], sacc[1][4 * u]);
+            mx[u] = max3f(mx[u], sacc[1][4 * u + 1], sacc[1][4 * u + 2]);
+        }
+        float mt = max3f(max3f(mx[0], mx[1], mx[2]), mx[3], sacc[1][3]);
+        mt = max3f(mt, sacc[1][7], sacc[1][11]);
+        mt = fmaxf(mt, sacc[1][15]);
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         const float m_new = fmaxf(m_run, mt);
         // keep the stale maximum while the new one exceeds it by less than 8 (weights stay
@@ -563,17 +580,15 @@ __device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const 
             for (int e = 0; e < 16; ++e)
                 sacc[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sacc[kb][e]));
     } else {
-        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(sacc[kb][e] - m_run);
-                ls[e & 3] += pe;
-                sacc[kb][e] = pe;
-            }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            for (int e = 0; e < 16; ++e) sacc[kb][e] = __builtin_amdgcn_exp2f(sacc[kb][e] - m_run);
     }
+    // softmax: the row sum takes the weights as the second product does (float16), two per
+    // instruction
+    float ls[2] = {0.0f, 0.0f};
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
     // O^T += V^T P^T. Step t covers keys 16t..16t+15; this lane's P^T elements are
     // sacc[t/2][8(t%2) + 0..7] = keys 16t + 4g + {0..3, 8..11}, and the two transposing reads
     // deliver V^T in exactly that key order.
@@ -586,6 +601,12 @@ __device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const 
             pk.y = pack_f16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
             pk.z = pack_f16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
             pk.w = pack_f16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
+            if (MODE == 1) {
+                ls[0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.x), ones, ls[0], false);
+                ls[1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.y), ones, ls[1], false);
+                ls[0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.z), ones, ls[0], false);
+                ls[1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.w), ones, ls[1], false);
+            }
         } else {
             pk.x = pack_bf16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
             pk.y = pack_bf16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
@@ -610,6 +631,7 @@ __device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const 
             }
         }
     }
+    if (MODE == 1) l_run += ls[0] + ls[1];
 }
 
 struct TileCtx {
@@ -861,22 +883,24 @@ void prefill_mfma_kernel(MfmaParams p) {
                 t1[ks] = trow[ks * 4 + g * 2 + 1];
             }
         }
-        const float qs = -p.cs;
+        // sigmoid: the negated base-2 logit, so q times -cs; softmax: the base-2 logit, q
+        // times cs
+        const float qs = MODE == 0 ? -p.cs : p.cs;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             uint4 x;
-            if (rope) x = MODE == 0 ? rotate_chunk_scaled(xq[ks], t0[ks], t1[ks], qs) : rotate_chunk(xq[ks], t0[ks], t1[ks]);
-            else x = MODE == 0 ? convert_chunk_scaled(xq[ks], qs) : convert_chunk(xq[ks]);
+            if (rope) x = rotate_chunk_scaled(xq[ks], t0[ks], t1[ks], qs);
+            else x = convert_chunk_scaled(xq[ks], qs);
             qreg[ks] = __builtin_bit_cast(f16x8_t, in ? x : make_uint4(0, 0, 0, 0));
         }
     }
 
-    // ALiBi bias in base-2 units. Softmax: the key part -(slope log2(e) / cs) kappa of the
-    // unscaled product; sigmoid: the whole bias of the negated logit, key part
+    // ALiBi bias in base-2 units. Softmax: the key part -slope log2(e) kappa (the query part
+    // is one add per score); sigmoid: the whole bias of the negated logit, key part
     // slope log2(e) kappa plus the query part
     if (ALIBI) cx.slope_l2 = slope * LOG2E;
     const BiasOperands bo = MODE == 0 ? bias_operands(ALIBI ? -cx.slope_l2 : 0.0f, lane, ALIBI)
-                                      : bias_operands(ALIBI ? cx.slope_l2 / p.cs : 0.0f, lane);
+                                      : bias_operands(ALIBI ? cx.slope_l2 : 0.0f, lane);
 
     f32x16_t oacc[DB];
 #pragma unroll
