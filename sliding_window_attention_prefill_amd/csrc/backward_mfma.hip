@@ -1053,9 +1053,13 @@ hipError_t launch_kernels(const BwdParams &bp, int n_dq, int n_dkv, int n_sink, 
         hipLaunchKernelGGL((bwd_dkv_kernel<D, MODE, ALIBI, false>), dim3((unsigned)n_dkv),
                            dim3(256), 0, st, bp);
     }
-    if (GP == 4)
-        hipLaunchKernelGGL((bwd_dq_kernel<D, 4, MODE, ALIBI>), dim3((unsigned)n_dq), dim3(256), 0, st, bp);
-    else if (GP == 2)
+    if constexpr (!(D == 128 && ALIBI)) {   // (the host never picks four heads there)
+        if (GP == 4) {
+            hipLaunchKernelGGL((bwd_dq_kernel<D, 4, MODE, ALIBI>), dim3((unsigned)n_dq), dim3(256), 0, st, bp);
+            return hipGetLastError();
+        }
+    }
+    if (GP == 2)
         hipLaunchKernelGGL((bwd_dq_kernel<D, 2, MODE, ALIBI>), dim3((unsigned)n_dq), dim3(256), 0, st, bp);
     else
         hipLaunchKernelGGL((bwd_dq_kernel<D, 1, MODE, ALIBI>), dim3((unsigned)n_dq), dim3(256), 0, st, bp);
@@ -1107,7 +1111,9 @@ hipError_t launch_bwd_d(const PrefillArgs &a, const BwdPlan &pl, const void *q, 
         hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, sink, n);
     }
     const int64_t G = a.Hq / a.Hkv;
-    const int GP = gp_of(G);
+    // four query heads per dq workgroup at d = 128 with ALiBi would keep more state than its
+    // registers hold (it spilled 19-24 registers to scratch): two heads per workgroup there
+    const int GP = (D == 128 && a.slopes != nullptr && gp_of(G) == 4) ? 2 : gp_of(G);
     const int64_t QP = 32 * 4 / GP;
     BwdParams bp = {};
     bp.kimg = kimg; bp.vimg = vimg; bp.qimg = qimg; bp.gimg = gimg; bp.stats = stats;

@@ -205,7 +205,9 @@ def test_chunk_invalid_sequences_get_nan_and_keep_their_cache():
 def test_chunk_full_size_sampled_rows():
     """A serving step at full size: 4 sequences, H_q 32 / H_kv 8, d 128, a 4096-token
     window (histories 0 .. 20000 tokens, chunks of 777 .. 2048 rows), softmax, RoPE
-    theta 1e6; sampled rows of every sequence against the oracle."""
+    theta 1e6; sampled rows of every sequence against the oracle, and the cache the call
+    leaves bit for bit against swa_kv_append of the same tokens (at H_kv 8, d 128 the append
+    spreads each 64-row tile over all eight of its workgroups)."""
     d, Hq, Hkv, w, s, theta = 128, 32, 8, 4096, 0, 1e6
     S = 4
     g = torch.Generator().manual_seed(2024)
@@ -215,11 +217,15 @@ def test_chunk_full_size_sampled_rows():
     cache = swa.SwaCache.empty(S, Hkv, w, s, d, torch.bfloat16)
     ring = oracle.Ring(S, Hkv, w, s, d)
     fill_history([cache], ring, hist, g, table, theta, tail_only=True)
+    twin = swa.SwaCache(cache.k_ring.clone(), cache.v_ring.clone())
     q, k, v, cu = packed_chunk(g, lens, Hq, Hkv, d)
     pos0 = torch.tensor(hist, dtype=torch.int32)
     out = swa.swa_prefill_chunk(q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV), pos0.to(DEV), cache,
                                 max_seqlen=max(lens), mode=wl.SOFTMAX, rope_table=table,
                                 out_dtype=torch.float32)
+    append_packed(twin, k, v, cu, pos0, table)
+    torch.cuda.synchronize()
+    assert_caches_equal(cache, twin)
     rows = []
     for q_ in range(S):
         a, n = int(cu[q_]), lens[q_]
