@@ -745,8 +745,10 @@ void bwd_dkv2_kernel(BwdParams p) {
     constexpr int DMA_R = T::IMG_BYTES / (NWG * 1024);   // 1 KB transfers per wavefront
     constexpr int STAGE = 2 * T::IMG + 256;              // Q tile, dO tile, 64 row statistics
     constexpr int PX = 4 * 2 * 64 * 16;                  // P: 4 key blocks x 2 row blocks x 64 lanes x 16
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE + PX];
-    uint16_t *const px = lds + 2 * STAGE;
+    // the dX role runs one step behind the P role: three stages (the P role's, the dX role's
+    // and the one being loaded) and two P buffers
+    __shared__ __attribute__((aligned(16))) uint16_t lds[3 * STAGE + 2 * PX];
+    uint16_t *const px0 = lds + 3 * STAGE;
 
     int b, hkv, kblk, split = 0;
     {
@@ -835,11 +837,19 @@ void bwd_dkv2_kernel(BwdParams p) {
 
     load(0, 0);
     __syncthreads();
-    for (int n = 0; n < n_steps; ++n) {
-        const int cur = n & 1;
-        if (n + 1 < n_steps) load(n + 1, cur ^ 1);
-        const int qt = t_lo + n / (int)p.G;
-        const int64_t hq = (int64_t)hkv * p.G + n % (int)p.G;
+    // iteration n: the P role forms and publishes P of step n and adds dV; the dX role takes
+    // step n - 1, whose P was published before the last barrier; stage n + 1 loads meanwhile.
+    // One barrier per iteration: it publishes P(n) and frees stage n - 1 and P buffer n - 1.
+    for (int n = 0; n <= n_steps; ++n) {
+        if (n + 1 < n_steps) load(n + 1, (n + 1) % 3);
+        const int my = role_p ? n : n - 1;   // the step this wavefront works on
+        if (my < 0 || my >= n_steps) {
+            __syncthreads();
+            continue;
+        }
+        const int cur = my % 3;
+        const int qt = t_lo + my / (int)p.G;
+        const int64_t hq = (int64_t)hkv * p.G + my % (int)p.G;
         const int i0 = qt * BK;
         const int ilo = i0 > qlo ? i0 : qlo, ihi = (i0 + BK < qhi ? i0 + BK : qhi) - 1;
         const bool any = active && ilo <= ihi && ihi >= jw &&
@@ -850,7 +860,7 @@ void bwd_dkv2_kernel(BwdParams p) {
         const uint16_t *gl = ql + T::IMG;
         const float *stl = reinterpret_cast<const float *>(ql + 2 * T::IMG);
         // this lane's P of row block qb: values 0..7 at pxw + qb * 1024, 8..15 at + 512
-        uint16_t *pxw = px + (kw * 2) * 64 * 16 + lane * 8;
+        uint16_t *pxw = px0 + (my & 1) * PX + (kw * 2) * 64 * 16 + lane * 8;
         f32x16_t sd[2];                                       // P (P role) or dP (dX role)
         if (any) {
             const float slope_l2 = ALIBI ? p.slopes[hq] * LOG2E : 0.0f;
@@ -910,7 +920,6 @@ void bwd_dkv2_kernel(BwdParams p) {
                 }
             }
         }
-        __syncthreads();   // P of every key block published
         if (any) {
             if (role_p) {
                 acc_tr<D>(gl, 0, toff, sd[0], acc);   // dV^T += dO^T P
