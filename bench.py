@@ -50,6 +50,8 @@ METRIC = "SWA prefill in-window TFLOP/s (% MFMA peak); decode tok/s (% HBM BW)"
 KERNEL_SRC = os.path.join(ROOT, "sliding_window_attention_prefill_amd", "csrc", "prefill_mfma.hip")
 SETTLE_S = 0.2   # untimed steady load before the timed prefill steps (clock ramp-up)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "sliding_window_attention_prefill_amd", "csrc", "decode.hip")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
 def in_window_keys(N: int, w: int, s: int) -> int:
@@ -71,20 +73,22 @@ def prefill_bytes(cfg, out_bytes: int) -> float:
     return float(q * el + 2 * kv * el + q * out_bytes)
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(workload: str, out_dtype: str):
-    """HBM bytes per launch of one prefill call (pre-pass + main kernel) from the committed
-    counter profile, if it was taken on the current kernel source."""
+def stored_traffic(workload: str, out_dtype: str, path: str = TRAFFIC_FILE,
+                   src: str = KERNEL_SRC):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) from a committed
+    counter profile, if it was taken on the current kernel source: one prefill call
+    (pre-pass + main kernel), or one fused append + decode launch."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash():
+    if t.get("kernel_sha256_16") != kernel_hash(src):
         return None
     e = t.get("workloads", {}).get("%s/%s" % (workload, out_dtype))
     return None if e is None else e.get("hbm_bytes_per_launch")
@@ -210,6 +214,10 @@ def bench_decode(cfg, out_dtype, copies=1):
         "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "cache_copies": copies,
         "cache_mb": round(copies * cache_bytes / 1e6, 1),
+        # counters see the eager launches of the same rotation (graph replays are not
+        # counted), so the bytes stand for the HBM-resident case only
+        "traffic": (stored_traffic(cfg.name, "f32" if out_dtype == torch.float32 else "bf16",
+                                   DECODE_TRAFFIC_FILE, DECODE_SRC) if copies > 1 else None),
         "note": ("cache (%.0f MB) %s the 256 MB last-level cache" % (
                      cache_bytes / 1e6, "fits in" if cache_bytes < 200e6 else "outgrows")
                  if copies == 1 else "%d cache copies in rotation: rings are read from HBM"
@@ -419,6 +427,10 @@ def main():
     ap.add_argument("--no-elementwise", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=8192,
                     help="query rows of sequence 0 the CPU baseline computes")
+    ap.add_argument("--profile-decode-cold", type=int, default=0, metavar="STEPS",
+                    help="only run STEPS fused append + decode launches of the SWA(64, 4) "
+                         "workload eagerly over 18 cache copies in rotation (for byte "
+                         "counters, which see eager launches), then exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB mebibytes three times (the "
                          "known-size kernel that scales the HBM byte counters), then exit")
@@ -440,6 +452,25 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
+
+    if args.profile_decode_cold:
+        import sliding_window_attention_prefill_amd as swa
+        c = wl.C4
+        st = wl.decode_inputs(c, device="cuda", steps=1)
+        copies = 18
+        caches = [swa.SwaCache(st.k_ring.clone(), st.v_ring.clone(), st.k_sink.clone(),
+                               st.v_sink.clone()) for _ in range(copies)]
+        table = swa.swa_rope_table(c.len_hi + args.profile_decode_cold + 1, c.d, c.rope_theta)
+        out = torch.empty((c.num_seqs, c.H_q, c.d), dtype=torch.float32, device="cuda")
+        kn, vn = st.k_steps[0, :, 0].contiguous(), st.v_steps[0, :, 0].contiguous()
+        for t in range(args.profile_decode_cold):
+            pos = (st.lengths + t).to(torch.int32)
+            swa.swa_decode_append(st.q_steps[0], kn, vn, pos, caches[t % copies], mode=c.mode,
+                                  rope_table=table, out=out)
+        torch.cuda.synchronize()
+        print(json.dumps({"decode_cold_eager_steps": args.profile_decode_cold,
+                          "cache_copies": copies}), flush=True)
         return
 
     cfgs = {"c2": wl.C2, "c3": wl.C3, "c5": wl.C5}
