@@ -110,6 +110,30 @@ __device__ __forceinline__ void dma_rounds(uint16_t *__restrict__ dst, __amdgpu_
             r, (lds_void_t *)(dst + (wave * ROUNDS + i) * 512), 16, base + off[i], 0, 0, 0);
 }
 
+// The same transfers when round i reads at off + i * stride: one offset register per lane.
+// A stride of 1 KB (consecutive kilobytes of a tile image) rides in the instruction's
+// immediate offset, which moves the LDS destination by the same amount, so every round
+// names the wavefront's first kilobyte; other strides are added per round.
+template <int ROUNDS>
+__device__ __forceinline__ void dma_rounds_strided(uint16_t *__restrict__ dst,
+                                                   __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   uint32_t stride, int wave) {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (lds_void_t *)(dst + (wave * ROUNDS + i) * 512), 16, off + i * stride, 0, 0, 0);
+}
+template <int ROUNDS>
+__device__ __forceinline__ void dma_rounds_kb(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t r,
+                                              uint32_t off, int wave) {
+    static_assert(ROUNDS >= 1 && ROUNDS <= 4, "the immediate offset holds at most 4095 bytes");
+    lds_void_t *const d = (lds_void_t *)(dst + wave * ROUNDS * 512);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 0, 0);
+    if constexpr (ROUNDS > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 1024, 0);
+    if constexpr (ROUNDS > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 2048, 0);
+    if constexpr (ROUNDS > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, off, 0, 3072, 0);
+}
+
 // Key offset (from j0 + 4g) of accumulator element e of score block kb.
 __device__ __forceinline__ constexpr int key_of(int kb, int e) {
     return kb * 32 + 8 * (e >> 2) + (e & 3);
@@ -131,6 +155,31 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
             bool ok = ((unsigned)dij < (unsigned)w) & ((dij & dmask) == 0);   // 0 <= i - j < w
             if (SINKS) ok = ok | ((dij >= 0) & (jb + key_of(kb, e) < s));
             sacc[kb][e] = ok ? sacc[kb][e] : fill;
+        }
+}
+
+// x = keep ? x : fill, written in x's own register (an instruction with the result tied to
+// its input), so that a conditionally masked accumulator needs no copy where the masked and
+// the unmasked paths meet.
+__device__ __forceinline__ float keep_or_fill(float x, bool keep, float fill) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+    asm("v_cndmask_b32_e64 %0, %1, %0, %2" : "+v"(x) : "v"(fill), "s"(m));
+    return x;
+}
+
+// mask_tile in place; with all_out every key is excluded (a tile that meets none of this
+// wavefront's key sets).
+template <bool SINKS>
+__device__ __forceinline__ void mask_tile_inplace(f32x16_t (&sacc)[2], int dq, int jb, int w,
+                                                  int s, int dmask, float fill, bool all_out) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int dij = dq - key_of(kb, e);
+            bool ok = ((unsigned)dij < (unsigned)w) & ((dij & dmask) == 0);
+            if (SINKS) ok = ok | ((dij >= 0) & (jb + key_of(kb, e) < s));
+            sacc[kb][e] = keep_or_fill(sacc[kb][e], ok & !all_out, fill);
         }
 }
 
@@ -212,12 +261,12 @@ __device__ __forceinline__ f16x8_t query_term(const BiasOperands &bo, int u) {
 template <int D, bool ALIBI>
 __device__ __forceinline__ void qk_tile_off(const uint16_t *__restrict__ kl, const int (&koff)[D / 16],
                                             const BiasOperands &bo, const f16x8_t &bb,
-                                            const f16x8_t (&qreg)[D / 16], f32x16_t (&sacc)[2]) {
+                                            const f16x8_t (&qreg)[D / 16], const f32x16_t &init,
+                                            f32x16_t (&sacc)[2]) {
     constexpr int KS = D / 16;
-    const f32x16_t zero = {};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-        sacc[kb] = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bb, zero, 0, 0, 0) : zero;
+        sacc[kb] = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bb, init, 0, 0, 0) : init;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -225,6 +274,14 @@ __device__ __forceinline__ void qk_tile_off(const uint16_t *__restrict__ kl, con
             const f16x8_t a = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + koff[ks]);
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sacc[kb], 0, 0, 0);
         }
+}
+
+template <int D, bool ALIBI>
+__device__ __forceinline__ void qk_tile_off(const uint16_t *__restrict__ kl, const int (&koff)[D / 16],
+                                            const BiasOperands &bo, const f16x8_t &bb,
+                                            const f16x8_t (&qreg)[D / 16], f32x16_t (&sacc)[2]) {
+    const f32x16_t zero = {};
+    qk_tile_off<D, ALIBI>(kl, koff, bo, bb, qreg, zero, sacc);
 }
 
 template <int D, bool ALIBI>

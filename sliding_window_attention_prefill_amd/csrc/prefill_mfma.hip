@@ -481,15 +481,10 @@ struct LaneOffsets {
     int k[D / 16];                   // LDS element offset of the K row read of score step ks
     int v[D / 32];                   // LDS element offset of the V transposing read, block db
     int vt[4];                       // LDS element offset of the V^T read of step t (block 0)
-    uint32_t dimg[Tile<D>::DMA_W];   // source byte offset in a packed tile image, per transfer
-    uint32_t dvraw[Tile<D>::DMA_W];  // source byte offset in the V input rows, per transfer
+    uint32_t dimg;    // source byte offset of the first transfer in a packed tile image
+    uint32_t dvraw;   // source byte offset of the first transfer in the V input rows
+    uint32_t dvstep;  // bytes between the V input rows of consecutive transfers
 };
-
-template <int D>
-__device__ __forceinline__ void dma_tile(uint16_t *__restrict__ dst, __amdgpu_buffer_rsrc_t r,
-                                         uint32_t base, const uint32_t *off, int wave) {
-    dma_rounds<Tile<D>::DMA_W>(dst, r, base, off, wave);
-}
 
 // S^T = K Q^T for the 64 keys of one tile at j0 (i: this lane's query). For sigmoid the
 // product is the negated base-2 logit t = -x log2(e) itself: q enters scaled by -cs and
@@ -511,6 +506,42 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return r;
 }
 
+// Softmax: the largest base-2 logit of one tile for this lane's query (both lane halves).
+// Three-operand steps in four independent chains; the scores come straight from the matrix
+// unit and v_max3 takes them as they are.
+__device__ __forceinline__ float tile_max(const f32x16_t (&sacc)[2]) {
+    float mx[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        mx[u] = max3f(sacc[0][4 * u], sacc[0][4 * u + 1], sacc[0][4 * u + 2]);
+        mx[u] = max3f(mx[u], sacc[0][4 * u + 3], sacc[1][4 * u]);
+        mx[u] = max3f(mx[u], sacc[1][4 * u + 1], sacc[1][4 * u + 2]);
+    }
+    float mt = max3f(max3f(mx[0], mx[1], mx[2]), mx[3], sacc[1][3]);
+    mt = max3f(mt, sacc[1][7], sacc[1][11]);
+    mt = fmaxf(mt, sacc[1][15]);
+    return fmaxf(mt, __shfl_xor(mt, 32, 64));
+}
+
+// Softmax: fold a tile maximum into the running one. The stale maximum stays while the new
+// one exceeds it by less than 8 (weights stay below 2^8); the final division uses the same
+// maximum.
+template <int D>
+__device__ __forceinline__ void fold_max(float mt, f32x16_t (&oacc)[D / 32], float &m_run,
+                                         float &l_run) {
+    const float m_new = fmaxf(m_run, mt);
+    const bool need = m_new > m_run + 8.0f;
+    if (__any(need)) {
+        const float corr = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
+        l_run *= corr;
+        m_run = need ? m_new : m_run;
+    }
+}
+
 // Scores of one tile made ready for weighting (run in the step that formed them): edge
 // masking (sigmoid scores are negated logits, so an excluded key gets +inf), and for
 // softmax the base-2 logits x log2(e) = acc + bias_q (the product of q scaled by cs; bias_q =
@@ -520,7 +551,6 @@ template <int D, int MODE, bool ALIBI, bool DIL>
 __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
                                             float &m_run, float &l_run, float cs, float bias_q,
                                             int kind, int dq, int jb, int w, int s, int dmask) {
-    constexpr int DB = D / 32;
     // the stride test exists only in the dilated instantiations
     constexpr float fill = MODE == 0 ? INFINITY : -INFINITY;
     if (D == 64 && kind == 3) mask_causal(sacc, dq, fill);
@@ -536,41 +566,17 @@ __device__ __forceinline__ void prep_scores(f32x16_t (&sacc)[2], f32x16_t (&oacc
 #pragma unroll
                 for (int e = 0; e < 16; ++e) sacc[kb][e] += bias_q;
         }
-        // row maximum in three-operand steps, four independent chains (the scores come
-        // straight from the matrix unit; v_max3 takes them as they are)
-        float mx[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            mx[u] = max3f(sacc[0][4 * u], sacc[0][4 * u + 1], sacc[0][4 * u + 2]);
-            mx[u] = max3f(mx[u], sacc[0][4 * u + 3], sacc[1][4 * u]);
-            mx[u] = max3f(mx[u], sacc[1][4 * u + 1], sacc[1][4 * u + 2]);
-        }
-        float mt = max3f(max3f(mx[0], mx[1], mx[2]), mx[3], sacc[1][3]);
-        mt = max3f(mt, sacc[1][7], sacc[1][11]);
-        mt = fmaxf(mt, sacc[1][15]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-        const float m_new = fmaxf(m_run, mt);
-        // keep the stale maximum while the new one exceeds it by less than 8 (weights stay
-        // below 2^8); the final division uses the same maximum.
-        const bool need = m_new > m_run + 8.0f;
-        if (__any(need)) {
-            const float corr = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= corr;
-            l_run *= corr;
-            m_run = need ? m_new : m_run;
-        }
+        fold_max<D>(tile_max(sacc), oacc, m_run, l_run);
     }
 }
 
-// Weights of one prepared tile, then O^T += V^T P^T.
-template <int D, int MODE, bool VF16>
-__device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const LaneOffsets<D> &lo,
-                                         f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
-                                         float m_run, float &l_run) {
-    constexpr int DB = D / 32;
+// Weights of one prepared tile, packed as the B operand of the second product (step t =
+// keys 16t..16t+15: this lane's P^T elements are sacc[t/2][8(t%2) + 0..7] = keys
+// 16t + 4g + {0..3, 8..11}); for softmax the row sum, taken from the packed weights as the
+// second product sees them (float16), two per instruction.
+template <int MODE, bool VF16>
+__device__ __forceinline__ void tile_weights(f32x16_t (&sacc)[2], float m_run, float &l_run,
+                                             uint4 (&pk)[4]) {
     if (MODE == 0) {
         // sigma(x) = 1 / (1 + 2^t); the scores already are t = -x log2(e) (an excluded key
         // has t = +inf -> 0)
@@ -585,41 +591,46 @@ __device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const 
 #pragma unroll
             for (int e = 0; e < 16; ++e) sacc[kb][e] = __builtin_amdgcn_exp2f(sacc[kb][e] - m_run);
     }
-    // softmax: the row sum takes the weights as the second product does (float16), two per
-    // instruction
     float ls[2] = {0.0f, 0.0f};
     const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-    // O^T += V^T P^T. Step t covers keys 16t..16t+15; this lane's P^T elements are
-    // sacc[t/2][8(t%2) + 0..7] = keys 16t + 4g + {0..3, 8..11}, and the two transposing reads
-    // deliver V^T in exactly that key order.
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int kb = t >> 1, e0 = 8 * (t & 1);
-        uint4 pk;
         if (VF16) {
-            pk.x = pack_f16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
-            pk.y = pack_f16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
-            pk.z = pack_f16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
-            pk.w = pack_f16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
+            pk[t].x = pack_f16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
+            pk[t].y = pack_f16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
+            pk[t].z = pack_f16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
+            pk[t].w = pack_f16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
             if (MODE == 1) {
-                ls[0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.x), ones, ls[0], false);
-                ls[1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.y), ones, ls[1], false);
-                ls[0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.z), ones, ls[0], false);
-                ls[1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk.w), ones, ls[1], false);
+                ls[0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[t].x), ones, ls[0], false);
+                ls[1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[t].y), ones, ls[1], false);
+                ls[0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[t].z), ones, ls[0], false);
+                ls[1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[t].w), ones, ls[1], false);
             }
         } else {
-            pk.x = pack_bf16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
-            pk.y = pack_bf16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
-            pk.z = pack_bf16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
-            pk.w = pack_bf16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
+            pk[t].x = pack_bf16x2(sacc[kb][e0 + 0], sacc[kb][e0 + 1]);
+            pk[t].y = pack_bf16x2(sacc[kb][e0 + 2], sacc[kb][e0 + 3]);
+            pk[t].z = pack_bf16x2(sacc[kb][e0 + 4], sacc[kb][e0 + 5]);
+            pk[t].w = pack_bf16x2(sacc[kb][e0 + 6], sacc[kb][e0 + 7]);
         }
+    }
+    if (MODE == 1) l_run += ls[0] + ls[1];
+}
+
+// O^T += V^T P^T with the packed weights of one tile: the two transposing reads (bf16 V rows)
+// or the one 16-byte read (float16 V^T image) deliver V^T in the key order of the weights.
+template <int D, bool VF16>
+__device__ __forceinline__ void tile_pv(const uint16_t *__restrict__ vl, const LaneOffsets<D> &lo,
+                                        const uint4 (&pk)[4], f32x16_t (&oacc)[D / 32]) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
             if constexpr (VF16) {
                 // V^T rows 32 db .. 32 db + 31 of the transposed tile: one 16-byte read
                 const f16x8_t a = *reinterpret_cast<const f16x8_t *>(vl + 32 * db * BK + lo.vt[t]);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    a, __builtin_bit_cast(f16x8_t, pk), oacc[db], 0, 0, 0);
+                    a, __builtin_bit_cast(f16x8_t, pk[t]), oacc[db], 0, 0, 0);
             } else {
                 const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4_t *)(vl + 16 * t * D + lo.v[db]));
@@ -627,11 +638,20 @@ __device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const 
                     (lds_s16x4_t *)(vl + (16 * t + 8) * D + lo.v[db]));
                 const s16x8_t a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8_t, a8), __builtin_bit_cast(bf16x8_t, pk), oacc[db], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8_t, a8), __builtin_bit_cast(bf16x8_t, pk[t]), oacc[db], 0, 0, 0);
             }
         }
     }
-    if (MODE == 1) l_run += ls[0] + ls[1];
+}
+
+// Weights of one prepared tile, then O^T += V^T P^T.
+template <int D, int MODE, bool VF16>
+__device__ __forceinline__ void weigh_pv(const uint16_t *__restrict__ vl, const LaneOffsets<D> &lo,
+                                         f32x16_t (&sacc)[2], f32x16_t (&oacc)[D / 32],
+                                         float m_run, float &l_run) {
+    uint4 pk[4];
+    tile_weights<MODE, VF16>(sacc, m_run, l_run, pk);
+    tile_pv<D, VF16>(vl, lo, pk, oacc);
 }
 
 struct TileCtx {
@@ -672,20 +692,45 @@ struct TileCtx {
 template <int D>
 __device__ __forceinline__ void load_k(uint16_t *__restrict__ dst, const TileCtx &cx,
                                        const LaneOffsets<D> &lo, int j0) {
-    dma_tile<D>(dst, cx.rk, cx.img_of(j0) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
+    dma_rounds_kb<Tile<D>::DMA_W>(dst, cx.rk, cx.img_of(j0) * Tile<D>::IMG_BYTES + lo.dimg, cx.wave);
 }
 template <int D, bool VF16>
 __device__ __forceinline__ void load_v(uint16_t *__restrict__ dst, const TileCtx &cx,
                                        const LaneOffsets<D> &lo, int j0) {
-    if (VF16) dma_tile<D>(dst, cx.rv, cx.img_of(j0) * Tile<D>::IMG_BYTES, lo.dimg, cx.wave);
-    else dma_tile<D>(dst, cx.rv, cx.img_of(j0) * cx.vtile_bytes, lo.dvraw, cx.wave);
+    if (VF16)
+        dma_rounds_kb<Tile<D>::DMA_W>(dst, cx.rv, cx.img_of(j0) * Tile<D>::IMG_BYTES + lo.dimg, cx.wave);
+    else
+        dma_rounds_strided<Tile<D>::DMA_W>(dst, cx.rv, cx.img_of(j0) * cx.vtile_bytes + lo.dvraw,
+                                           lo.dvstep, cx.wave);
 }
 
-// Step t of the software pipeline. On entry s_cur holds the prepared scores of tile t, K
-// buffer k_next holds tile t + 1 and V buffer v_cur tile t. The step starts the transfers of
-// K tile t + 2 (into k_fill, free since tile t's scores were formed) and V tile t + 1 (into
-// v_fill, free since tile t - 1's product), forms the scores of tile t + 1 while it weighs
-// tile t, and prepares tile t + 1's scores.
+// Edge masking of a freshly formed tile at j, in place (the masked scores stay in the
+// registers of the unmasked ones, so the rare masked path costs the common one no copies).
+// kind < 0 (no tile, or one that meets none of this wavefront's key sets) excludes every
+// key, so that weighing the tile adds nothing.
+template <int D, int MODE, bool DIL>
+__device__ __forceinline__ void mask_scores(f32x16_t (&sacc)[2], const TileCtx &cx, int j,
+                                            int kind) {
+    constexpr float fill = MODE == 0 ? INFINITY : -INFINITY;
+    if (kind != 0) {
+        const int dq = cx.i - j - 4 * cx.g, jb = j + 4 * cx.g;
+        if (kind == 2)
+            mask_tile_inplace<true>(sacc, dq, jb, cx.w, cx.s, DIL ? cx.dmask : 0, fill, false);
+        else
+            mask_tile_inplace<false>(sacc, dq, jb, cx.w, cx.s, DIL ? cx.dmask : 0, fill, kind < 0);
+    }
+}
+
+// Step t of the software pipeline (d = 128). On entry s_cur holds the prepared scores of
+// tile t, K buffer k_next holds tile t + 1 and V buffer v_cur tile t. The step starts the
+// transfers of K tile t + 2 (into k_fill, free since tile t's scores were formed) and V tile
+// t + 1 (into v_fill, free since tile t - 1's product), forms the scores of tile t + 1 while
+// it weighs tile t, and prepares tile t + 1's scores. The scores of tile t + 1 are formed
+// whether or not that tile exists or meets this wavefront's queries (one definition keeps
+// them in place across the steps); unused, they are never weighed (sigmoid) or are masked out
+// whole (softmax). Softmax masks tile t + 1 in place right after forming it (edge tiles only)
+// and takes its maximum after tile t's product; sigmoid weighs tile t first. Each order
+// measured faster for its mode.
 // The four buffers are distinct restrict pointers, so no LDS read here waits for the
 // transfers this step starts.
 template <int D, int MODE, bool ALIBI, bool VF16, bool DIL>
@@ -699,16 +744,41 @@ __device__ __forceinline__ void pipe_step(uint16_t *__restrict__ k_fill,
                                           float &m_run, float &l_run, int t) {
     const bool has1 = t + 1 < cx.n_tiles;
     if (t + 2 < cx.n_tiles) load_k<D>(k_fill, cx, lo, cx.j0_of(t + 2));
-    const int j0 = cx.j0_of(t), j1 = cx.j0_of(t + 1);
+    const int j1 = cx.j0_of(t + 1);
     if (has1) load_v<D, VF16>(v_fill, cx, lo, j1);
-    const int kind0 = cx.template kind_of<D == 64>(j0);
-    const int kind1 = has1 ? cx.template kind_of<D == 64>(j1) : -1;
-    if (kind1 >= 0) qk_tile<D, MODE, ALIBI>(k_next, lo, bo, qreg, s_next, cx.i, j1);
-    if (kind0 >= 0) weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run);
-    if (kind1 >= 0)
-        prep_scores<D, MODE, ALIBI, DIL>(s_next, oacc, m_run, l_run, cx.cs,
-                                    cx.slope_l2 * (float)(cx.i - j1), kind1,
-                                    cx.i - j1 - 4 * cx.g, j1 + 4 * cx.g, cx.w, cx.s, cx.dmask);
+    const int kind1 = has1 ? cx.template kind_of<false>(j1) : -1;
+    qk_tile<D, MODE, ALIBI>(k_next, lo, bo, qreg, s_next, cx.i, j1);
+    {
+        // K rows read four products ahead of their use (the compiler's own order issues each
+        // pair of reads right before its products)
+        constexpr int NR = 2 * (D / 16), AH = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // LDS reads
+#pragma unroll
+        for (int u = 0; u < NR - AH; ++u) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+    }
+    if constexpr (MODE == 0) {
+        if (cx.template kind_of<false>(cx.j0_of(t)) >= 0)
+            weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run);
+        if (kind1 >= 0)
+            prep_scores<D, MODE, ALIBI, DIL>(s_next, oacc, m_run, l_run, cx.cs, 0.0f, kind1,
+                                             cx.i - j1 - 4 * cx.g, j1 + 4 * cx.g, cx.w, cx.s,
+                                             cx.dmask);
+    } else {
+        mask_scores<D, MODE, DIL>(s_next, cx, j1, kind1);
+        weigh_pv<D, MODE, VF16>(v_cur, lo, s_cur, oacc, m_run, l_run);
+        if (ALIBI) {
+            const float bq = cx.slope_l2 * (float)(cx.i - j1);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s_next[kb][e] += bq;
+        }
+        fold_max<D>(tile_max(s_next), oacc, m_run, l_run);
+    }
 }
 
 // Step t without pipelining: start the transfers of tile t + 1 (K and V) into the other
@@ -823,7 +893,8 @@ void prefill_mfma_kernel(MfmaParams p) {
         cx.row_bytes = p.row_bytes;
         cx.ns_img = ns_img; cx.shift = shift;
         cx.vtile_bytes = p.chunked ? (uint32_t)T::IMG_BYTES : (uint32_t)BK * p.row_bytes;
-        cx.tid = tid; cx.wave = wave; cx.qa = qa; cx.qb = qa + 31 < N ? qa + 31 : N - 1;
+        // the wavefront index is uniform: keep it (and the LDS addresses of the transfers) scalar
+        cx.tid = tid; cx.wave = __builtin_amdgcn_readfirstlane(wave); cx.qa = qa; cx.qb = qa + 31 < N ? qa + 31 : N - 1;
         cx.i = i; cx.g = g; cx.w = p.w; cx.s = p.s; cx.N = N; cx.dmask = p.dmask;
         cx.n_tiles = ts_end + (tw_end - tw_begin + 1);
         cx.ts_end = ts_end; cx.tw_begin = tw_begin;
@@ -847,12 +918,17 @@ void prefill_mfma_kernel(MfmaParams p) {
     // 32 db + qc equals that of row qc)
 #pragma unroll
     for (int t = 0; t < 4; ++t) lo.vt[t] = vt_slot(qc, 2 * t + g);
-#pragma unroll
-    for (int r = 0; r < T::DMA_W; ++r) {
-        const int slot = (wave * T::DMA_W + r) * 64 + lane;  // 16-byte slot of the tile image
+    {
+        // transfer r of this wavefront fills the 16-byte slots (wave DMA_W + r) 64 + lane of
+        // the tile image: 512 / D rows per transfer, and the swizzle of a lane's row does not
+        // depend on r (it takes only row bits below 512 / D)
+        const uint32_t vrow = p.chunked ? (uint32_t)(2 * D) : p.row_bytes;
+        const int slot = wave * T::DMA_W * 64 + lane;
         const int row = slot / T::C, c = (slot % T::C) ^ vswz<D>(row);
-        lo.dimg[r] = (uint32_t)slot * 16;
-        lo.dvraw[r] = (uint32_t)row * (p.chunked ? (uint32_t)(2 * D) : p.row_bytes) + c * 16;
+        static_assert(vswz<D>(512 / D) == 0 && vswz<D>(2 * (512 / D)) == 0, "swizzle period");
+        lo.dimg = (uint32_t)slot * 16;
+        lo.dvraw = (uint32_t)row * vrow + c * 16;
+        lo.dvstep = (uint32_t)(512 / D) * vrow;
     }
 
     // ---- first transfers: K tile 0 (and 1 when pipelined) and V tile 0, in flight while the
@@ -914,12 +990,23 @@ void prefill_mfma_kernel(MfmaParams p) {
         f32x16_t sa[2], sb[2];
         __syncthreads();
         {
-            const int j0 = cx.j0_of(0), kind0 = cx.template kind_of<D == 64>(j0);
-            if (kind0 >= 0) {
-                qk_tile<D, MODE, ALIBI>(kbuf0, lo, bo, qreg, sa, i, j0);
-                prep_scores<D, MODE, ALIBI, DIL>(sa, oacc, m_run, l_run, cx.cs,
-                                            cx.slope_l2 * (float)(i - j0), kind0, i - j0 - 4 * g,
-                                            j0 + 4 * g, cx.w, cx.s, cx.dmask);
+            const int j0 = cx.j0_of(0), kind0 = cx.template kind_of<false>(j0);
+            qk_tile<D, MODE, ALIBI>(kbuf0, lo, bo, qreg, sa, i, j0);
+            if (MODE == 0) {
+                if (kind0 >= 0)
+                    prep_scores<D, MODE, ALIBI, DIL>(sa, oacc, m_run, l_run, cx.cs, 0.0f, kind0,
+                                                     i - j0 - 4 * g, j0 + 4 * g, cx.w, cx.s,
+                                                     cx.dmask);
+            } else {
+                mask_scores<D, MODE, DIL>(sa, cx, j0, kind0);
+                if (ALIBI) {
+                    const float bq = cx.slope_l2 * (float)(i - j0);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) sa[kb][e] += bq;
+                }
+                fold_max<D>(tile_max(sa), oacc, m_run, l_run);
             }
         }
         __syncthreads();
@@ -927,11 +1014,11 @@ void prefill_mfma_kernel(MfmaParams p) {
         // ---- tile t lives in K/V buffer t % 2; two steps per trip keep the score registers
         for (int t = 0; t < cx.n_tiles; t += 2) {
             pipe_step<D, MODE, ALIBI, VF16, DIL>(kbuf0, vbuf1, kbuf1, vbuf0, cx, lo, bo, qreg, sa, sb,
-                                            oacc, m_run, l_run, t);
+                                                 oacc, m_run, l_run, t);
             __syncthreads();
             if (t + 1 >= cx.n_tiles) break;
             pipe_step<D, MODE, ALIBI, VF16, DIL>(kbuf1, vbuf0, kbuf0, vbuf1, cx, lo, bo, qreg, sb, sa,
-                                            oacc, m_run, l_run, t + 1);
+                                                 oacc, m_run, l_run, t + 1);
             __syncthreads();
         }
     } else {
@@ -1111,8 +1198,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
                                        : launch_pack<128>(pp, npb, a.rope != nullptr, pl.vf16, st);
         if (e != hipSuccess) return e;
     }
-    const int nb = (int)(a.B * a.Hkv * mp.n_hgroups * mp.n_qtiles);
     const bool alibi = a.slopes != nullptr;
+    const int nb = (int)(a.B * a.Hkv * mp.n_hgroups * mp.n_qtiles);
     if (a.d == 64) {
         if (GP == 4) return launch_gp<64, 4>(mp, nb, a.mode, alibi, st);
         if (GP == 2) return launch_gp<64, 2>(mp, nb, a.mode, alibi, st);
