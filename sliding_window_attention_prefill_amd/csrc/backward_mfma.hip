@@ -601,8 +601,10 @@ void bwd_dkv_kernel(BwdParams p) {
         const int ilo = i0 > qlo ? i0 : qlo, ihi = (i0 + BK < qhi ? i0 + BK : qhi) - 1;
         const bool any = active && ilo <= ihi && ihi >= jw &&
                          ((ilo - (jw + 31) < p.w) || jw < p.s);
-        const bool all = ilo == i0 && ihi == i0 + BK - 1 && i0 >= jw + 31 &&
-                         ((i0 + BK - 1 - jw < p.w) || jw + 31 < p.s) && jw + 31 < N;
+        // uniform by construction; read back as a scalar so that the per-element masking below
+        // branches once per step, not per element under an execution mask
+        const bool all = __builtin_amdgcn_readfirstlane((int)(ilo == i0 && ihi == i0 + BK - 1 && i0 >= jw + 31 &&
+                             ((i0 + BK - 1 - jw < p.w) || jw + 31 < p.s) && jw + 31 < N)) != 0;
         if (any) {
             const uint16_t *ql = lds + cur * STAGE;
             const uint16_t *gl = ql + T::IMG;
@@ -644,8 +646,8 @@ void bwd_dkv_kernel(BwdParams p) {
                         float x = sacc[e];
                         if (!all) {
                             const int dij = iq - j;
-                            const bool ok = iq >= qlo && iq < qhi && iq < N && j < N && dij >= 0 &&
-                                            (dij < p.w || j < p.s);
+                            const bool ok = (iq >= qlo) & (iq < qhi) & (iq < N) & (j < N) & (dij >= 0) &
+                                            ((dij < p.w) | (j < p.s));
                             x = ok ? x : (MODE == 0 ? INFINITY : -INFINITY);
                         }
                         float pe, dxe;
@@ -854,8 +856,10 @@ void bwd_dkv2_kernel(BwdParams p) {
         const int ilo = i0 > qlo ? i0 : qlo, ihi = (i0 + BK < qhi ? i0 + BK : qhi) - 1;
         const bool any = active && ilo <= ihi && ihi >= jw &&
                          ((ilo - (jw + 31) < p.w) || jw < p.s);
-        const bool all = ilo == i0 && ihi == i0 + BK - 1 && i0 >= jw + 31 &&
-                         ((i0 + BK - 1 - jw < p.w) || jw + 31 < p.s) && jw + 31 < N;
+        // uniform by construction; read back as a scalar so that the per-element masking below
+        // branches once per step, not per element under an execution mask
+        const bool all = __builtin_amdgcn_readfirstlane((int)(ilo == i0 && ihi == i0 + BK - 1 && i0 >= jw + 31 &&
+                             ((i0 + BK - 1 - jw < p.w) || jw + 31 < p.s) && jw + 31 < N)) != 0;
         const uint16_t *ql = lds + cur * STAGE;
         const uint16_t *gl = ql + T::IMG;
         const float *stl = reinterpret_cast<const float *>(ql + 2 * T::IMG);
@@ -901,8 +905,8 @@ void bwd_dkv2_kernel(BwdParams p) {
                             float x = sd[qb][e];
                             if (!all) {
                                 const int dij = iq - j;
-                                const bool ok = iq >= qlo && iq < qhi && iq < N && j < N && dij >= 0 &&
-                                                (dij < p.w || j < p.s);
+                                const bool ok = (iq >= qlo) & (iq < qhi) & (iq < N) & (j < N) & (dij >= 0) &
+                                                ((dij < p.w) | (j < p.s));
                                 x = ok ? x : (MODE == 0 ? INFINITY : -INFINITY);
                             }
                             sd[qb][e] = MODE == 0

@@ -149,7 +149,13 @@ struct MfmaParams {
     int out_bf16;
     int chunked;              // 1: rows and positions per sequence from cg; V from vimg
     ChunkGeom cg;
-    float *lse;               // softmax row log-normalisers [B, Hq, N] (natural log), or null
+    float *lse;               // softmax row log-normalisers [B, Hq, N_mem] (natural log), or null
+    // whole sequences: query/key i is memory row b N_mem + pos_off + pos_stride i at position
+    // pos_off + pos_stride i, and ALiBi slopes are multiplied by slope_mul (one residue class
+    // of a dilated window: pos_stride = r, slope_mul = r; else 0, 1, N, 1)
+    int64_t N_mem;
+    int pos_off, pos_stride;
+    float slope_mul;
 };
 
 struct PackParams {
@@ -158,6 +164,10 @@ struct PackParams {
     const float *rope;
     int64_t N, Hkv;
     int n_ktiles;
+    // key j of the (strided) sequence is memory row b N_mem + pos_off + pos_stride j and
+    // position pos_off + pos_stride j (a residue class of a dilated window; else 0, 1, N)
+    int64_t N_mem;
+    int pos_off, pos_stride;
 };
 
 // ---------------------------------------------------------------------------------------
@@ -196,15 +206,16 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
             const bool in = j < p.N;
             t0[r] = make_float4(1.f, 0.f, 1.f, 0.f);
             t1[r] = t0[r];
+            const int64_t pos = p.pos_off + (int64_t)p.pos_stride * j;
             if (ROT && in) {
-                const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
+                const float *t = p.rope + (pos * (D / 2) + c * 4) * 2;
                 t0[r] = as_float4(ldg16(t));
                 t1[r] = as_float4(ldg16(t + 4));
             }
 #pragma unroll
             for (int u = 0; u < PACK_HG; ++u) {
                 xk[r][u] = make_uint4(0, 0, 0, 0);
-                if (in && u < nh) xk[r][u] = ldg16(p.k + ((b * p.N + j) * p.Hkv + h0 + u) * D + c * 8);
+                if (in && u < nh) xk[r][u] = ldg16(p.k + ((b * p.N_mem + pos) * p.Hkv + h0 + u) * D + c * 8);
             }
         }
 #pragma unroll
@@ -228,9 +239,10 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
             const int cidx = tid + 256 * pt, row = cidx / T::C, c = cidx % T::C;
             const int64_t j = (int64_t)jt * BK + row;
             const bool in = j < p.N;
+            const int64_t pos = p.pos_off + (int64_t)p.pos_stride * j;
             float4 t0 = make_float4(1.f, 0.f, 1.f, 0.f), t1 = t0;
             if (ROT && in) {
-                const float *t = p.rope + (j * (D / 2) + c * 4) * 2;
+                const float *t = p.rope + (pos * (D / 2) + c * 4) * 2;
                 t0 = as_float4(ldg16(t));
                 t1 = as_float4(ldg16(t + 4));
             }
@@ -240,8 +252,9 @@ __global__ __launch_bounds__(256) void prefill_pack_kernel(PackParams p) {
 #pragma unroll
             for (int u = 0; u < PACK_HG; ++u) {
                 xk[u] = xv[u] = make_uint4(0, 0, 0, 0);
-                if (u < nh && in) xk[u] = ldg16(p.k + ((b * p.N + j) * p.Hkv + h0 + u) * D + c * 8);
-                if (u < nh && jv < p.N) xv[u] = ldg16(p.v + ((b * p.N + jv) * p.Hkv + h0 + u) * D + vd);
+                const int64_t posv = p.pos_off + (int64_t)p.pos_stride * jv;
+                if (u < nh && in) xk[u] = ldg16(p.k + ((b * p.N_mem + pos) * p.Hkv + h0 + u) * D + c * 8);
+                if (u < nh && jv < p.N) xv[u] = ldg16(p.v + ((b * p.N_mem + posv) * p.Hkv + h0 + u) * D + vd);
             }
             const int kslot = (row * T::C + (c ^ kswz<D>(row))) * 8;
 #pragma unroll
@@ -855,9 +868,10 @@ void prefill_mfma_kernel(MfmaParams p) {
     const int qc = lane & 31, g = lane >> 5;
     const int hp = wave / WPH, pb = wave % WPH;
     const int64_t h = (int64_t)hkv * p.G + hg * GP + hp;
-    // query rows: positions [qpos0, N) at rows qrow0 + (position - qpos0)
+    // query rows: positions [qpos0, N) at memory rows qrow0 + rstep (position - qpos0)
     int qpos0 = 0, nq = (int)p.N, shift = 0, ns_img = 0;
-    int64_t qrow0 = (int64_t)b * p.N;
+    int64_t qrow0 = (int64_t)b * p.N_mem + p.pos_off;   // memory row of query qpos0
+    int rstep = p.pos_stride;                           // memory rows between queries
     if (p.chunked) {
         const ChunkSeq cs = chunk_seq(p.cg, b);
         if (!cs.rows_ok) return;
@@ -867,6 +881,7 @@ void prefill_mfma_kernel(MfmaParams p) {
         }
         if (qt * QP >= cs.n) return;
         qpos0 = cs.p0; nq = cs.n; qrow0 = cs.row0; shift = cs.shift; ns_img = p.cg.ns_img;
+        rstep = 1;
     }
     const int N = qpos0 + nq;
     const int q0 = qpos0 + qt * QP;
@@ -884,7 +899,7 @@ void prefill_mfma_kernel(MfmaParams p) {
 
     TileCtx cx;
     {
-        const int64_t kvoff = ((int64_t)b * p.N * p.Hkv + hkv) * D;
+        const int64_t kvoff = (((int64_t)b * p.N_mem + p.pos_off) * p.Hkv + hkv) * D;
         const int64_t imoff = ((int64_t)b * p.Hkv + hkv) * p.n_ktiles * T::IMG;
         const uint32_t imbytes = (uint32_t)p.n_ktiles * T::IMG_BYTES;
         cx.rk = make_rsrc(p.kimg + imoff, imbytes);
@@ -933,7 +948,7 @@ void prefill_mfma_kernel(MfmaParams p) {
 
     // ---- first transfers: K tile 0 (and 1 when pipelined) and V tile 0, in flight while the
     // query fragment and the slope load
-    const float slope = ALIBI ? p.slopes[h] : 0.0f;
+    const float slope = ALIBI ? p.slopes[h] * p.slope_mul : 0.0f;
     load_k<D>(kbuf0, cx, lo, cx.j0_of(0));
     load_v<D, VF16>(vbuf0, cx, lo, cx.j0_of(0));
     if (T::PIPE && cx.n_tiles > 1) load_k<D>(kbuf1, cx, lo, cx.j0_of(1));
@@ -946,9 +961,11 @@ void prefill_mfma_kernel(MfmaParams p) {
     {
         const bool in = i < N;
         const int ic = in ? i : N - 1;
-        const uint16_t *qrow = p.q + ((qrow0 + (ic - qpos0)) * p.Hq + h) * D;
-        const float4 *trow = rope ? reinterpret_cast<const float4 *>(p.rope + (int64_t)ic * D)
-                                  : nullptr;
+        const uint16_t *qrow = p.q + ((qrow0 + (int64_t)(ic - qpos0) * rstep) * p.Hq + h) * D;
+        // rotation angles at the query's position (chunked: the position itself; a residue
+        // class: pos_off + r i)
+        const int64_t qpos = p.chunked ? (int64_t)ic : p.pos_off + (int64_t)p.pos_stride * ic;
+        const float4 *trow = rope ? reinterpret_cast<const float4 *>(p.rope + qpos * D) : nullptr;
         uint4 xq[KS];
         float4 t0[KS], t1[KS];
 #pragma unroll
@@ -1039,7 +1056,8 @@ void prefill_mfma_kernel(MfmaParams p) {
     const float l_tot = MODE == 1 ? l_run + __shfl_xor(l_run, 32, 64) : 1.0f;
     const float inv = MODE == 1 ? 1.0f / l_tot : 1.0f;
     if (MODE == 1 && p.lse != nullptr && g == 0 && i < N)
-        p.lse[((int64_t)b * p.Hq + h) * p.N + i] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+        p.lse[((int64_t)b * p.Hq + h) * p.N_mem + p.pos_off + (int64_t)p.pos_stride * i] =
+            (m_run + log2f(l_tot)) * 0.6931471805599453f;
     float *ol = reinterpret_cast<float *>(lds) + (wave & 3) * (32 * T::OSTR);
     constexpr int C4 = D / 4;  // 4-float chunks per row
 #pragma unroll
@@ -1057,12 +1075,12 @@ void prefill_mfma_kernel(MfmaParams p) {
         }
         __syncthreads();
         if ((wave >> 2) == round) {
-            // this wavefront's 32 rows start at element obase; row r lies r * Hq * D further
+            // this wavefront's 32 rows start at element obase; row r lies r * rstep * Hq * D further
             // (32-bit offsets: Hq * D * 32 < 2^31 is a launch condition)
-            const int64_t obase = ((qrow0 + (qa - qpos0)) * p.Hq + h) * D;
+            const int64_t obase = ((qrow0 + (int64_t)(qa - qpos0) * rstep) * p.Hq + h) * D;
             void *ob = p.out_bf16 ? static_cast<void *>(static_cast<uint16_t *>(p.o) + obase)
                                   : static_cast<void *>(static_cast<float *>(p.o) + obase);
-            const int rstride = (int)p.Hq * D;
+            const int rstride = rstep * (int)p.Hq * D;
 #pragma unroll
             for (int rr = 0; rr < 32 * C4 / 64; ++rr) {
                 const int ch = lane + 64 * rr;
@@ -1129,9 +1147,22 @@ Plan plan_of(const PrefillArgs &a) {
 
 }  // namespace
 
+// Dilated windows without sinks run as one plain window per residue class of positions;
+// past MAX_CLASSES classes (two launches each) the single in-kernel stride test is cheaper.
+constexpr int64_t MAX_CLASSES = 64;
+bool class_path(const PrefillArgs &a) { return a.dil > 1 && a.s == 0 && a.dil <= MAX_CLASSES; }
+
 bool prefill_mfma_supported(const PrefillArgs &a) {
     if (a.in_dt != 1 || (a.d != 64 && a.d != 128)) return false;
-    if ((a.dil & (a.dil - 1)) != 0 || a.dil > (int64_t(1) << 24)) return false;
+    // dilated windows: without sinks a dilation up to MAX_CLASSES runs as residue classes
+    // (strided rows: dilation x Hq x d x 32 elements of output per wavefront stay below
+    // 2^31); otherwise the in-kernel stride test, which needs a power of two
+    if (a.dil > (int64_t(1) << 24)) return false;
+    if (class_path(a)) {
+        if (a.dil * a.Hq * a.d * 32 >= (int64_t(1) << 31)) return false;
+    } else if ((a.dil & (a.dil - 1)) != 0) {
+        return false;
+    }
     if (a.B * a.N == 0) return true;
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
@@ -1156,10 +1187,16 @@ size_t prefill_mfma_workspace_bytes(const PrefillArgs &a) {
     return pl.img_bytes + (pl.vf16 ? pl.img_bytes : 0);
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
-                               const void *v, void *o, void *ws, hipStream_t st, float *lse) {
-    if (a.B * a.N == 0) return hipSuccess;
-    const Plan pl = plan_of(a);
+// One pre-pass + main kernel pair over the (strided) sequence of n positions: memory rows and
+// positions pos_off + r j, j < n; ALiBi slopes times r; dmask the in-kernel stride test
+// (dilation - 1) of the general form, 0 when the positions are one residue class.
+hipError_t launch_prefill_pair(const PrefillArgs &a, const void *q, const void *k,
+                               const void *v, void *o, void *ws, hipStream_t st, float *lse,
+                               int64_t n, int pos_off, int r, int64_t w_ext, int dmask) {
+    const bool vf16 = a.mode == 1;
+    const int64_t n_ktiles = (n + BK - 1) / BK;
+    // the workspace holds the images of the whole sequence; a class uses its front part
+    const size_t img_bytes = plan_of(a).img_bytes;
     const int64_t G = a.Hq / a.Hkv;
     const int GP = pack_of(G);
     const int64_t QP = 32 * (a.d == 128 ? Tile<128>::NW : Tile<64>::NW) / GP;
@@ -1168,34 +1205,36 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     mp.k = static_cast<const uint16_t *>(k);
     mp.v = static_cast<const uint16_t *>(v);
     mp.kimg = static_cast<const uint16_t *>(ws);
-    mp.vimg = pl.vf16 ? static_cast<const uint16_t *>(ws) + pl.img_bytes / 2 : nullptr;
+    mp.vimg = vf16 ? static_cast<const uint16_t *>(ws) + img_bytes / 2 : nullptr;
     mp.o = o;
     mp.slopes = a.slopes;
     mp.rope = a.rope;
-    mp.N = a.N; mp.Hq = a.Hq; mp.Hkv = a.Hkv; mp.G = G;
-    mp.n_qtiles = (int)((a.N + QP - 1) / QP);
+    mp.N = n; mp.Hq = a.Hq; mp.Hkv = a.Hkv; mp.G = G;
+    mp.n_qtiles = (int)((n + QP - 1) / QP);
     mp.n_hgroups = (int)(G / GP);
-    mp.n_ktiles = (int)pl.n_ktiles;
-    // positions the window spans (w - 1 < N keeps the product small)
-    const int64_t extent = a.w - 1 >= a.N ? a.N : a.dil * (a.w - 1) + 1;
-    mp.w = (int)(extent < a.N ? extent : a.N);
-    mp.dmask = (int)(a.dil - 1);
-    mp.s = (int)(a.s < a.N ? a.s : a.N);
+    mp.n_ktiles = (int)n_ktiles;
+    mp.w = (int)(w_ext < n ? w_ext : n);
+    mp.dmask = dmask;
+    mp.s = (int)(a.s < n ? a.s : n);
     mp.cs = a.scale * LOG2E;
-    mp.kv_bytes = (uint32_t)(((a.N - 1) * a.Hkv + 1) * a.d * 2);
-    mp.row_bytes = (uint32_t)(a.Hkv * a.d * 2);
+    // bytes from this sequence's first V row to past its last one (raw V reads)
+    mp.kv_bytes = (uint32_t)(((n - 1) * r * a.Hkv + 1) * a.d * 2);
+    mp.row_bytes = (uint32_t)(r * a.Hkv * a.d * 2);
     mp.out_bf16 = a.out_dt == 1;
     mp.lse = lse;
+    mp.N_mem = a.N; mp.pos_off = pos_off; mp.pos_stride = r;
+    mp.slope_mul = (float)r;
 
     {
         PackParams pp = {};
         pp.k = mp.k; pp.v = mp.v;
         pp.kimg = static_cast<uint16_t *>(ws);
-        pp.vimg = pl.vf16 ? static_cast<uint16_t *>(ws) + pl.img_bytes / 2 : nullptr;
-        pp.rope = a.rope; pp.N = a.N; pp.Hkv = a.Hkv; pp.n_ktiles = (int)pl.n_ktiles;
-        const int npb = (int)(a.B * pl.n_ktiles * ((a.Hkv + PACK_HG - 1) / PACK_HG));
-        const hipError_t e = a.d == 64 ? launch_pack<64>(pp, npb, a.rope != nullptr, pl.vf16, st)
-                                       : launch_pack<128>(pp, npb, a.rope != nullptr, pl.vf16, st);
+        pp.vimg = vf16 ? static_cast<uint16_t *>(ws) + img_bytes / 2 : nullptr;
+        pp.rope = a.rope; pp.N = n; pp.Hkv = a.Hkv; pp.n_ktiles = (int)n_ktiles;
+        pp.N_mem = a.N; pp.pos_off = pos_off; pp.pos_stride = r;
+        const int npb = (int)(a.B * n_ktiles * ((a.Hkv + PACK_HG - 1) / PACK_HG));
+        const hipError_t e = a.d == 64 ? launch_pack<64>(pp, npb, a.rope != nullptr, vf16, st)
+                                       : launch_pack<128>(pp, npb, a.rope != nullptr, vf16, st);
         if (e != hipSuccess) return e;
     }
     const bool alibi = a.slopes != nullptr;
@@ -1208,6 +1247,27 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *
     if (GP == 4) return launch_gp<128, 4>(mp, nb, a.mode, alibi, st);
     if (GP == 2) return launch_gp<128, 2>(mp, nb, a.mode, alibi, st);
     return launch_gp<128, 1>(mp, nb, a.mode, alibi, st);
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs &a, const void *q, const void *k,
+                               const void *v, void *o, void *ws, hipStream_t st, float *lse) {
+    if (a.B * a.N == 0) return hipSuccess;
+    if (class_path(a)) {
+        // a dilated window without sinks is the plain window of w keys on each residue class
+        // of positions mod r: run the classes one after another, each over the strided rows
+        // (keys and queries rotated at their true positions, slopes times r); the classes
+        // share the workspace, in stream order
+        const int r = a.dil < a.N ? (int)a.dil : (int)a.N;
+        for (int c = 0; c < r; ++c) {
+            const int64_t n = (a.N - c + r - 1) / r;
+            const hipError_t e = launch_prefill_pair(a, q, k, v, o, ws, st, lse, n, c, r, a.w, 0);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    // positions the window spans (w - 1 < N keeps the product small)
+    const int64_t extent = a.w - 1 >= a.N ? a.N : a.dil * (a.w - 1) + 1;
+    return launch_prefill_pair(a, q, k, v, o, ws, st, lse, a.N, 0, 1, extent, (int)(a.dil - 1));
 }
 
 }  // namespace swa
@@ -1325,6 +1385,7 @@ hipError_t launch_prefill_chunk(const DecodeArgs &a, const CacheArgs &c, const v
         mp.slopes = a.slopes;
         mp.rope = a.rope;
         mp.N = 0; mp.Hq = a.Hq; mp.Hkv = c.Hkv; mp.G = G;
+        mp.N_mem = 0; mp.pos_off = 0; mp.pos_stride = 1; mp.slope_mul = 1.0f;
         mp.n_qtiles = (int)((max_q + QP - 1) / QP);
         mp.n_hgroups = (int)(G / GP);
         mp.n_ktiles = (int)pl.n_ktiles;

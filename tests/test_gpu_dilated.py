@@ -1,10 +1,12 @@
 """GPU parity of dilated windows (swa_prefill with dilation r > 1) with the oracle.
 
-The window keeps every r-th position: keys i, i - r, ..., i - r (w - 1) plus the sinks. The
-matrix-core path takes power-of-two dilations (2, 4, 8 here) over both head sizes, both
-modes, grouped heads, ALiBi and RoPE, sinks, and windows wider than the sequence; other
-dilations and float32 inputs run on the general kernel. Dilation 1 must reproduce the plain
-window bit for bit.
+The window keeps every r-th position: keys i, i - r, ..., i - r (w - 1) plus the sinks. On
+the matrix cores, a dilation without sinks (r up to 64, any r) runs as the plain window on
+each residue class of positions (strided rows, true positions for the rotation, slopes times
+r); with sinks a power-of-two dilation runs through the in-kernel stride test. Both head
+sizes, both modes, grouped heads, ALiBi and RoPE, sinks, classes of one or two positions and
+windows wider than a class; other dilations with sinks and float32 inputs run on the general
+kernel. Dilation 1 must reproduce the plain window bit for bit.
 """
 import numpy as np
 import pytest
@@ -26,6 +28,12 @@ CASES = [  # dtype, B, Hq, Hkv, N, d, w, s, r, mode, alibi, theta
     ("bf16", 1, 3, 1, 260, 64, 9, 2, 3, wl.SOFTMAX, True, 1e4),     # r = 3: general kernel
     ("f32", 1, 2, 2, 150, 32, 12, 1, 2, wl.SIGMOID, True, 1e4),     # float32: general kernel
     ("bf16", 1, 4, 4, 200, 96, 10, 0, 4, wl.SOFTMAX, False, 1e4),   # d 96: general kernel
+    # residue classes (no sinks): r not a power of two, N not a multiple of r, GQA, ALiBi
+    ("bf16", 2, 4, 2, 301, 64, 20, 0, 3, wl.SIGMOID, True, 1e4),
+    ("bf16", 1, 8, 2, 517, 128, 40, 0, 5, wl.SOFTMAX, True, 1e6),
+    ("bf16", 1, 4, 1, 700, 128, 300, 0, 2, wl.SIGMOID, False, 1e4),  # window wider than a class
+    ("bf16", 1, 2, 2, 90, 64, 5, 0, 64, wl.SOFTMAX, True, 1e4),      # classes of 1 or 2 rows
+    ("bf16", 1, 2, 2, 90, 64, 5, 0, 100, wl.SOFTMAX, False, 1e4),    # r > 64 with no power of two: general kernel
 ]
 
 
