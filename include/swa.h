@@ -61,9 +61,11 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
  * Dilated window (the dilated-window member of the sparse-attention family the Sliding
  * Window Attention glossary lists beside SWA): with dilation r > 1 the window keeps every
  * r-th position, K(i) = { j <= i : ((i - j) mod r = 0 and (i - j) / r < w) or j < s }, so w
- * keys span r (w - 1) + 1 positions; the sinks are unchanged. The matrix-core path takes r a
- * power of two (other r run on the general kernel); the cache entry points take no
- * dilation.
+ * keys span r (w - 1) + 1 positions; the sinks are unchanged. On the matrix cores a dilated
+ * window without sinks and r <= 64 runs as the plain window on each residue class of
+ * positions mod r, one pre-pass and main kernel pair per class on the strided rows (2 r
+ * launches on the stream); with sinks, or past r = 64, r must be a power of two (other r
+ * run on the general kernel). The cache entry points take no dilation.
  * bf16 inputs with d in {64, 128}, H_q * d below 2^26 and 16-byte aligned tensors run on the
  * matrix cores, which form the score product from float16 operands (rotated q and k; for
  * sigmoid q is also multiplied by -scale * log2(e) before its rounding, and the ALiBi term
