@@ -1052,40 +1052,47 @@ void prefill_mfma_kernel(MfmaParams p) {
     }
 
     // ---- epilogue: normalise, stage O row-major in LDS (four wavefronts at a time), store
-    // whole rows
+    // whole rows. The loop holds every register, so the lane's indices are formed again here
+    // from the scalar wavefront index and the lane id rather than kept across it.
+    int elane;  // the lane id, read here (an asm statement the compiler cannot hoist)
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(elane));
+    const int ew = cx.wave;
+    const int eqc = elane & 31, eg = elane >> 5;
+    const int64_t eh = (int64_t)hkv * p.G + hg * GP + ew / WPH;
+    const int eqa = q0 + 32 * (ew % WPH), ei = eqa + eqc;
     const float l_tot = MODE == 1 ? l_run + __shfl_xor(l_run, 32, 64) : 1.0f;
     const float inv = MODE == 1 ? 1.0f / l_tot : 1.0f;
-    if (MODE == 1 && p.lse != nullptr && g == 0 && i < N)
-        p.lse[((int64_t)b * p.Hq + h) * p.N_mem + p.pos_off + (int64_t)p.pos_stride * i] =
+    if (MODE == 1 && p.lse != nullptr && eg == 0 && ei < N)
+        p.lse[((int64_t)b * p.Hq + eh) * p.N_mem + p.pos_off + (int64_t)p.pos_stride * ei] =
             (m_run + log2f(l_tot)) * 0.6931471805599453f;
-    float *ol = reinterpret_cast<float *>(lds) + (wave & 3) * (32 * T::OSTR);
+    float *ol = reinterpret_cast<float *>(lds) + (ew & 3) * (32 * T::OSTR);
     constexpr int C4 = D / 4;  // 4-float chunks per row
 #pragma unroll
     for (int round = 0; round < T::NW / 4; ++round) {
-        if ((wave >> 2) == round) {
+        if ((ew >> 2) == round) {
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int d0 = 32 * db + 8 * r + 4 * g;
-                    *reinterpret_cast<float4 *>(ol + qc * T::OSTR + d0) =
+                    const int d0 = 32 * db + 8 * r + 4 * eg;
+                    *reinterpret_cast<float4 *>(ol + eqc * T::OSTR + d0) =
                         make_float4(oacc[db][4 * r] * inv, oacc[db][4 * r + 1] * inv,
                                     oacc[db][4 * r + 2] * inv, oacc[db][4 * r + 3] * inv);
                 }
         }
         __syncthreads();
-        if ((wave >> 2) == round) {
+        if ((ew >> 2) == round) {
             // this wavefront's 32 rows start at element obase; row r lies r * rstep * Hq * D further
             // (32-bit offsets: Hq * D * 32 < 2^31 is a launch condition)
-            const int64_t obase = ((qrow0 + (int64_t)(qa - qpos0) * rstep) * p.Hq + h) * D;
+            const int64_t obase = ((qrow0 + (int64_t)(eqa - qpos0) * rstep) * p.Hq + eh) * D;
             void *ob = p.out_bf16 ? static_cast<void *>(static_cast<uint16_t *>(p.o) + obase)
                                   : static_cast<void *>(static_cast<float *>(p.o) + obase);
             const int rstride = rstep * (int)p.Hq * D;
 #pragma unroll
             for (int rr = 0; rr < 32 * C4 / 64; ++rr) {
-                const int ch = lane + 64 * rr;
+                const int ch = elane + 64 * rr;
                 const int qrow = ch / C4, c4 = ch % C4;
-                if (qa + qrow < N) {
+                if (eqa + qrow < N) {
                     const float4 x = *reinterpret_cast<const float4 *>(ol + qrow * T::OSTR + 4 * c4);
                     store_out4<true>(ob, p.out_bf16, qrow * rstride + 4 * c4, x.x, x.y, x.z, x.w);  // whole rows
                 }
