@@ -628,6 +628,18 @@ void bwd_dkv_kernel(BwdParams p) {
                     sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(aq, kreg[ks], sacc, 0, 0, 0);
                     dacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ag, vreg[ks], dacc, 0, 0, 0);
                 }
+                // edge steps: pairs outside the key sets get the fill that makes their weight
+                // zero, in place (one branch per row block)
+                if (!all) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int iq = i0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
+                        const int dij = iq - j;
+                        const bool ok = (iq >= qlo) & (iq < qhi) & (iq < N) & (j < N) & (dij >= 0) &
+                                        ((dij < p.w) | (j < p.s));
+                        sacc[e] = keep_or_fill(sacc[e], ok, MODE == 0 ? INFINITY : -INFINITY);
+                    }
+                }
                 // weights into sacc, dX into dacc
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -642,14 +654,7 @@ void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
                     for (int e4 = 0; e4 < 4; ++e4) {
                         const int e = 4 * u + e4;
-                        const int iq = i0 + r0 + e4;
-                        float x = sacc[e];
-                        if (!all) {
-                            const int dij = iq - j;
-                            const bool ok = (iq >= qlo) & (iq < qhi) & (iq < N) & (j < N) & (dij >= 0) &
-                                            ((dij < p.w) | (j < p.s));
-                            x = ok ? x : (MODE == 0 ? INFINITY : -INFINITY);
-                        }
+                        const float x = sacc[e];
                         float pe, dxe;
                         if (MODE == 0) {
                             pe = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x));
@@ -887,6 +892,20 @@ void bwd_dkv2_kernel(BwdParams p) {
                 sd[qb] = a;
             }
             if (role_p) {
+                // edge steps: pairs outside the key sets get the fill that makes their weight
+                // zero, in place (one branch per step)
+                if (!all) {
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int iq = i0 + 32 * qb + 8 * (e >> 2) + 4 * g + (e & 3);
+                            const int dij = iq - j;
+                            const bool ok = (iq >= qlo) & (iq < qhi) & (iq < N) & (j < N) & (dij >= 0) &
+                                            ((dij < p.w) | (j < p.s));
+                            sd[qb][e] = keep_or_fill(sd[qb][e], ok, MODE == 0 ? INFINITY : -INFINITY);
+                        }
+                }
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -901,14 +920,7 @@ void bwd_dkv2_kernel(BwdParams p) {
 #pragma unroll
                         for (int e4 = 0; e4 < 4; ++e4) {
                             const int e = 4 * u + e4;
-                            const int iq = i0 + r0 + e4;
-                            float x = sd[qb][e];
-                            if (!all) {
-                                const int dij = iq - j;
-                                const bool ok = (iq >= qlo) & (iq < qhi) & (iq < N) & (j < N) & (dij >= 0) &
-                                                ((dij < p.w) | (j < p.s));
-                                x = ok ? x : (MODE == 0 ? INFINITY : -INFINITY);
-                            }
+                            const float x = sd[qb][e];
                             sd[qb][e] = MODE == 0
                                 ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x))
                                 : __builtin_amdgcn_exp2f(fmaf(x, p.cs, lb) - l2v[e4]);
