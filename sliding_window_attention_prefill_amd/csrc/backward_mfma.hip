@@ -426,29 +426,50 @@ void bwd_dq_kernel(BwdParams p) {
         const int j0 = j0_of(t);
         const int kind = kind_of(j0);
         if (kind >= 0) {
-            f32x16_t sacc[2], dacc[2];
             const uint16_t *kl = lds + cur * T::IMG, *vl = lds + (2 + cur) * T::IMG;
-            qk_tile_off<D, ALIBI>(kl, koff, bo, (MODE == 0 && ALIBI) ? query_term(bo, i - j0) : bo.b,
-                                  qreg, sacc);
-            qk_tile_off<D, false>(vl, koff, bo, greg, dacc);
+            const f16x8_t bb = (MODE == 0 && ALIBI) ? query_term(bo, i - j0) : bo.b;
             constexpr float fill = MODE == 0 ? INFINITY : -INFINITY;
-            if (kind == 1) mask_tile<false>(sacc, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s, 0, fill);
-            else if (kind == 2) mask_tile<true>(sacc, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s, 0, fill);
             const float bq = slope_l2 * (float)(i - j0);
+            // one 32-key block at a time: S^T and dP^T (their chains alternate), dX^T, then
+            // dQ^T += K^T dX^T; the next block's products overlap this block's vector work
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int kb = 0; kb < 2; ++kb) {
+                const f32x16_t zero = {};
+                f32x16_t sa = ALIBI ? __builtin_amdgcn_mfma_f32_32x32x16_f16(bo.a[kb], bb, zero, 0, 0, 0) : zero;
+                f32x16_t da = zero;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const f16x8_t ak = *reinterpret_cast<const f16x8_t *>(kl + kb * 32 * D + koff[ks]);
+                    const f16x8_t av = *reinterpret_cast<const f16x8_t *>(vl + kb * 32 * D + koff[ks]);
+                    sa = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, qreg[ks], sa, 0, 0, 0);
+                    da = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, greg[ks], da, 0, 0, 0);
+                }
+                {
+                    // rows read four products ahead of their use
+                    constexpr int NR = 2 * KS, AH = 4;
+                    __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);  // LDS reads
+                    if (ALIBI) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+                    for (int u = 0; u < NR - AH; ++u) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // matrix
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+                }
+                if (kind == 1) mask_block<false>(sa, kb, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s, fill);
+                else if (kind == 2) mask_block<true>(sa, kb, i - j0 - 4 * g, j0 + 4 * g, p.w, p.s, fill);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     if (MODE == 0) {
-                        const float pe = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sacc[kb2][e]));
-                        sacc[kb2][e] = dacc[kb2][e] * fmaf(-pe, pe, pe);   // dP p (1 - p)
+                        const float pe = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(sa[e]));
+                        sa[e] = da[e] * fmaf(-pe, pe, pe);   // dP p (1 - p)
                     } else {
-                        const float pe = __builtin_amdgcn_exp2f(fmaf(sacc[kb2][e], p.cs, bq) - l2);
-                        sacc[kb2][e] = pe * (dacc[kb2][e] - dl);
+                        const float pe = __builtin_amdgcn_exp2f(fmaf(sa[e], p.cs, bq) - l2);
+                        sa[e] = pe * (da[e] - dl);
                     }
                 }
-            acc_tr<D>(kl, 0, toff, sacc[0], acc);
-            acc_tr<D>(kl, 1, toff, sacc[1], acc);
+                acc_tr<D>(kl, kb, toff, sa, acc);
+            }
         }
         __syncthreads();
     }

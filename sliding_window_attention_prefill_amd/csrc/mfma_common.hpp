@@ -158,6 +158,19 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sacc)[2], int dq, int jb, i
         }
 }
 
+// mask_tile for one 32-key block kb of the tile.
+template <bool SINKS>
+__device__ __forceinline__ void mask_block(f32x16_t &x, int kb, int dq, int jb, int w, int s,
+                                           float fill) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int dij = dq - key_of(kb, e);
+        bool ok = (unsigned)dij < (unsigned)w;   // 0 <= i - j < w
+        if (SINKS) ok = ok | ((dij >= 0) & (jb + key_of(kb, e) < s));
+        x[e] = ok ? x[e] : fill;
+    }
+}
+
 // x = keep ? x : fill, written in x's own register (an instruction with the result tied to
 // its input), so that a conditionally masked accumulator needs no copy where the masked and
 // the unmasked paths meet.
