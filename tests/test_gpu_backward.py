@@ -74,7 +74,30 @@ CASES = [  # B, Hq, Hkv, N, d, w, s, mode, alibi, theta
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%d_Hq%d_Hkv%d_N%d_d%d_w%d_s%d_m%d" % c[:8])
+def _random_cases(n, seed):
+    """Seeded draws over the matrix-core backward's options: head size, 1-8 query heads per
+    kv head, ragged lengths (including one row and tile edges), windows from 1 to past the
+    sequence, sinks (some past the window, which the extra sink workgroups take), both modes,
+    ALiBi and RoPE."""
+    rs = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rs.choice([64, 128]))
+        Hkv = int(rs.choice([1, 2]))
+        G = int(rs.choice([1, 2, 4, 8]))
+        B = int(rs.choice([1, 2]))
+        N = int(rs.choice([1, 63, 64, 65, int(rs.randint(2, 600)), int(rs.randint(2, 600))]))
+        w = int(rs.choice([1, int(rs.randint(1, 200)), int(rs.randint(200, 700))]))
+        s = int(rs.choice([0, 0, 1, int(rs.randint(1, 100))]))
+        mode = wl.SIGMOID if rs.rand() < 0.5 else wl.SOFTMAX
+        alibi = bool(rs.rand() < 0.5)
+        theta = float(rs.choice([0.0, 1e4, 1e6]))
+        cases.append((B, Hkv * G, Hkv, N, d, w, s, mode, alibi, theta))
+    return cases
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(16, 20261204),
+                         ids=lambda c: "B%d_Hq%d_Hkv%d_N%d_d%d_w%d_s%d_m%d" % c[:8])
 def test_backward_matches_oracle(case):
     B, Hq, Hkv, N, d, w, s, mode, alibi, theta = case
     q, k, v, dout = _inputs(B, Hq, Hkv, N, d, seed=N + d + w)

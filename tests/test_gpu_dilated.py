@@ -37,7 +37,29 @@ CASES = [  # dtype, B, Hq, Hkv, N, d, w, s, r, mode, alibi, theta
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s_N%d_d%d_w%d_s%d_r%d_m%d" % ((c[0],) + c[4:10]))
+def _random_cases(n, seed):
+    """Seeded draws: dilations 2-70 (residue classes without sinks, the stride test with sinks
+    and a power of two, the general kernel otherwise), lengths that are not multiples of r,
+    windows narrower and wider than a class, both head sizes and modes, GQA, ALiBi, RoPE."""
+    rs = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        r = int(rs.choice([2, 3, 4, 6, 7, 8, 16, int(rs.randint(2, 70))]))
+        d = int(rs.choice([64, 128]))
+        Hkv = int(rs.choice([1, 2]))
+        G = int(rs.choice([1, 2, 4]))
+        N = int(rs.choice([int(rs.randint(1, 80)), int(rs.randint(80, 600))]))
+        w = int(rs.choice([1, int(rs.randint(2, 40)), int(rs.randint(2, 40)), int(rs.randint(40, 300))]))
+        s = int(rs.choice([0, 0, 0, int(rs.randint(1, 40))]))
+        mode = wl.SIGMOID if rs.rand() < 0.5 else wl.SOFTMAX
+        alibi = bool(rs.rand() < 0.5)
+        theta = float(rs.choice([0.0, 1e4]))
+        cases.append(("bf16", int(rs.choice([1, 2])), Hkv * G, Hkv, N, d, w, s, r, mode, alibi, theta))
+    return cases
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(14, 20261205),
+                         ids=lambda c: "%s_N%d_d%d_w%d_s%d_r%d_m%d" % ((c[0],) + c[4:10]))
 def test_dilated_matches_oracle(case):
     dtype, B, Hq, Hkv, N, d, w, s, r, mode, alibi, theta = case
     slopes = tuple(np.linspace(-0.4, 0.4, Hq).tolist()) if alibi else None
