@@ -5,7 +5,8 @@ loop can capture a call once and replay it. Each test captures one call with its
 workspace allocated beforehand, then replays it several times. Before every replay it refills
 the inputs in place, runs the same call eagerly into separate outputs, and synchronises. Every
 replay must give the eager call's bits: the kernels are deterministic, and a replay reads
-whatever the captured buffers hold at that moment.
+whatever the captured buffers hold at that moment. The last test runs calls concurrently on
+separate streams.
 """
 import numpy as np
 import pytest
@@ -200,3 +201,58 @@ def test_decode_loop_replays_match_eager(w, s):
         assert torch.equal(out_g, out_e), "step %d" % step
         assert _caches_equal(cache_g, cache_e), "step %d cache" % step
         pos += 1
+
+
+def test_calls_on_separate_streams_run_concurrently():
+    """The library holds no state, so calls on different streams may overlap: a prefill, a
+    backward and a decode step enqueued on three streams (each with its own workspace) at
+    once give the bits of the same calls run one after another."""
+    g = torch.Generator().manual_seed(11)
+    B, N, Hq, Hkv, d, w, theta = 1, 700, 8, 2, 128, 200, 1e4
+    q = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=DEV)
+    k = torch.empty((B, N, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty_like(k)
+    dout = torch.empty((B, N, Hq, d), dtype=torch.float32, device=DEV)
+    _fill(g, q, k, v, dout)
+    table = swa.swa_rope_table(N, d, theta)
+    pkw = dict(w=w, s=2, mode=wl.SOFTMAX, rope_table=table)
+    bkw = dict(w=w, s=0, mode=wl.SIGMOID, rope_table=table)
+    o_sig, _ = swa.swa_prefill_train(q, k, v, out_dtype=torch.float32, **bkw)
+    S = 4
+    cache = swa.SwaCache.empty(S, Hkv, 64, 4, d, torch.bfloat16)
+    hist = torch.empty((S, 100, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    hist_v = torch.empty_like(hist)
+    _fill(g, hist, hist_v)
+    swa.swa_kv_append(cache, hist, hist_v, torch.zeros(S, dtype=torch.int32, device=DEV),
+                      rope_table=table)
+    dq_ = torch.empty((S, Hq, d), dtype=torch.bfloat16, device=DEV)
+    dk_ = torch.empty((S, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    dv_ = torch.empty_like(dk_)
+    _fill(g, dq_, dk_, dv_)
+    pos = torch.full((S,), 100, dtype=torch.int32, device=DEV)
+    twin = _clone_cache(cache)
+    torch.cuda.synchronize()
+
+    def run(streams, c):
+        outs = {}
+        with torch.cuda.stream(streams[0]):
+            outs["prefill"] = swa.swa_prefill(q, k, v, out_dtype=torch.float32, **pkw)
+        with torch.cuda.stream(streams[1]):
+            outs["grads"] = swa.swa_prefill_backward(q, k, v, o_sig, None, dout, **bkw)
+        with torch.cuda.stream(streams[2]):
+            outs["decode"] = swa.swa_decode_append(dq_, dk_, dv_, pos, c, mode=wl.SOFTMAX,
+                                                   rope_table=table, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return outs
+
+    cur = torch.cuda.current_stream()
+    seq = run([cur, cur, cur], twin)
+    side = [torch.cuda.Stream() for _ in range(3)]
+    for st in side:
+        st.wait_stream(cur)
+    par = run(side, cache)
+    assert torch.equal(par["prefill"], seq["prefill"])
+    for a, b in zip(par["grads"], seq["grads"]):
+        assert torch.equal(a, b)
+    assert torch.equal(par["decode"], seq["decode"])
+    assert _caches_equal(cache, twin)
