@@ -87,14 +87,47 @@ CASES = [  # d, G, H_kv, mode, alibi, w, s, theta
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "d%d_G%d_Hkv%d_m%d_a%d_w%d_s%d" % c[:7])
+def _random_cases(n, seed):
+    """Seeded draws: 1-5 sequences with histories from empty to several times the window
+    (wrapped rings), two rounds of ragged chunks (empty, one row, tile edges, several tiles),
+    both head sizes and modes, 1-8 query heads per kv head, sinks, ALiBi, RoPE."""
+    rs = np.random.RandomState(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rs.choice([64, 128]))
+        G = int(rs.choice([1, 2, 3, 4, 8]))
+        Hkv = int(rs.choice([1, 2]))
+        mode = wl.SIGMOID if rs.rand() < 0.5 else wl.SOFTMAX
+        alibi = bool(rs.rand() < 0.5)
+        w = int(rs.choice([1, int(rs.randint(2, 100)), int(rs.randint(2, 100)),
+                           int(rs.randint(100, 500)), int(rs.randint(100, 500))]))
+        s = int(rs.choice([0, 0, 1, int(rs.randint(1, 70))]))
+        theta = float(rs.choice([0.0, 1e4, 1e6]))
+        S = int(rs.randint(1, 6))
+        hist = [int(rs.choice([0, int(rs.randint(1, w + 2)), int(rs.randint(w, 4 * w + 10))]))
+                for _ in range(S)]
+        rounds = [[int(rs.choice([0, 1, 63, 64, 65, int(rs.randint(1, 260))])) for _ in range(S)]
+                  for _ in range(2)]
+        cases.append((d, G, Hkv, mode, alibi, w, s, theta, tuple(hist),
+                      tuple(tuple(r) for r in rounds)))
+    return cases
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(12, 20261206),
+                         ids=lambda c: "d%d_G%d_Hkv%d_m%d_a%d_w%d_s%d" % c[:7])
 def test_chunk_matches_oracle(case):
-    d, G, Hkv, mode, alibi, w, s, theta = case
+    d, G, Hkv, mode, alibi, w, s, theta = case[:8]
     Hq = G * Hkv
-    S = 4
-    g = torch.Generator().manual_seed(w * 31 + d + G)
-    hist = [0, w // 2 + 5, 3 * w + 17, 2 * w + 1]
-    rounds = [[70, 1, 130, 0], [0, 64, 33, 200]]
+    if len(case) > 8:
+        hist, rounds = list(case[8]), [list(r) for r in case[9]]
+    else:
+        hist = [0, w // 2 + 5, 3 * w + 17, 2 * w + 1]
+        rounds = [[70, 1, 130, 0], [0, 64, 33, 200]]
+    S = len(hist)
+    g = torch.Generator().manual_seed(w * 31 + d + G + (0 if len(case) == 8 else 1000 + 7 * S))
+    for r in rounds:
+        if max(r) == 0:
+            r[0] = 1   # at least one row per call
     max_pos = max(hist) + sum(max(r) for r in rounds) + 1
     table = swa.swa_rope_table(max_pos, d, theta) if theta > 0 else None
     cache = swa.SwaCache.empty(S, Hkv, w, s, d, torch.bfloat16)
