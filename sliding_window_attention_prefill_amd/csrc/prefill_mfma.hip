@@ -21,7 +21,7 @@
 //     softmax is online with a lazily rescaled accumulator. O^T += V^T P^T takes the
 //     weights straight from registers.
 //   * Score operands are float16: q and k are widened from bf16, rotated in float32 and
-//     rounded once (inputs must stay within the float16 range, |x| < 65504).
+//     rounded once; values past the float16 range saturate at +-65504.
 //   * A pre-pass rotates every key once into float16 tile images laid out exactly as LDS
 //     holds them (for softmax it also stores V transposed, as float16 images of V^T); the
 //     main kernel copies tiles with buffer-to-LDS transfers, which take no registers and no
@@ -33,7 +33,9 @@
 //     transposing one), its keys stored in the order of the score registers.
 //   * ALiBi: the key part of the bias enters the score accumulator through one more matrix
 //     instruction per 32-key block (exact key offsets against a two-term float16 split of
-//     the slope), so each score needs one FMA for scale and bias together.
+//     the slope). Softmax adds the query part with one add per score; sigmoid carries it in
+//     two more k-slots of the same instruction, so its scores need no vector work before
+//     the weights.
 //   * LDS rows are XOR-swizzled in 16-byte chunks so that the row reads of K and the
 //     transposing reads of V are free of bank conflicts; the register path, the transfers
 //     and the pre-pass all write that swizzle.
