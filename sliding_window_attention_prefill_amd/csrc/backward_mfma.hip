@@ -17,15 +17,18 @@
 //     transposing reads; for softmax every row also gets its base-2 log-normaliser (from the
 //     forward) and dout . o.
 //   * dq: one workgroup per (batch, kv head, head group, query tile) walks the key tiles of
-//     its band as the forward does: S^T = K Q^T and dP^T = V dO^T from LDS rows, dX^T in
-//     registers (one query per lane), then dQ^T += K^T dX^T with K read transposed.
+//     its band as the forward does, one 32-key block at a time: S^T = K Q^T and
+//     dP^T = V dO^T from LDS rows, dX^T in registers (one query per lane), then
+//     dQ^T += K^T dX^T with K read transposed.
 //   * dk, dv: one workgroup per (batch, kv head, 128 keys) walks the query tiles whose window
 //     reaches its keys, for every query head of the group: S = Q K^T and dP = dO V^T with K
 //     and V held in registers (one key per lane), then dV^T += dO^T P and dK^T += Q^T dX with
 //     dO and Q read transposed. Queries that see a sink key only through the sink rule are
-//     taken by extra workgroups that add their share atomically before the key blocks finish.
-//   * All products take float16 operands with float32 accumulation (inputs and dout must stay
-//     within the float16 range).
+//     taken by extra workgroups, each storing its share in a slot of its own; the key
+//     block's own workgroup adds the slots in split order, so the result is the same bits on
+//     every run.
+//   * All products take float16 operands with float32 accumulation; values past the float16
+//     range saturate at +-65504.
 #include "mfma_common.hpp"
 #include "swa_kernels.hpp"
 
