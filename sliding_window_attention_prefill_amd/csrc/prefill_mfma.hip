@@ -535,7 +535,12 @@ __device__ __forceinline__ float tile_max(const f32x16_t (&sacc)[2]) {
     float mt = max3f(max3f(mx[0], mx[1], mx[2]), mx[3], sacc[1][3]);
     mt = max3f(mt, sacc[1][7], sacc[1][11]);
     mt = fmaxf(mt, sacc[1][15]);
-    return fmaxf(mt, __shfl_xor(mt, 32, 64));
+    // the other lane half holds the query's other 32 keys: exchange the halves in registers
+    // (v_permlane32_swap swaps lanes 32..63 of one operand with lanes 0..31 of the other, so
+    // the larger of its two results is the maximum over lanes l and l ^ 32)
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt),
+                                                     false, false);
+    return max3f(__uint_as_float(sw[0]), __uint_as_float(sw[1]), mt);
 }
 
 // Softmax: fold a tile maximum into the running one. The stale maximum stays while the new
@@ -1062,7 +1067,13 @@ void prefill_mfma_kernel(MfmaParams p) {
     const int eqc = elane & 31, eg = elane >> 5;
     const int64_t eh = (int64_t)hkv * p.G + hg * GP + ew / WPH;
     const int eqa = q0 + 32 * (ew % WPH), ei = eqa + eqc;
-    const float l_tot = MODE == 1 ? l_run + __shfl_xor(l_run, 32, 64) : 1.0f;
+    float l_tot = 1.0f;
+    if (MODE == 1) {
+        // the sum over both lane halves (lanes l and l ^ 32 saw the query's two key halves)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run),
+                                                         __float_as_uint(l_run), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     const float inv = MODE == 1 ? 1.0f / l_tot : 1.0f;
     if (MODE == 1 && p.lse != nullptr && eg == 0 && ei < N)
         p.lse[((int64_t)b * p.Hq + eh) * p.N_mem + p.pos_off + (int64_t)p.pos_stride * ei] =
