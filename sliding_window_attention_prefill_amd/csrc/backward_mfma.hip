@@ -849,13 +849,12 @@ void bwd_dkv2_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
 
-    auto load = [&](int n, int buf) {
+    auto load = [&](int n, uint16_t *__restrict__ st) {
         const int qt = t_lo + n / (int)p.G;
         const int64_t hq = (int64_t)hkv * p.G + n % (int)p.G;
         const int64_t slice = ((int64_t)b * p.Hq + hq) * p.n_tiles * T::IMG;
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.qimg + slice, qslice_bytes);
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.gimg + slice, qslice_bytes);
-        uint16_t *st = lds + buf * STAGE;
         dma_rounds<DMA_R>(st, rq, (uint32_t)qt * T::IMG_BYTES, dimg, wave);
         dma_rounds<DMA_R>(st + T::IMG, rg, (uint32_t)qt * T::IMG_BYTES, dimg, wave);
         if (MODE == 1 && wave == 0 && lane < 32) {
@@ -866,19 +865,12 @@ void bwd_dkv2_kernel(BwdParams p) {
         }
     };
 
-    load(0, 0);
-    __syncthreads();
-    // iteration n: the P role forms and publishes P of step n and adds dV; the dX role takes
-    // step n - 1, whose P was published before the last barrier; stage n + 1 loads meanwhile.
-    // One barrier per iteration: it publishes P(n) and frees stage n - 1 and P buffer n - 1.
-    for (int n = 0; n <= n_steps; ++n) {
-        if (n + 1 < n_steps) load(n + 1, (n + 1) % 3);
-        const int my = role_p ? n : n - 1;   // the step this wavefront works on
-        if (my < 0 || my >= n_steps) {
-            __syncthreads();
-            continue;
-        }
-        const int cur = my % 3;
+    // One step of one role. The three stages and the P buffers are passed as distinct restrict
+    // pointers, so the compiler knows that the transfers into the next stage cannot touch what
+    // this step reads from LDS and does not wait for them before those reads.
+    auto work = [&](int n, int my, uint16_t *__restrict__ fill, const uint16_t *__restrict__ ql,
+                    uint16_t *__restrict__ pxw) {
+        if (n + 1 < n_steps) load(n + 1, fill);
         const int qt = t_lo + my / (int)p.G;
         const int64_t hq = (int64_t)hkv * p.G + my % (int)p.G;
         const int i0 = qt * BK;
@@ -889,11 +881,8 @@ void bwd_dkv2_kernel(BwdParams p) {
         // branches once per step, not per element under an execution mask
         const bool all = __builtin_amdgcn_readfirstlane((int)(ilo == i0 && ihi == i0 + BK - 1 && i0 >= jw + 31 &&
                              ((i0 + BK - 1 - jw < p.w) || jw + 31 < p.s) && jw + 31 < N)) != 0;
-        const uint16_t *ql = lds + cur * STAGE;
         const uint16_t *gl = ql + T::IMG;
         const float *stl = reinterpret_cast<const float *>(ql + 2 * T::IMG);
-        // this lane's P of row block qb: values 0..7 at pxw + qb * 1024, 8..15 at + 512
-        uint16_t *pxw = px0 + (my & 1) * PX + (kw * 2) * 64 * 16 + lane * 8;
         f32x16_t sd[2];                                       // P (P role) or dP (dX role)
         if (any) {
             const float slope_l2 = ALIBI ? p.slopes[hq] * LOG2E : 0.0f;
@@ -992,6 +981,23 @@ void bwd_dkv2_kernel(BwdParams p) {
                 }
             }
         }
+    };
+
+    load(0, lds);
+    __syncthreads();
+    // iteration n: the P role forms and publishes P of step n and adds dV; the dX role takes
+    // step n - 1, whose P was published before the last barrier; stage n + 1 loads meanwhile.
+    // One barrier per iteration: it publishes P(n) and frees stage n - 1 and P buffer n - 1.
+    for (int n = 0; n <= n_steps; ++n) {
+        const int my = role_p ? n : n - 1;   // the step this wavefront works on
+        uint16_t *const fill = lds + ((n + 1) % 3) * STAGE;
+        if (my < 0 || my >= n_steps) {
+            if (n + 1 < n_steps) load(n + 1, fill);
+            __syncthreads();
+            continue;
+        }
+        // this lane's P of row block qb: values 0..7 at pxw + qb * 1024, 8..15 at + 512
+        work(n, my, fill, lds + (my % 3) * STAGE, px0 + (my & 1) * PX + (kw * 2) * 64 * 16 + lane * 8);
         __syncthreads();
     }
 
