@@ -332,7 +332,12 @@ void bwd_dq_kernel(BwdParams p) {
     // K tiles at lds + buf * IMG, V tiles at lds + (2 + buf) * IMG
 
     const int logical = xcd_logical();
-    const int qt = logical % p.n_qtiles;
+    // query tile order as in the forward: the tiles whose bands the sequence start cuts short
+    // come last, longest first
+    int rot = (p.w - 1 + QP - 1) / QP;
+    if (rot > p.n_qtiles) rot = p.n_qtiles;
+    const int lt = logical % p.n_qtiles;
+    const int qt = lt < p.n_qtiles - rot ? lt + rot : p.n_qtiles - 1 - lt;
     int rest = logical / p.n_qtiles;
     const int hg = rest % p.n_hgroups;
     rest /= p.n_hgroups;

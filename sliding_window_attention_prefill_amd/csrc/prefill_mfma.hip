@@ -43,7 +43,11 @@
 //     math.
 //   * The output goes through LDS so that every global store writes whole rows.
 //   * Workgroups are numbered so that each of the 8 XCDs walks a contiguous run of query
-//     tiles of the same (batch, kv head), keeping shared K/V tiles in that XCD's L2.
+//     tiles of the same (batch, kv head), keeping shared K/V tiles in that XCD's L2. Within
+//     a run the tiles go in sequence order, so workgroups dispatched one after another read
+//     each K/V tile a short time apart, except that the first tiles of the sequence (whose
+//     bands the sequence start cuts short) come last, longest first: short work then fills
+//     the end of the grid instead of its start.
 #include "mfma_common.hpp"
 #include "swa_kernels.hpp"
 
@@ -864,7 +868,11 @@ void prefill_mfma_kernel(MfmaParams p) {
     const int nb = gridDim.x, bid = blockIdx.x;
     const int per = nb / 8, rem = nb % 8, xcd = bid % 8, local = bid / 8;
     const int logical = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-    const int qt = logical % p.n_qtiles;
+    // query tiles [rot, n) in order, then the rot tiles with shortened bands, longest first
+    int rot = (p.w - 1 + QP - 1) / QP;
+    if (rot > p.n_qtiles) rot = p.n_qtiles;
+    const int lt = logical % p.n_qtiles;
+    const int qt = lt < p.n_qtiles - rot ? lt + rot : p.n_qtiles - 1 - lt;
     int rest = logical / p.n_qtiles;
     const int hg = rest % p.n_hgroups;
     rest /= p.n_hgroups;
