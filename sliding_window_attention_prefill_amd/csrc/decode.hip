@@ -254,8 +254,9 @@ __global__ __launch_bounds__(256) void decode_general_kernel(DecodeGen a, const 
 }
 
 // Decode for a bf16 cache, d in {64, 128}, G = H_q / H_kv in {1, 2, 4, 8}: the whole-window
-// kernel (w + s <= 128) and the matrix-core kernel (longer windows) below share these
-// arguments.
+// kernels (w + s <= 128: decode_wmfma_kernel at d = 128 with four or eight query heads per kv
+// head, decode_window_kernel otherwise) and the split matrix-core kernel (longer windows)
+// below share these arguments.
 // With APPEND a block first writes the new token (rotated key, value) to its ring slot and
 // sink entry, keeps it in LDS and uses that copy for position q_pos, so the slot it wrote is
 // never read back within the launch.
@@ -821,6 +822,259 @@ __device__ __forceinline__ void dec_step(const DecCtx &cx, uint16_t *__restrict_
         }
 }
 
+// Whole-window decode on the matrix cores, d = 128 with four query heads per block and at most
+// 128 window + sink rows (e.g. SWA(64, 4)). As in decode_window_kernel, every K and V row a
+// query can read is known without its position, so all loads are issued first. One block of
+// four wavefronts per (sequence, kv head, head part); wavefront t owns storage rows
+// 32 t .. 32 t + 31 (ring slots, then sink entries):
+//   scores  S^T = K Q^T with v_mfma_f32_32x32x16_bf16, the K rows as loaded in the A operand
+//           layout and the query in bf16 hi / lo columns (as in decode_mfma_kernel), so both
+//           factors enter exactly; the position then decides which rows count and their bias.
+//   weights per wavefront: sigmoid directly, softmax against the wavefront's own maximum.
+//   values  O^T += V^T P^T with V staged in LDS and read transposed, P in hi / lo columns.
+// The four partial results (and, for softmax, their maxima and sums) meet in LDS once.
+template <int OUT, bool APPEND>
+__global__ __launch_bounds__(256) void decode_wmfma_kernel(DecodeFast a, const uint16_t *__restrict__ q,
+                                                           const int32_t *__restrict__ q_pos,
+                                                           void *__restrict__ o,
+                                                           const uint16_t *__restrict__ k_new,
+                                                           const uint16_t *__restrict__ v_new) {
+    constexpr int D = 128, G = 4, KS = D / 16, DB = D / 32, C = D / 8;
+    __shared__ __attribute__((aligned(16))) uint16_t vt[4][32 * D];   // V rows, chunk-swizzled
+    __shared__ __attribute__((aligned(16))) uint4 qop[KS * 64];       // query operand, columns < 2G
+    __shared__ __attribute__((aligned(16))) uint16_t knr[D];          // appended key, rotated
+    __shared__ __attribute__((aligned(16))) float red[4][2 * G][D];   // partial O^T per wavefront
+    __shared__ float mls[4][G][2];                                     // (maximum, sum) per wavefront
+
+    // grid (sequence, kv head, head part): no division by a runtime count before the loads
+    const int sq = blockIdx.x, hk = blockIdx.y, hs = blockIdx.z;
+    const int p = q_pos[sq];
+    const int hbase = hk * a.G + hs * G;
+    const int tid = threadIdx.x, lane = tid & 63, t = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int NK = a.w + a.s;
+    const int64_t ring_base = ((int64_t)sq * a.Hkv + hk) * a.w * D;
+    const int64_t sink_base = ((int64_t)sq * a.Hkv + hk) * a.s * D;
+    auto row_ptr = [&](const uint16_t *ring, const uint16_t *sink, int e) {
+        return e < a.w ? ring + ring_base + (int64_t)e * D : sink + sink_base + (int64_t)(e - a.w) * D;
+    };
+
+    // ---- loads that do not depend on the position, all in flight together
+    const bool live = 32 * t < NK;                 // uniform: the wavefront owns any row
+    const int er = 32 * t + col;                   // this lane's K row
+    uint4 kx[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        kx[ks] = er < NK ? ldg16(row_ptr(a.k_ring, a.k_sink, er) + 8 * (2 * ks + half)) : make_uint4(0, 0, 0, 0);
+    // V rows in the LDS layout of decode_mfma_kernel's tiles: slot 64 i + lane holds row
+    // slot / C, stored chunk slot % C, which is chunk (slot % C) ^ dec_vswz(row)
+    uint4 vx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int slot = 64 * i + lane, r = slot / C, c = (slot % C) ^ dec_vswz<D>(r);
+        const int e = 32 * t + r;
+        vx[i] = e < NK ? ldg16(row_ptr(a.v_ring, a.v_sink, e) + 8 * c) : make_uint4(0, 0, 0, 0);
+    }
+    // the query pair this thread rotates: head tid / 64, dimensions 2 (tid % 64) + {0, 1}
+    const int qh = tid >> 6, qj = tid & 63;
+    const uint32_t qw = *reinterpret_cast<const uint32_t *>(q + ((int64_t)sq * a.Hq + hbase + qh) * D + 2 * qj);
+    uint32_t kw = 0;
+    uint4 vn = make_uint4(0, 0, 0, 0);
+    if (APPEND) {
+        const int64_t src = ((int64_t)sq * a.Hkv + hk) * D;
+        if (tid < D / 2) kw = *reinterpret_cast<const uint32_t *>(k_new + src + 2 * tid);
+        if (lane < C) vn = *reinterpret_cast<const uint4 *>(v_new + src + 8 * lane);
+    }
+
+    const bool valid = p >= 0 && (!a.rope || (int64_t)p < a.rope_rows);
+    if (!valid) {
+        for (int idx = tid; idx < G * D; idx += 256)
+            Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hbase) * D + idx, qnan());
+        return;
+    }
+    float cs = 1.0f, sn = 0.0f;
+    if (a.rope) {
+        const float2 cw = *reinterpret_cast<const float2 *>(a.rope + ((int64_t)p * (D / 2) + qj) * 2);
+        cs = cw.x; sn = cw.y;
+    }
+    const int slot_new = p % a.w;
+    {
+        // query operand: column qh carries the bf16 part hi of the rotated, scaled query and
+        // column G + qh its remainder lo; dimension d sits in k-step d / 16, lane half
+        // (d % 16) / 8, element d % 8
+        const float x0 = bf16_bits_to_f32(qw & 0xffffu), x1 = bf16_bits_to_f32(qw >> 16);
+        const float r0 = fmaf(-x1, sn, x0 * cs) * a.cs, r1 = fmaf(x0, sn, x1 * cs) * a.cs;
+        const float h0 = bf16_bits_to_f32(f32_to_bf16_bits(r0)), h1 = bf16_bits_to_f32(f32_to_bf16_bits(r1));
+        const int d = 2 * qj, ks = d >> 4, hf = (d >> 3) & 1, el = d & 7;
+        uint32_t *qo = reinterpret_cast<uint32_t *>(qop);
+        qo[((64 * ks + 32 * hf + qh) * 8 + el) >> 1] = pack_bf16x2(h0, h1);
+        qo[((64 * ks + 32 * hf + G + qh) * 8 + el) >> 1] = pack_bf16x2(r0 - h0, r1 - h1);
+    }
+    if (APPEND && tid < D / 2) {
+        // the appended key, rotated and rounded as the cache stores it
+        const float x0 = bf16_bits_to_f32(kw & 0xffffu), x1 = bf16_bits_to_f32(kw >> 16);
+        const uint32_t kr = pack_bf16x2(fmaf(-x1, sn, x0 * cs), fmaf(x0, sn, x1 * cs));
+        reinterpret_cast<uint32_t *>(knr)[tid] = kr;
+        if (hs == 0) {
+            *reinterpret_cast<uint32_t *>(a.k_ring + ring_base + (int64_t)slot_new * D + 2 * tid) = kr;
+            if (p < a.s) *reinterpret_cast<uint32_t *>(a.k_sink + sink_base + (int64_t)p * D + 2 * tid) = kr;
+        }
+    }
+    if (APPEND && hs == 0 && t == 0 && lane < C) {
+        *reinterpret_cast<uint4 *>(a.v_ring + ring_base + (int64_t)slot_new * D + 8 * lane) = vn;
+        if (p < a.s) *reinterpret_cast<uint4 *>(a.v_sink + sink_base + (int64_t)p * D + 8 * lane) = vn;
+    }
+    // V rows into this wavefront's LDS tile; then the appended value over its slot's row (the
+    // same wavefront, later in program order)
+    uint16_t *const vl = vt[t];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(vl + (64 * i + lane) * 8) = vx[i];
+    if (APPEND && (slot_new >> 5) == t && lane < C) {
+        const int r = slot_new & 31;
+        *reinterpret_cast<uint4 *>(vl + (r * C + (lane ^ dec_vswz<D>(r))) * 8) = vn;
+    }
+    __syncthreads();
+
+    f32x16_t oacc[DB];
+    float m_w = -INFINITY, l_w = 0.0f;
+    if (live) {
+        if (APPEND && er == slot_new) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) kx[ks] = *reinterpret_cast<const uint4 *>(knr + 8 * (2 * ks + half));
+        }
+        const bool qcol = col < 2 * G, lo_part = col >= G;
+        // every operand read first, then two independent product chains
+        uint4 qb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qb[ks] = qcol ? qop[64 * ks + lane] : make_uint4(0, 0, 0, 0);
+        f32x16_t sacc = {}, sacc2 = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ks += 2) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx[ks]),
+                                                           __builtin_bit_cast(bf16x8_t, qb[ks]), sacc, 0, 0, 0);
+            sacc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kx[ks + 1]),
+                                                            __builtin_bit_cast(bf16x8_t, qb[ks + 1]), sacc2, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[e] += sacc2[e];
+        // hi + lo columns; element e is storage row 32 t + 8 (e / 4) + 4 half + e % 4, which
+        // counts when it holds a position of the key set: ring slot r holds
+        // p - ((slot_new - r) mod w), sink entry j position j while the window no longer
+        // covers it; the bias is slope (p - position)
+        const int partner = lo_part ? lane - G : lane + G;
+        const int hg = lo_part ? col - G : col;
+        const float slope = (a.slopes && qcol) ? a.slopes[hbase + hg] * 1.4426950408889634f : 0.0f;
+        const int lo = p - a.w + 1 > 0 ? p - a.w + 1 : 0;
+        float s[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int r = 32 * t + 8 * (e >> 2) + 4 * half + (e & 3);
+            const float full = sacc[e] + __shfl(sacc[e], partner, 64);
+            int dist;
+            bool inset;
+            if (r < a.w) {
+                dist = slot_new >= r ? slot_new - r : slot_new - r + a.w;
+                inset = dist <= p;
+            } else {
+                dist = p - (r - a.w);
+                inset = r < NK && r - a.w < lo;
+            }
+            s[e] = inset ? fmaf(slope, (float)dist, full) : -INFINITY;
+        }
+        if (a.mode == 0) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-s[e]));
+        } else {
+            float mt = s[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mt = fmaxf(mt, s[e]);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+            mt = fmaxf(mt, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+            m_w = mt;
+            const float mref = mt == -INFINITY ? 0.0f : mt;   // a wavefront with no row of the set
+            float ls = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                s[e] = __builtin_amdgcn_exp2f(s[e] - mref);
+                ls += s[e];
+            }
+            const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(ls), __float_as_uint(ls), false, false);
+            l_w = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
+        }
+        // P^T operand of k-step j (rows 16 j + 4 half + {0..3, 8..11}): bf16 hi (columns < G)
+        // or lo (columns G .. 2G - 1)
+        uint4 pk[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float x[8];
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const float v = s[8 * j + m];
+                const float h = bf16_bits_to_f32(f32_to_bf16_bits(v));
+                x[m] = lo_part ? v - h : v;
+            }
+            const uint4 pp = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                        pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+            pk[j] = qcol ? pp : make_uint4(0, 0, 0, 0);
+        }
+        // transposing read: lane (G4, rr, a) supplies row 4 (G4 / 2) + rr and column group
+        // 16 (G4 % 2) + 4 a of the 8 x 32 block one read covers
+        const int G4 = lane >> 4, rr = (lane >> 2) & 3, aa = lane & 3;
+        const int row_l = 4 * (G4 >> 1) + rr, cb = 2 * (G4 & 1) + (aa >> 1);
+        const int fq = dec_vswz<D>(rr) >> 2;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            oacc[db] = f32x16_t{};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int vo = row_l * D + (4 * (db ^ fq) + cb) * 8 + 4 * (aa & 1);
+                const s16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vl + 16 * j * D + vo));
+                const s16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(vl + (16 * j + 8) * D + vo));
+                const s16x8_t a8 = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8),
+                                                                   __builtin_bit_cast(bf16x8_t, pk[j]),
+                                                                   oacc[db], 0, 0, 0);
+            }
+        }
+        // partial O^T: element e of block db is dimension 32 db + 8 (e / 4) + 4 half + e % 4
+        if (qcol) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    *reinterpret_cast<float4 *>(&red[t][col][32 * db + 8 * u + 4 * half]) =
+                        make_float4(oacc[db][4 * u], oacc[db][4 * u + 1], oacc[db][4 * u + 2], oacc[db][4 * u + 3]);
+        }
+        if (lane < G) {
+            mls[t][lane][0] = m_w;
+            mls[t][lane][1] = l_w;
+        }
+    }
+    __syncthreads();
+    // ---- merge of the wavefronts that own rows: sigmoid adds; softmax rescales each partial
+    // by 2^(m_t - M)
+    const int nt = (NK + 31) >> 5;
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int g = idx / D, d = idx % D;
+        float sum = 0.0f;
+        if (a.mode == 0) {
+            for (int tt = 0; tt < nt; ++tt) sum += red[tt][g][d] + red[tt][G + g][d];
+        } else {
+            float M = -INFINITY;
+            for (int tt = 0; tt < nt; ++tt) M = fmaxf(M, mls[tt][g][0]);
+            float den = 0.0f;
+            for (int tt = 0; tt < nt; ++tt) {
+                const float m = mls[tt][g][0];
+                const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+                sum = fmaf(red[tt][g][d] + red[tt][G + g][d], f, sum);
+                den = fmaf(mls[tt][g][1], f, den);
+            }
+            sum /= den;
+        }
+        Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hbase + g) * D + d, sum);
+    }
+}
+
 // Two wavefronts per SIMD: two blocks per CU keep 16 tiles of transfers in flight.
 template <int D, int G, int OUT, bool APPEND>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeFast a, const uint16_t *__restrict__ q,
@@ -1022,6 +1276,14 @@ hipError_t launch_fast_t(const DecodeFast &f, const void *q, const int32_t *q_po
         // reading the window for its four heads (splitting four heads over two blocks
         // measured slower: 11.9 against 8.6 us per SWA(64, 4) step)
         constexpr int GB = G < 4 ? G : 4;
+        // d = 128 with four heads per block on the matrix cores (its grid is (sequences,
+        // kv heads, head parts): y stays within 65535, x times 256 threads within 2^32)
+        if (D == 128 && GB == 4 && f.Hkv <= 65535 && f.S <= (1 << 24)) {
+            hipLaunchKernelGGL((decode_wmfma_kernel<OUT, APPEND>), dim3((unsigned)f.S, (unsigned)f.Hkv, (unsigned)(G / GB)),
+                               dim3(256), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
+                               static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL((decode_window_kernel<D, GB, OUT, APPEND, 512>), dim3((unsigned)(f.S * f.Hkv * (G / GB))),
                            dim3(512), 0, st, f, static_cast<const uint16_t *>(q), q_pos, o,
                            static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new));
