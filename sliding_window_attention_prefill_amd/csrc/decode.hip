@@ -347,11 +347,8 @@ __global__ __launch_bounds__(NT) void decode_window_kernel(DecodeFast a, const u
                                                             const uint16_t *__restrict__ k_new,
                                                             const uint16_t *__restrict__ v_new) {
     using C = WinCfg<D, NT>;
-    // d = 128 with four heads: a wavefront holds four row groups of the same chunks, summed
-    // in registers by lane-half and lane-row swaps before one LDS pass over the wavefronts
-    constexpr bool WRED = D == 128 && G == 4;
     __shared__ float sc[G][128];
-    __shared__ __attribute__((aligned(16))) float red[WRED ? C::NW : C::RPP][G][D];
+    __shared__ __attribute__((aligned(16))) float red[C::RPP][G][D];
     __shared__ float lsum[G];
     // block: (sequence, kv head, head part); the kv head's a.G query heads are split into
     // parts of G heads, each block reading the whole window for its part
@@ -533,49 +530,19 @@ __global__ __launch_bounds__(NT) void decode_window_kernel(DecodeFast a, const u
             }
         }
     }
-    if constexpr (WRED) {
-        // lanes l, l + 16, l + 32, l + 48 hold row groups 4 wave + {0..3} of the same chunk.
-        // Value k = 8 g + c of a lane: the half swap sums k and 16 + k over the lane halves
-        // (lanes 0..31 keep k < 16, lanes 32..63 the rest), the row swap sums j and 8 + j
-        // over neighbouring 16-lane rows, so lane l ends with head l / 16, dimensions
-        // 8 (l % 16) .. + 7, summed over the wavefront's four row groups.
-        float v[32];
+    // partial sums of the RPP row groups, added through LDS
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int c = 0; c < 8; ++c) v[8 * g + c] = acc[g][c];
-        float s1[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]), __float_as_uint(v[16 + k]),
-                                                             false, false);
-            s1[k] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-        float s2[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(s1[j]), __float_as_uint(s1[8 + j]),
-                                                             false, false);
-            s2[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        }
-        float4 *dst = reinterpret_cast<float4 *>(&red[wave][lane >> 4][8 * (lane & 15)]);
-        dst[0] = make_float4(s2[0], s2[1], s2[2], s2[3]);
-        dst[1] = make_float4(s2[4], s2[5], s2[6], s2[7]);
-    } else {
-        // partial sums of the RPP row groups, added through LDS
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float4 *dst = reinterpret_cast<float4 *>(&red[rbase][g][8 * col]);
-            dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
-            dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
-        }
+    for (int g = 0; g < G; ++g) {
+        float4 *dst = reinterpret_cast<float4 *>(&red[rbase][g][8 * col]);
+        dst[0] = make_float4(acc[g][0], acc[g][1], acc[g][2], acc[g][3]);
+        dst[1] = make_float4(acc[g][4], acc[g][5], acc[g][6], acc[g][7]);
     }
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += NT) {
         const int g = idx / D, cc = idx % D;
         float sum = 0.0f;
 #pragma unroll
-        for (int r = 0; r < (WRED ? C::NW : C::RPP); ++r) sum += red[r][g][cc];
+        for (int r = 0; r < C::RPP; ++r) sum += red[r][g][cc];
         if (a.mode == 1) sum /= lsum[g];
         Elem<OUT>::store(o, ((int64_t)sq * a.Hq + hbase + g) * D + cc, sum);
     }
