@@ -795,8 +795,8 @@ __device__ __forceinline__ void dec_step(const DecCtx &cx, uint16_t *__restrict_
 // four wavefronts per (sequence, kv head, head part); wavefront t owns storage rows
 // 32 t .. 32 t + 31 (ring slots, then sink entries):
 //   scores  S^T = K Q^T with v_mfma_f32_32x32x16_bf16, the K rows as loaded in the A operand
-//           layout and the query in bf16 hi / lo columns (as in decode_mfma_kernel), so both
-//           factors enter exactly; the position then decides which rows count and their bias.
+//           layout (exact) and the query in bf16 hi / lo columns (as in decode_mfma_kernel,
+//           about 16 bits); the position then decides which rows count and their bias.
 //   weights per wavefront: sigmoid directly, softmax against the wavefront's own maximum.
 //   values  O^T += V^T P^T with V staged in LDS and read transposed, P in hi / lo columns.
 // The four partial results (and, for softmax, their maxima and sums) meet in LDS once.
