@@ -1021,22 +1021,32 @@ __global__ __launch_bounds__(256) void decode_wmfma_kernel(DecodeFast a, const u
     // ---- merge of the wavefronts that own rows: sigmoid adds; softmax rescales each partial
     // by 2^(m_t - M)
     const int nt = (NK + 31) >> 5;
-    for (int idx = tid; idx < G * D; idx += 256) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = tid + 256 * it;
         const int g = idx / D, d = idx % D;
+        // every read of the (at most four) wavefronts first, then the arithmetic
+        float x[4], m[4], l[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const bool in = tt < nt;
+            x[tt] = in ? red[tt][g][d] + red[tt][G + g][d] : 0.0f;
+            m[tt] = in ? mls[tt][g][0] : -INFINITY;
+            l[tt] = in ? mls[tt][g][1] : 0.0f;
+        }
         float sum = 0.0f;
         if (a.mode == 0) {
-            for (int tt = 0; tt < nt; ++tt) sum += red[tt][g][d] + red[tt][G + g][d];
+            sum = (x[0] + x[1]) + (x[2] + x[3]);
         } else {
-            float M = -INFINITY;
-            for (int tt = 0; tt < nt; ++tt) M = fmaxf(M, mls[tt][g][0]);
+            const float M = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
             float den = 0.0f;
-            for (int tt = 0; tt < nt; ++tt) {
-                const float m = mls[tt][g][0];
-                const float f = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-                sum = fmaf(red[tt][g][d] + red[tt][G + g][d], f, sum);
-                den = fmaf(mls[tt][g][1], f, den);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const float f = m[tt] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m[tt] - M);
+                sum = fmaf(x[tt], f, sum);
+                den = fmaf(l[tt], f, den);
             }
-            sum /= den;
+            sum *= __builtin_amdgcn_rcpf(den);
         }
         // streaming (non-temporal) stores: the outputs are not read again by this launch, and
         // the launch's end waits for them (0.33 us less per SWA(64, 4) step than plain stores)
